@@ -1,0 +1,224 @@
+/*
+ * vpk.h -- C ABI of libvpk: forward attention of packed variable-length queries
+ * over a paged KV cache, with an in-place append of new keys/values, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are the public pull-request pages this library is
+ * built from, cited by page title and section):
+ *
+ *   For every sequence b of a batch, with Lq = q_len, Lc = cached length,
+ *   Ln = new length, Lk = Lc + Ln, S = page_size, g = Hq / Hkv:
+ *
+ *   1. append: new token j (0 <= j < Ln) is stored at logical position
+ *      pos = Lc + j, i.e. page block_table[b][pos / S], slot pos % S, all kv
+ *      heads; bf16 caches receive the bytes unchanged, fp8 caches receive
+ *      e4m3fn(fp32(x) * fp32(1 / scale)), rounded to nearest even, saturated to
+ *      +-448.  ("Add flash_attn_varlen_func_with_kvcache", Usage: the cache is
+ *      updated in place and read through per-sequence lengths; Minor Changes:
+ *      the cache length is its own parameter and the new tokens carry their own
+ *      cumulative offsets.)
+ *   2. attention: out[i, h] = sum_j softmax_j(scale * q_i . k_j) v_j over the
+ *      keys j < Lk of the sequence, keys and values read from the cache after
+ *      the append, kv head h / g, with j <= i + Lk - Lq when causal (the
+ *      diagonal aligned to the end of the keys); lse[h, i] = ln sum_j
+ *      exp(scale * q_i . k_j).  A query that sees no key gets out = 0 and
+ *      lse = -inf.  ("Extend FlashAttention Prefill with KV cache",
+ *      description: cached plus current KV, causal and non-causal; "Add KV
+ *      cache for paged/non-paged attention", Description: one page table for
+ *      K and V, batches that mix context and generation; "[Kernel][Triton][FP8]
+ *      Adding fp8 and variable length sequence support to Triton FAv2 kernel",
+ *      feature list: 8-bit KV cache, causal, grouped-query heads, variable
+ *      lengths.)
+ *
+ * Layouts (all contiguous, row-major, element strides implied by the shape):
+ *   q, out            [total_q, num_q_heads, head_dim]        bf16
+ *   k_new, v_new      [total_knew, num_kv_heads, head_dim]    bf16
+ *   k_cache, v_cache  [num_pages, page_size, num_kv_heads, head_dim]
+ *                     bf16 or fp8 e4m3fn (kv_cache_dtype)
+ *   block_table       [batch, max_pages_per_seq]              int32
+ *   cu_seqlens_q      [batch + 1] int32, 0 = c[0] <= c[1] <= ... = total_q
+ *   cu_seqlens_knew   [batch + 1] int32, likewise ending at total_knew
+ *   cache_seqlens     [batch]     int32, cached length BEFORE the append
+ *   lse               [num_q_heads, total_q]                  fp32, natural log
+ *
+ * Memory and ownership: every pointer is borrowed.  Device pointers (q, k_new,
+ * v_new, caches, block_table, out, lse and the device index arrays) must stay
+ * valid until the work enqueued on `stream` has run; the call returns as soon
+ * as the work is enqueued.  Host pointers (dims, host mirrors, kv_scale) are
+ * read before the call returns.  The caches are modified in place only at the
+ * slots of the appended tokens.  cache_seqlens is never modified: the caller
+ * advances it, as with the cache-length parameter of the flash-attention page.
+ * Device buffers must be 16-byte aligned (lse: 4-byte).
+ *
+ * The library keeps a per-device, per-stream workspace (work list, split
+ * partials) that it allocates on first use and grows as needed; two calls that
+ * overlap in time on one device must therefore use the same stream or
+ * different streams, never the same stream from two host threads at once.
+ *
+ * Errors: every entry point returns a vpk_status; nothing throws or aborts.
+ * vpk_last_error() gives a message for the calling thread's last failure.
+ * Argument errors are detected on the host from the dims and the host mirrors
+ * before anything is enqueued.
+ */
+#ifndef VPK_H_
+#define VPK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VPK_ABI_VERSION 1
+
+typedef enum {
+  VPK_SUCCESS = 0,
+  VPK_ERROR_INVALID_VALUE = 1,   /* a shape, pointer, length or page id is wrong */
+  VPK_ERROR_NOT_SUPPORTED = 2,   /* valid but not implemented (e.g. head_dim 96) */
+  VPK_ERROR_CAPACITY = 3,        /* Lc + Ln exceeds max_pages_per_seq * page_size */
+  VPK_ERROR_HIP = 4,             /* a HIP runtime call failed */
+  VPK_ERROR_OUT_OF_MEMORY = 5    /* workspace allocation failed */
+} vpk_status;
+
+typedef enum {
+  VPK_DTYPE_BF16 = 1,
+  VPK_DTYPE_FP8_E4M3FN = 2       /* OCP e4m3fn, per-tensor scale */
+} vpk_dtype;
+
+/* Problem sizes.  kv_cache_dtype is ignored when there is no cache. */
+typedef struct {
+  int32_t batch;               /* B >= 0 */
+  int32_t total_q;             /* Tq = cu_seqlens_q[B] */
+  int32_t total_knew;          /* Tn = cu_seqlens_knew[B]; 0 without new K/V */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv, Hq % Hkv == 0 */
+  int32_t head_dim;            /* D: 64 or 128 */
+  int32_t num_pages;           /* P: pages of each cache tensor; 0 without a cache */
+  int32_t max_pages_per_seq;   /* row length of block_table */
+  int32_t kv_cache_dtype;      /* vpk_dtype */
+} vpk_dims;
+
+/* Host copies of the index arrays (same contents as the device arrays).  The
+ * work list is planned from these.  Any member may be NULL: the library then
+ * copies the device array to the host with a blocking copy on `stream` (slow
+ * path; not allowed inside stream capture).  block_table, when given, lets the
+ * host reject page ids outside [0, num_pages) for the slots that are read or
+ * written; without it the kernels skip such pages (their keys read as zero and
+ * appends to them are dropped) and raise a device error flag that
+ * vpk_device_error() returns. */
+typedef struct {
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_knew;
+  const int32_t* cache_seqlens;
+  const int32_t* block_table;
+} vpk_host_index;
+
+/*
+ * attn_varlen_paged_fwd -- the whole call: append the new K/V (if any) into
+ * the cache (if any), then attention for every packed query row.
+ *
+ *   dims            sizes (host).
+ *   q               device bf16 [Tq, Hq, D].
+ *   cu_seqlens_q    device int32 [B + 1].
+ *   k_new, v_new    device bf16 [Tn, Hkv, D], or both NULL (attend over the
+ *                   cache only, as the flash-attention page's Usage section
+ *                   allows).
+ *   cu_seqlens_knew device int32 [B + 1]; NULL iff k_new is NULL.
+ *   k_cache,v_cache device [P, S, Hkv, D] in kv_cache_dtype, or both NULL: no
+ *                   cache, attention runs over k_new/v_new of each sequence and
+ *                   nothing is stored.  With a cache, new tokens are appended
+ *                   first and attention reads every key from the cache.
+ *   block_table     device int32 [B, max_pages_per_seq], shared by K and V;
+ *                   entries beyond ceil(Lk / S) of a row are never read.
+ *   cache_seqlens   device int32 [B] (NULL without a cache).
+ *   page_size       S >= 1 tokens per page (ignored without a cache).
+ *   causal          0 or 1.
+ *   scale           softmax scale, finite.
+ *   kv_scale        host float[2] = {k_scale, v_scale} > 0 for an fp8 cache:
+ *                   stored code c means c * scale; NULL for bf16.
+ *   out             device bf16 [Tq, Hq, D].
+ *   lse             device fp32 [Hq, Tq], or NULL.
+ *   host            host mirrors (see vpk_host_index), or NULL.
+ *   stream          hipStream_t (NULL = default stream).
+ *
+ * Returns VPK_SUCCESS once all work is enqueued.  Split-KV, the persistent
+ * work schedule and the merge pass are internal choices of the library.
+ */
+int32_t attn_varlen_paged_fwd(const vpk_dims* dims,
+                              const void* q, const int32_t* cu_seqlens_q,
+                              const void* k_new, const void* v_new,
+                              const int32_t* cu_seqlens_knew,
+                              void* k_cache, void* v_cache,
+                              const int32_t* block_table, const int32_t* cache_seqlens,
+                              int32_t page_size, int32_t causal, float scale,
+                              const float* kv_scale,
+                              void* out, float* lse,
+                              const vpk_host_index* host, void* stream);
+
+/*
+ * kv_cache_append -- step 1 alone: store k_new/v_new into the paged cache at
+ * positions [Lc, Lc + Ln) of each sequence (same rules and arguments as above).
+ * Idempotent: repeating it with the same arguments writes the same bytes.
+ */
+int32_t kv_cache_append(const vpk_dims* dims,
+                        const void* k_new, const void* v_new,
+                        const int32_t* cu_seqlens_knew,
+                        void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        int32_t page_size, const float* kv_scale,
+                        const vpk_host_index* host, void* stream);
+
+/* Message describing the calling thread's last non-success status ("" if none). */
+const char* vpk_last_error(void);
+
+/* VPK_ABI_VERSION of the loaded library. */
+int32_t vpk_abi_version(void);
+
+/*
+ * Tuning / test knobs (process-wide).  Names:
+ *   "force_splits"     0 = planner decides; n >= 1 = split every work item's
+ *                      key range into n parts (tests of the merge pass).
+ *   "persistent"       -1 = planner decides, 0 = one work item per workgroup,
+ *                      1 = persistent grid with static per-workgroup queues.
+ *   "split_min_keys"   smallest key range of a split part (default 256).
+ *   "num_cus"          compute units assumed by the planner (0 = query device).
+ * Returns VPK_ERROR_INVALID_VALUE for an unknown name or value.
+ */
+int32_t vpk_set_option(const char* name, int64_t value);
+
+/*
+ * Kernel timing: when enabled, every launch of the library's kernels is
+ * bracketed by HIP events recorded on the launch stream.  vpk_timing_read
+ * synchronises those events and returns the summed milliseconds and the
+ * launch count per kernel since the last reset.
+ *   kernel: 0 = attention, 1 = append, 2 = merge.
+ */
+int32_t vpk_timing_enable(int32_t enable);
+int32_t vpk_timing_reset(void);
+int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+/* Synchronise `stream` and return (and clear) the device error flag of its
+ * workspace: bit 0 = a page id outside [0, num_pages) was met. */
+int32_t vpk_device_error(void* stream, int32_t* flags);
+
+/*
+ * Planner introspection (host only, needs no GPU): build the work list the
+ * attention launch would use and copy it out.  Each item is 8 int32:
+ *   {seq, row0, nrows, kv_head, key_begin, key_end, part, queue}
+ * where rows are packed (token * g + head-in-group) and part >= 0 marks a
+ * split part whose result goes through the merge pass.  `num_cus` as for the
+ * "num_cus" option (> 0 here).  Returns VPK_ERROR_CAPACITY with *n_items set
+ * when `capacity` is too small.
+ */
+int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host,
+                       int32_t has_cache, int32_t has_new, int32_t page_size,
+                       int32_t causal, int32_t num_cus,
+                       int32_t* items, int32_t capacity, int32_t* n_items,
+                       int32_t* n_queues);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VPK_H_ */

@@ -65,7 +65,12 @@ def _encode(rows: np.ndarray, src_dtype: str, cache_dtype: str, scale: Optional[
         else:
             raise ValueError(src_dtype)
         inv = np.float32(1.0) / np.float32(scale)      # fp32 reciprocal of the scale
-        return e4m3fn_encode((x32 * inv).astype(np.float32))
+        with np.errstate(over="ignore", invalid="ignore"):
+            prod = (x32 * inv).astype(np.float32)
+        # 1/scale > 0, so the product has the input's sign; for a NaN input the
+        # input's sign is the one stored (a NaN product's sign is not defined)
+        prod = np.where(np.signbit(x32), -np.abs(prod), np.abs(prod)).astype(np.float32)
+        return e4m3fn_encode(prod)
     raise ValueError(f"cannot store {src_dtype} in a {cache_dtype} cache")
 
 

@@ -152,13 +152,15 @@ def _draw_lengths(name: str, rng: np.random.Generator):
 def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=True,
                 cache_dtype="bf16", seed=0, scale=None, pool_factor=1.25,
                 poison=False, extra_pages=0, name="custom", tiny_table=False,
-                value_std=1.0) -> Workload:
+                value_std=1.0, lengths_only=False) -> Workload:
     """Draw a workload with explicit per-sequence lengths.
 
     ``cache_dtype=None`` means there is no cache: attention runs over the new
     tokens only and ``cache_lens`` must be all zero.
     ``new_lens`` entries may be 0; pass ``new_lens=None`` for a call without new
     K/V (attention over the cache only).
+    ``lengths_only`` skips every value draw (q/k/v/caches are empty arrays);
+    lengths and the page-table rule are kept, the permutation itself differs.
     """
     rng = np.random.default_rng(seed)
     q_lens = np.asarray(q_lens, np.int64)
@@ -176,9 +178,13 @@ def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=T
     cu_kn = np.concatenate([[0], np.cumsum(new_lens)]).astype(np.int32)
     Tq, Tk = int(cu_q[-1]), int(kv_lens.sum())
 
-    q32 = rng.standard_normal((Tq, Hq, D), dtype=np.float32) * np.float32(value_std)
-    k32 = rng.standard_normal((Tk, Hkv, D), dtype=np.float32) * np.float32(value_std)
-    v32 = rng.standard_normal((Tk, Hkv, D), dtype=np.float32) * np.float32(value_std)
+    if lengths_only:
+        Tq_, Tk_ = 0, 0
+    else:
+        Tq_, Tk_ = Tq, Tk
+    q32 = rng.standard_normal((Tq_, Hq, D), dtype=np.float32) * np.float32(value_std)
+    k32 = rng.standard_normal((Tk_, Hkv, D), dtype=np.float32) * np.float32(value_std)
+    v32 = rng.standard_normal((Tk_, Hkv, D), dtype=np.float32) * np.float32(value_std)
     q = to_bf16_bits(q32)
     kb = to_bf16_bits(k32)
     vb = to_bf16_bits(v32)
@@ -186,7 +192,7 @@ def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=T
 
     # split every sequence's keys into its cached prefix and its new tokens
     new_idx = np.concatenate([np.arange(cu_k[b] + cache_lens[b], cu_k[b + 1]) for b in range(B)]
-                             ).astype(np.int64) if Tk else np.zeros(0, np.int64)
+                             ).astype(np.int64) if Tk_ else np.zeros(0, np.int64)
     k_new = kb[new_idx] if has_new else None
     v_new = vb[new_idx] if has_new else None
 
@@ -206,7 +212,7 @@ def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=T
             max_pages = bt.shape[1]
         else:
             pool = int(math.ceil(pool_factor * need.sum())) + extra_pages
-            pool = max(pool, int(need.sum()))
+            pool = max(pool, int(need.sum()), 1)
             perm = rng.permutation(pool)
             max_pages = max(int(need.max()) if B else 0, 1)
             bt = np.full((B, max_pages), -1, np.int32)
@@ -215,6 +221,12 @@ def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=T
                 bt[b, :need[b]] = perm[off:off + need[b]]
                 off += need[b]
         shape = (pool, S, Hkv, D)
+        if lengths_only:
+            empty = np.zeros((0, S, Hkv, D), np.uint8 if cache_dtype == "fp8" else np.uint16)
+            wl.update(k_cache=empty, v_cache=empty.copy(), block_table=bt,
+                      cache_seqlens=cache_lens.astype(np.int32),
+                      kv_scale=(np.float32(1), np.float32(1)) if cache_dtype == "fp8" else None)
+            return Workload(**wl)
         if poison:
             fill_k = np.full(shape, np.nan, np.float32)
             fill_v = np.full(shape, np.nan, np.float32)
@@ -265,7 +277,8 @@ def make_custom(*, q_lens, new_lens, cache_lens, Hq, Hkv, D, page_size, causal=T
     return Workload(**wl)
 
 
-def make_workload(name: str, rep: int = 0, *, poison: bool = False) -> Workload:
+def make_workload(name: str, rep: int = 0, *, poison: bool = False,
+                  lengths_only: bool = False) -> Workload:
     """The named workload with seed ``SEED_BASE[name] + 1000 * rep``."""
     spec = WORKLOADS[name]
     seed = SEED_BASE[name] + 1000 * rep
@@ -277,4 +290,4 @@ def make_workload(name: str, rep: int = 0, *, poison: bool = False) -> Workload:
     return make_custom(q_lens=ql, new_lens=nl, cache_lens=cl, Hq=spec["Hq"], Hkv=spec["Hkv"],
                        D=spec["D"], page_size=spec["page_size"], causal=spec["causal"],
                        cache_dtype=spec["cache_dtype"], seed=seed + 500, poison=poison,
-                       name=name, tiny_table=(name == "tiny"))
+                       name=name, tiny_table=(name == "tiny"), lengths_only=lengths_only)

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+* append and page gather: bit-exact (cache bytes; one-hot gather probe);
+* attention values: max-abs 2e-2 (3e-2 with an fp8 cache), mean-abs 2e-3,
+  lse max-abs 1e-3, rows without visible keys exactly 0 / -inf;
+* full-size workloads in the launch configuration the bench times, checked on
+  sampled sequences the oracle computes one by one.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import varlen_paged_kv_amd as vpk
+from synth import make_custom, make_workload
+from synth.workloads import to_bf16_bits
+
+from gpu_util import (DeviceCall, check_attention, dev_bf16, dev_i32, dev_u8, oracle_full, say,
+                      to_np_out)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    vpk.set_option("force_splits", 0)
+    vpk.set_option("persistent", -1)
+
+
+def _run_and_check(wl, label, with_new=True):
+    say(f"[case] {label}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} S={wl.page_size} "
+        f"causal={wl.causal} cache={wl.cache_dtype} seed={wl.seed}")
+    dc = DeviceCall(wl, with_new=with_new)
+    out, lse = dc.run()
+    torch.cuda.synchronize()
+    ref = oracle_full(wl, with_new=with_new)
+    kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
+    errs = check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"],
+                           ref["lse"], kind, label=label)
+    kc, vc = dc.cache_host()
+    if kc is not None:
+        assert np.array_equal(kc, ref["k_cache"]), f"{label}: k_cache bytes differ"
+        assert np.array_equal(vc, ref["v_cache"]), f"{label}: v_cache bytes differ"
+    say(f"[ok] {label}: max {errs[0]:.2e} mean {errs[1]:.2e} lse {errs[2]:.2e}")
+    return dc, out, lse
+
+
+def test_tiny_workload():
+    _run_and_check(make_workload("tiny"), "tiny")
+
+
+SMALL = [
+    # label, q_lens, new_lens, cache_lens, Hq, Hkv, D, S, causal, cache
+    ("ragged_S16_g4", [1, 37, 200, 129], [1, 37, 200, 129], [0, 65, 300, 1000], 8, 2, 128, 16, True, "bf16"),
+    ("noncausal_S5_g1_D64", [3, 70, 1], [3, 70, 1], [10, 0, 257], 4, 4, 64, 5, False, "bf16"),
+    ("S1_g8", [2, 9], [2, 9], [130, 5], 8, 1, 128, 1, True, "bf16"),
+    ("S64_fp8", [100, 1, 1, 33], [100, 1, 1, 33], [0, 900, 64, 129], 8, 2, 128, 64, True, "fp8"),
+    ("fp8_D64_S4_noncausal", [5, 66], [5, 66], [31, 2], 4, 2, 64, 4, False, "fp8"),
+    ("no_cache_prefill", [1, 130, 257, 64], [1, 130, 257, 64], [0, 0, 0, 0], 8, 2, 128, 0, True, None),
+    ("no_cache_noncausal_D64", [17, 3, 300], [17, 3, 300], [0, 0, 0], 4, 1, 64, 0, False, None),
+    ("q_longer_than_kv", [10, 4], [3, 0], [0, 2], 4, 2, 128, 16, True, "bf16"),
+    ("empty_sequences", [0, 5, 0, 1], [0, 5, 0, 0], [3, 0, 0, 0], 4, 2, 128, 16, True, "bf16"),
+    ("zero_kv_all_rows_dead", [4], [0], [0], 4, 2, 128, 16, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases(case):
+    label, ql, nl, cl, hq, hkv, d, s, causal, cache = case
+    wl = make_custom(q_lens=ql, new_lens=nl, cache_lens=cl, Hq=hq, Hkv=hkv, D=d, page_size=s,
+                     causal=causal, cache_dtype=cache, seed=zlib.crc32(label.encode()) % 1000)
+    _run_and_check(wl, label)
+
+
+def test_cache_only_no_new_tokens():
+    wl = make_custom(q_lens=[2, 1, 7], new_lens=None, cache_lens=[5, 300, 64], Hq=8, Hkv=2, D=128,
+                     page_size=16, seed=11)
+    _run_and_check(wl, "cache_only")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_poisoned_unused_slots(cache):
+    wl = make_custom(q_lens=[3, 1, 77], new_lens=[3, 1, 77], cache_lens=[13, 200, 5], Hq=8, Hkv=2,
+                     D=128, page_size=16, cache_dtype=cache, seed=12, poison=True)
+    _run_and_check(wl, f"poison_{cache}")
+
+
+def _medium(seed=13, cache="bf16"):
+    return make_custom(q_lens=[1, 1, 150, 3], new_lens=[1, 1, 150, 3], cache_lens=[2000, 700, 900, 64],
+                       Hq=8, Hkv=2, D=128, page_size=16, cache_dtype=cache, seed=seed)
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_split_invariance(cache):
+    wl = _medium(cache=cache)
+    ref = oracle_full(wl)
+    kind = "fp8" if cache == "fp8" else "bf16"
+    results = []
+    for n in (1, 2, 7):
+        vpk.set_option("force_splits", n)
+        say(f"[case] split_invariance {cache} force_splits={n}")
+        out, lse = DeviceCall(wl).run()
+        torch.cuda.synchronize()
+        o, l = to_np_out(out), lse.cpu().numpy().astype(np.float64)
+        check_attention(o, l, ref["out"], ref["lse"], kind, label=f"splits={n}")
+        results.append((o, l))
+    for o, l in results[1:]:
+        assert np.abs(l - results[0][1]).max() <= 1e-5
+        assert np.abs(o - results[0][0]).max() <= 1.6e-2
+
+
+def test_persistent_schedule_is_bitwise_identical():
+    wl = _medium(seed=14)
+    outs = []
+    for mode in (0, 1):
+        vpk.set_option("persistent", mode)
+        say(f"[case] persistent={mode}")
+        out, lse = DeviceCall(wl).run()
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_deterministic_and_idempotent_append():
+    wl = _medium(seed=15)
+    dc = DeviceCall(wl)
+    say("[case] determinism run 1")
+    o1, l1 = dc.run()
+    k1, v1 = dc.cache_host()
+    say("[case] determinism run 2 (same cache, append repeated)")
+    o2, l2 = dc.run()
+    k2, v2 = dc.cache_host()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_non_default_stream():
+    wl = _medium(seed=16)
+    s = torch.cuda.Stream()
+    dc = DeviceCall(wl)
+    say("[case] non-default stream")
+    with torch.cuda.stream(s):
+        out, lse = dc.run(stream=s)
+    s.synchronize()
+    ref = oracle_full(wl)
+    check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                    label="stream")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_append_entry_point_bit_exact(cache):
+    wl = make_custom(q_lens=[5, 1, 40], new_lens=[5, 1, 40], cache_lens=[3, 64, 0], Hq=4, Hkv=2,
+                     D=128, page_size=16, cache_dtype=cache, seed=17)
+    dc = DeviceCall(wl)
+    say(f"[case] kv_cache_append {cache}")
+    for _ in range(2):   # idempotent
+        vpk.kv_cache_append(dc.k_new, dc.v_new, dc.cu_kn, dc.k_cache, dc.v_cache, dc.bt, dc.cl,
+                            wl.page_size, wl.kv_scale if cache == "fp8" else None,
+                            host_index=dc.host)
+        kc, vc = dc.cache_host()
+        rk, rv = oracle.append(wl.k_new, wl.v_new, wl.cu_seqlens_knew, wl.k_cache, wl.v_cache,
+                               wl.block_table, wl.cache_seqlens, wl.page_size, cache, wl.kv_scale)
+        assert np.array_equal(kc, rk) and np.array_equal(vc, rv)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0137, 37.0, 2.0 ** -12])
+def test_fp8_encoder_every_bf16_pattern(scale):
+    # all 65536 bf16 bit patterns (NaN and inf included) as 512 new tokens of one
+    # sequence with Hkv = 1, D = 128, appended into an fp8 cache
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(512, 1, 128)
+    P, S = 32, 16
+    k_cache = np.zeros((P, S, 1, 128), np.uint8)
+    bt = np.random.default_rng(18).permutation(P).astype(np.int32)[None, :]
+    cu = np.array([0, 512], np.int32)
+    cl = np.array([0], np.int32)
+    ks = (np.float32(scale), np.float32(scale * 3))
+    say(f"[case] fp8 encoder all patterns scale={scale}")
+    kc_d, vc_d = dev_u8(k_cache), dev_u8(k_cache.copy())
+    kn = dev_bf16(bits)
+    vn = dev_bf16(bits[::-1].copy())
+    vpk.kv_cache_append(kn, vn, dev_i32(cu), kc_d, vc_d, dev_i32(bt), dev_i32(cl), S, ks,
+                        host_index=dict(cu_seqlens_knew=cu, cache_seqlens=cl, block_table=bt))
+    rk, rv = oracle.append(bits, bits[::-1].copy(), cu, k_cache, k_cache.copy(), bt, cl, S, "fp8", ks)
+    assert np.array_equal(kc_d.cpu().numpy(), rk)
+    assert np.array_equal(vc_d.cpu().numpy(), rv)
+
+
+def _one_hot_case(S, cache, seed):
+    """Keys orthogonal (40 * e_code), each query aimed at one visible key: out must be that V row."""
+    rng = np.random.default_rng(seed)
+    D, Hq, Hkv = 128, 8, 2
+    g = Hq // Hkv
+    lens = [(3, 90), (5, 0), (1, 127), (20, 20)]          # (q_len, cache_len); new = q_len
+    B = len(lens)
+    ql = np.array([a for a, _ in lens]); cl = np.array([c for _, c in lens])
+    lk = ql + cl
+    wl = make_custom(q_lens=ql, new_lens=ql, cache_lens=cl, Hq=Hq, Hkv=Hkv, D=D, page_size=S,
+                     causal=True, cache_dtype=cache, seed=seed)
+    fp8 = cache == "fp8"
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    all_codes = []
+    K = np.zeros((int(lk.sum()), Hkv, D), np.float32)
+    V = np.zeros_like(K)
+    for b in range(B):
+        codes = rng.permutation(D)[: lk[b]]
+        for h in range(Hkv):
+            for j in range(lk[b]):
+                K[cu_k[b] + j, h, codes[j]] = 40.0
+                if fp8:   # distinct e4m3 values per key: code pattern
+                    V[cu_k[b] + j, h] = oracle.e4m3fn_decode(((np.arange(D) * 3 + j * 5 + h) % 100 + 8).astype(np.uint8))
+                else:
+                    V[cu_k[b] + j, h] = rng.standard_normal(D).astype(np.float32)
+        all_codes.append(codes)
+    Vb = to_bf16_bits(V)
+    Q = np.zeros((int(ql.sum()), Hq, D), np.float32)
+    target = np.zeros((int(ql.sum()), Hq), np.int64)
+    for b in range(B):
+        codes = all_codes[b]
+        for i in range(ql[b]):
+            t = wl.cu_seqlens_q[b] + i
+            for h in range(Hq):
+                last = i + lk[b] - ql[b]             # last visible key (end-aligned causal)
+                j = int(rng.integers(0, last + 1))
+                target[t, h] = cu_k[b] + j
+                Q[t, h, codes[j]] = 40.0
+    wl.q = to_bf16_bits(Q)
+    new_idx = np.concatenate([np.arange(cu_k[b] + cl[b], cu_k[b + 1]) for b in range(B)])
+    Kb = to_bf16_bits(K)
+    wl.k_new, wl.v_new = Kb[new_idx], Vb[new_idx]
+    if fp8:
+        wl.kv_scale = (np.float32(1.0), np.float32(1.0))
+    for b in range(B):
+        for j in range(cl[b]):
+            page, slot = wl.block_table[b, j // S], j % S
+            if fp8:
+                wl.k_cache[page, slot] = oracle.e4m3fn_encode(K[cu_k[b] + j])
+                wl.v_cache[page, slot] = oracle.e4m3fn_encode(V[cu_k[b] + j])
+            else:
+                wl.k_cache[page, slot] = Kb[cu_k[b] + j]
+                wl.v_cache[page, slot] = Vb[cu_k[b] + j]
+    expect = np.zeros((int(ql.sum()), Hq, D), np.uint16)
+    for t in range(int(ql.sum())):
+        for h in range(Hq):
+            expect[t, h] = Vb[target[t, h], h // g]
+    return wl, expect
+
+
+@pytest.mark.parametrize("S", [1, 4, 16, 64])
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_one_hot_gather_probe_bit_exact(S, cache):
+    wl, expect = _one_hot_case(S, cache, seed=S * 10 + (cache == "fp8"))
+    say(f"[case] one-hot probe S={S} cache={cache}")
+    out, _ = DeviceCall(wl).run()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"first mismatches at {bad[:5].tolist()}"
+
+
+FULL = ["varlen_prefill", "paged_decode", "chunked_prefill", "mixed_fp8"]
+SAMPLE = {"varlen_prefill": 3, "paged_decode": 8, "chunked_prefill": 2, "mixed_fp8": 7}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workloads_sampled(name):
+    wl = make_workload(name)
+    say(f"[case] full size {name}: Tq={wl.Tq} Tn={wl.Tn} pages={wl.num_pages}")
+    dc = DeviceCall(wl)
+    out, lse = dc.run()
+    torch.cuda.synchronize()
+    o_all = to_np_out(out)
+    l_all = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o_all)) and np.all(np.isfinite(l_all))
+    # appended slots, bit-exact, through the oracle's own append
+    kc_ref, vc_ref = (oracle.append(wl.k_new, wl.v_new, wl.cu_seqlens_knew, wl.k_cache, wl.v_cache,
+                                    wl.block_table, wl.cache_seqlens, wl.page_size, wl.cache_dtype,
+                                    wl.kv_scale) if wl.k_cache is not None else (None, None))
+    if kc_ref is not None:
+        kc, vc = dc.cache_host()
+        assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+    # sampled sequences: the longest one plus random ones
+    rng = np.random.default_rng(99)
+    ql = wl.q_lens()
+    pick = {int(np.argmax(wl.kv_lens() * np.maximum(ql, 1)))}
+    if name == "mixed_fp8":
+        pick |= {int(rng.integers(0, 4))} | set(int(x) for x in rng.choice(np.arange(4, wl.B), 5, replace=False))
+    else:
+        pick |= set(int(x) for x in rng.choice(wl.B, SAMPLE[name] - 1, replace=False))
+    kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
+    Qf = oracle.bf16_bits_to_f64
+    for b in sorted(pick):
+        s, e = int(wl.cu_seqlens_q[b]), int(wl.cu_seqlens_q[b + 1])
+        K, V = oracle.sequence_kv(b, k_new=wl.k_new, v_new=wl.v_new,
+                                  cu_seqlens_knew=wl.cu_seqlens_knew, k_cache=kc_ref,
+                                  v_cache=vc_ref, block_table=wl.block_table,
+                                  cache_seqlens=wl.cache_seqlens, page_size=wl.page_size,
+                                  cache_dtype=wl.cache_dtype, kv_scale=wl.kv_scale)
+        ro, rl = oracle.attend(Qf(wl.q[s:e]), K, V, wl.causal, wl.scale)
+        check_attention(o_all[s:e], l_all[:, s:e], ro, rl, kind, label=f"{name} seq {b}")
+    say(f"[ok] {name}: sequences {sorted(pick)}")

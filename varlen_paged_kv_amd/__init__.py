@@ -1,0 +1,246 @@
+"""varlen_paged_kv_amd: varlen attention over a paged KV cache on MI355X (gfx950).
+
+Thin Python binding over libvpk.so (C ABI in include/vpk.h).  PyTorch supplies
+device memory and the current HIP stream; every step of the computation (the
+in-place append, the page gather, both MFMA contractions, the online softmax,
+the split merge) runs in the library's HIP kernels.  There is no fallback: if
+the library is missing or the tensors are not on a GPU, the calls raise.
+
+    out, lse = attn_varlen_paged_fwd(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew,
+                                     k_cache, v_cache, block_table, cache_seqlens,
+                                     page_size, causal, scale, kv_scale)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import VpkDims, VpkHostIndex
+
+__all__ = ["attn_varlen_paged_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
+           "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug",
+           "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_MERGE"]
+
+KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_MERGE = 0, 1, 2
+
+
+class VpkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_lib.STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+        self.msg = msg
+
+
+def _check(status: int):
+    if status != _lib.VPK_SUCCESS:
+        raise VpkError(status, _lib.load().vpk_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} must be contiguous")
+    return t
+
+
+def _host_i32(x) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+_BF16 = (torch.bfloat16,)
+_I32 = (torch.int32,)
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _host_index(cu_q, cu_kn, cache_lens, block_table):
+    keep = [_host_i32(cu_q), _host_i32(cu_kn), _host_i32(cache_lens), _host_i32(block_table)]
+    hi = VpkHostIndex(*[None if a is None else a.ctypes.data for a in keep])
+    return hi, keep
+
+
+def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                          cu_seqlens_knew: Optional[torch.Tensor] = None,
+                          k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
+                          block_table: Optional[torch.Tensor] = None,
+                          cache_seqlens: Optional[torch.Tensor] = None,
+                          page_size: int = 0, causal: bool = True, scale: Optional[float] = None,
+                          kv_scale: Optional[Sequence[float]] = None, *,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True, host_index: Optional[dict] = None,
+                          stream=None):
+    """Append k_new/v_new into the paged cache (if both are given), then attend.
+
+    Shapes: q [Tq, Hq, D] bf16; k_new/v_new [Tn, Hkv, D] bf16; caches
+    [P, S, Hkv, D] bf16 or fp8 e4m3fn (uint8 / float8_e4m3fn); block_table
+    [B, max_pages] int32; cu_seqlens_* [B + 1] int32; cache_seqlens [B] int32.
+    ``host_index`` may hold host copies (CPU tensors or arrays) under the keys
+    cu_seqlens_q, cu_seqlens_knew, cache_seqlens, block_table; missing ones are
+    read back from the device by the library (a blocking copy).
+    Returns (out [Tq, Hq, D] bf16, lse [Hq, Tq] fp32 or None).
+    """
+    lib = _lib.load()
+    q = _dev(q, "q", _BF16)
+    cu_seqlens_q = _dev(cu_seqlens_q, "cu_seqlens_q", _I32)
+    k_new = _dev(k_new, "k_new", _BF16)
+    v_new = _dev(v_new, "v_new", _BF16)
+    cu_seqlens_knew = _dev(cu_seqlens_knew, "cu_seqlens_knew", _I32)
+    fp8 = k_cache is not None and k_cache.dtype in _FP8
+    k_cache = _dev(k_cache, "k_cache", _FP8 if fp8 else _BF16)
+    v_cache = _dev(v_cache, "v_cache", _FP8 if fp8 else _BF16)
+    block_table = _dev(block_table, "block_table", _I32)
+    cache_seqlens = _dev(cache_seqlens, "cache_seqlens", _I32)
+    if q.dim() != 3:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "q must be [total_q, num_q_heads, head_dim]")
+    Tq, Hq, D = q.shape
+    B = cu_seqlens_q.numel() - 1
+    Hkv = (k_new if k_new is not None else k_cache).shape[-2]
+    Tn = 0 if k_new is None else k_new.shape[0]
+    P = 0 if k_cache is None else k_cache.shape[0]
+    for name, t, shp in (("k_new", k_new, (Tn, Hkv, D)), ("v_new", v_new, (Tn, Hkv, D)),
+                         ("k_cache", k_cache, (P, page_size, Hkv, D)),
+                         ("v_cache", v_cache, (P, page_size, Hkv, D))):
+        if t is not None and tuple(t.shape) != shp:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    maxp = 0 if block_table is None else block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    dims = VpkDims(B, Tq, Tn, Hq, Hkv, D, P, maxp,
+                   _lib.VPK_DTYPE_FP8_E4M3FN if fp8 else _lib.VPK_DTYPE_BF16)
+    ks = None
+    if fp8:
+        if kv_scale is None:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache")
+        ks = (ctypes.c_float * 2)(float(kv_scale[0]), float(kv_scale[1]))
+    h = host_index or {}
+    hi, keep = _host_index(h.get("cu_seqlens_q"), h.get("cu_seqlens_knew"),
+                           h.get("cache_seqlens"), h.get("block_table"))
+    st = lib.attn_varlen_paged_fwd(ctypes.byref(dims), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_new),
+                                   _ptr(v_new), _ptr(cu_seqlens_knew), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens),
+                                   int(page_size), int(bool(causal)), float(scale), ks,
+                                   _ptr(out), _ptr(lse), ctypes.byref(hi), _stream_handle(stream))
+    del keep
+    _check(st)
+    return out, lse
+
+
+def kv_cache_append(k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table, cache_seqlens,
+                    page_size: int, kv_scale=None, *, host_index: Optional[dict] = None, stream=None):
+    """Store k_new/v_new into the paged cache at positions [Lc, Lc + Ln) of each sequence."""
+    lib = _lib.load()
+    fp8 = k_cache.dtype in _FP8
+    k_new = _dev(k_new, "k_new", _BF16)
+    v_new = _dev(v_new, "v_new", _BF16)
+    cu_seqlens_knew = _dev(cu_seqlens_knew, "cu_seqlens_knew", _I32)
+    k_cache = _dev(k_cache, "k_cache", _FP8 if fp8 else _BF16)
+    v_cache = _dev(v_cache, "v_cache", _FP8 if fp8 else _BF16)
+    block_table = _dev(block_table, "block_table", _I32)
+    cache_seqlens = _dev(cache_seqlens, "cache_seqlens", _I32)
+    Tn, Hkv, D = k_new.shape
+    B = cu_seqlens_knew.numel() - 1
+    dims = VpkDims(B, 0, Tn, Hkv, Hkv, D, k_cache.shape[0], block_table.shape[1],
+                   _lib.VPK_DTYPE_FP8_E4M3FN if fp8 else _lib.VPK_DTYPE_BF16)
+    ks = None
+    if fp8:
+        ks = (ctypes.c_float * 2)(float(kv_scale[0]), float(kv_scale[1]))
+    h = host_index or {}
+    hi, keep = _host_index(None, h.get("cu_seqlens_knew"), h.get("cache_seqlens"), h.get("block_table"))
+    st = lib.kv_cache_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_knew),
+                             _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens),
+                             int(page_size), ks, ctypes.byref(hi), _stream_handle(stream))
+    del keep
+    _check(st)
+
+
+def set_option(name: str, value: int):
+    _check(_lib.load().vpk_set_option(name.encode(), int(value)))
+
+
+def abi_version() -> int:
+    return int(_lib.load().vpk_abi_version())
+
+
+def timing_enable(on: bool = True):
+    _check(_lib.load().vpk_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(_lib.load().vpk_timing_reset())
+
+
+def timing_read(kernel: int):
+    """(total milliseconds, launches) of one kernel since the last reset."""
+    ms = ctypes.c_double(0)
+    n = ctypes.c_int64(0)
+    _check(_lib.load().vpk_timing_read(int(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def device_error(stream=None) -> int:
+    f = ctypes.c_int32(0)
+    _check(_lib.load().vpk_device_error(_stream_handle(stream), ctypes.byref(f)))
+    return f.value
+
+
+def plan_debug(*, batch, num_q_heads, num_kv_heads, head_dim, cu_seqlens_q, cu_seqlens_knew=None,
+               cache_seqlens=None, block_table=None, page_size=1, causal=True, num_cus=256,
+               has_cache=None, num_pages=None, kv_cache_dtype="bf16", capacity=None):
+    """Host-only view of the attention work list: int32 array [n_items, 8] and the queue count."""
+    lib = _lib.load()
+    cu_q = _host_i32(cu_seqlens_q)
+    cu_kn = _host_i32(cu_seqlens_knew)
+    cl = _host_i32(cache_seqlens)
+    bt = _host_i32(block_table)
+    has_cache = (cl is not None) if has_cache is None else has_cache
+    has_new = cu_kn is not None
+    maxp = bt.shape[1] if bt is not None else (1 << 20)
+    if num_pages is None:
+        num_pages = (int(bt.max()) + 1) if bt is not None and bt.size else (1 << 20)
+    dims = VpkDims(batch, int(cu_q[-1]), int(cu_kn[-1]) if has_new else 0, num_q_heads,
+                   num_kv_heads, head_dim, num_pages if has_cache else 0, maxp,
+                   _lib.VPK_DTYPE_FP8_E4M3FN if kv_cache_dtype == "fp8" else _lib.VPK_DTYPE_BF16)
+    hi, keep = _host_index(cu_q, cu_kn, cl, bt)
+    cap = capacity if capacity is not None else 1 << 16
+    while True:
+        buf = np.zeros((cap, 8), np.int32)
+        n = ctypes.c_int32(0)
+        nq = ctypes.c_int32(0)
+        st = lib.vpk_plan_debug(ctypes.byref(dims), ctypes.byref(hi), int(has_cache), int(has_new),
+                                int(page_size), int(bool(causal)), int(num_cus),
+                                buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap,
+                                ctypes.byref(n), ctypes.byref(nq))
+        if st == _lib.VPK_ERROR_CAPACITY and n.value > cap and capacity is None:
+            cap = n.value
+            continue
+        _check(st)
+        del keep
+        return buf[:n.value].copy(), nq.value

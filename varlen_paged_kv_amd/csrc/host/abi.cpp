@@ -1,0 +1,730 @@
+// C ABI of libvpk: argument checks, host mirrors, planning, workspace and
+// launches.  Nothing here throws across the boundary; every failure becomes a
+// vpk_status plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../../include/vpk.h"
+#include "../vpk_internal.h"
+#include "plan.h"
+
+namespace {
+
+using vpk::AppendParams;
+using vpk::AttnParams;
+using vpk::MergeGroup;
+using vpk::MergeParams;
+using vpk::Plan;
+using vpk::PlanInput;
+using vpk::SeqInfo;
+using vpk::WorkItem;
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(VPK_ERROR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct Options {
+  std::atomic<int64_t> force_splits{0};
+  std::atomic<int64_t> persistent{-1};
+  std::atomic<int64_t> split_min_keys{256};
+  std::atomic<int64_t> num_cus{0};
+} g_opt;
+
+// ------------------------------------------------------------------ timing
+
+struct TimingRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+std::mutex g_tmu;
+std::atomic<bool> g_timing{false};
+std::vector<TimingRec> g_tpending;
+std::vector<hipEvent_t> g_tfree;
+double g_tms[3] = {0, 0, 0};
+int64_t g_tcount[3] = {0, 0, 0};
+
+hipEvent_t take_event() {
+  if (!g_tfree.empty()) {
+    hipEvent_t e = g_tfree.back();
+    g_tfree.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct KernelTimer {
+  int kernel;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  KernelTimer(int k, hipStream_t st) : kernel(k), s(st) {
+    if (!g_timing.load()) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    a = take_event();
+    b = take_event();
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~KernelTimer() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_tpending.push_back(TimingRec{kernel, a, b});
+  }
+};
+
+// --------------------------------------------------------------- workspace
+
+struct Staging {
+  void* host = nullptr;
+  size_t bytes = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+struct Workspace {
+  int device = -1;
+  char* dev = nullptr;
+  size_t bytes = 0;
+  Staging stage[4];
+  int next = 0;
+};
+
+std::mutex g_wmu;
+std::map<std::pair<int, void*>, Workspace*> g_ws;
+
+constexpr size_t kFlagBytes = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t get_workspace(hipStream_t stream, size_t need, Workspace** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_wmu);
+  Workspace*& w = g_ws[std::make_pair(dev, static_cast<void*>(stream))];
+  if (!w) {
+    w = new (std::nothrow) Workspace();
+    if (!w) return fail(VPK_ERROR_OUT_OF_MEMORY, "workspace bookkeeping");
+    w->device = dev;
+  }
+  if (w->bytes < need) {
+    if (w->dev) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (workspace growth)");
+      (void)hipFree(w->dev);
+      w->dev = nullptr;
+      w->bytes = 0;
+    }
+    const size_t bytes = align_up(std::max(need + need / 2, static_cast<size_t>(1) << 20), 1 << 20);
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
+    e = hipMemset(p, 0, kFlagBytes);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "hipMemset workspace flag");
+    }
+    w->dev = static_cast<char*>(p);
+    w->bytes = bytes;
+  }
+  *out = w;
+  return VPK_SUCCESS;
+}
+
+// Copy `bytes` of host data into the workspace at `dst_off` through a pinned
+// staging buffer (4 in rotation; a buffer is reused once its copy finished).
+int32_t stage_upload(Workspace* w, hipStream_t stream, const void* src, size_t bytes, size_t dst_off) {
+  if (bytes == 0) return VPK_SUCCESS;
+  Staging& st = w->stage[w->next];
+  w->next = (w->next + 1) % 4;
+  hipError_t e;
+  if (st.pending) {
+    e = hipEventSynchronize(st.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
+    st.pending = false;
+  }
+  if (!st.ev) {
+    e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
+  }
+  if (st.bytes < bytes) {
+    if (st.host) (void)hipHostFree(st.host);
+    st.host = nullptr;
+    st.bytes = 0;
+    const size_t nb = align_up(std::max(bytes + bytes / 2, static_cast<size_t>(64) << 10), 4096);
+    e = hipHostMalloc(&st.host, nb, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    st.bytes = nb;
+  }
+  std::memcpy(st.host, src, bytes);
+  e = hipMemcpyAsync(w->dev + dst_off, st.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
+  e = hipEventRecord(st.ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
+  st.pending = true;
+  return VPK_SUCCESS;
+}
+
+// ---------------------------------------------------------- host mirrors
+
+int32_t fetch_index(const int32_t* dev, size_t n, hipStream_t stream, std::vector<int32_t>& buf,
+                    const int32_t** out) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(VPK_ERROR_NOT_SUPPORTED, "host mirrors are required during stream capture");
+  buf.resize(n);
+  if (n) {
+    hipError_t e = hipMemcpyAsync(buf.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (index array to host)");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (index array to host)");
+  }
+  *out = buf.data();
+  return VPK_SUCCESS;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Mirrors {
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_kn = nullptr;
+  const int32_t* cache_lens = nullptr;
+  const int32_t* block_table = nullptr;   // may stay null (no host check)
+  std::vector<int32_t> b1, b2, b3;
+};
+
+struct Call {
+  const vpk_dims* d;
+  bool has_new, has_cache, fp8;
+  int32_t page_size;
+  const float* kv_scale;
+};
+
+int32_t check_cu(const int32_t* cu, int32_t B, int32_t total, const char* name) {
+  if (cu[0] != 0) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + "[0] must be 0");
+  for (int32_t b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b]) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + " must be non-decreasing");
+  if (cu[B] != total)
+    return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + "[batch] must equal the total length");
+  return VPK_SUCCESS;
+}
+
+// Shape/pointer checks that need no index contents.
+int32_t check_dims(const Call& c) {
+  const vpk_dims* d = c.d;
+  if (!d) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
+  if (d->batch < 0 || d->total_q < 0 || d->total_knew < 0)
+    return fail(VPK_ERROR_INVALID_VALUE, "negative batch or length");
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(VPK_ERROR_INVALID_VALUE, "head counts must be positive");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(VPK_ERROR_INVALID_VALUE, "num_q_heads must be a multiple of num_kv_heads");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(VPK_ERROR_NOT_SUPPORTED, "head_dim must be 64 or 128");
+  if (static_cast<int64_t>(d->total_q) * d->num_q_heads > INT32_MAX ||
+      static_cast<int64_t>(d->total_knew) * d->num_kv_heads > INT32_MAX)
+    return fail(VPK_ERROR_NOT_SUPPORTED, "too many rows for 32-bit row indices");
+  if (c.has_cache) {
+    if (c.page_size < 1) return fail(VPK_ERROR_INVALID_VALUE, "page_size must be >= 1");
+    if (d->num_pages < 1) return fail(VPK_ERROR_INVALID_VALUE, "num_pages must be >= 1 with a cache");
+    if (d->max_pages_per_seq < 1) return fail(VPK_ERROR_INVALID_VALUE, "max_pages_per_seq must be >= 1");
+    if (static_cast<int64_t>(d->num_pages) * c.page_size > INT32_MAX ||
+        static_cast<int64_t>(d->max_pages_per_seq) * c.page_size > INT32_MAX)
+      return fail(VPK_ERROR_NOT_SUPPORTED, "too many cache slots for 32-bit slot indices");
+    if (d->kv_cache_dtype != VPK_DTYPE_BF16 && d->kv_cache_dtype != VPK_DTYPE_FP8_E4M3FN)
+      return fail(VPK_ERROR_INVALID_VALUE, "kv_cache_dtype must be VPK_DTYPE_BF16 or VPK_DTYPE_FP8_E4M3FN");
+    if (c.fp8) {
+      if (!c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache");
+      for (int i = 0; i < 2; ++i)
+        if (!std::isfinite(c.kv_scale[i]) || !(c.kv_scale[i] > 0.f))
+          return fail(VPK_ERROR_INVALID_VALUE, "kv_scale entries must be finite and > 0");
+    }
+  }
+  return VPK_SUCCESS;
+}
+
+int32_t get_mirrors(const Call& c, const int32_t* cu_q_dev, const int32_t* cu_kn_dev,
+                    const int32_t* cl_dev, const vpk_host_index* host, hipStream_t stream,
+                    bool need_q, Mirrors& m) {
+  const int32_t B = c.d->batch;
+  int32_t st;
+  if (need_q) {
+    if (host && host->cu_seqlens_q) m.cu_q = host->cu_seqlens_q;
+    else if ((st = fetch_index(cu_q_dev, B + 1, stream, m.b1, &m.cu_q)) != VPK_SUCCESS) return st;
+  }
+  if (c.has_new) {
+    if (host && host->cu_seqlens_knew) m.cu_kn = host->cu_seqlens_knew;
+    else if ((st = fetch_index(cu_kn_dev, B + 1, stream, m.b2, &m.cu_kn)) != VPK_SUCCESS) return st;
+  }
+  if (c.has_cache) {
+    if (host && host->cache_seqlens) m.cache_lens = host->cache_seqlens;
+    else if ((st = fetch_index(cl_dev, B, stream, m.b3, &m.cache_lens)) != VPK_SUCCESS) return st;
+    if (host && host->block_table) m.block_table = host->block_table;
+  }
+  return VPK_SUCCESS;
+}
+
+// Length and page checks on the host mirrors.
+int32_t check_contents(const Call& c, const Mirrors& m, bool need_q) {
+  const vpk_dims* d = c.d;
+  const int32_t B = d->batch;
+  int32_t st;
+  if (need_q && (st = check_cu(m.cu_q, B, d->total_q, "cu_seqlens_q")) != VPK_SUCCESS) return st;
+  if (c.has_new && (st = check_cu(m.cu_kn, B, d->total_knew, "cu_seqlens_knew")) != VPK_SUCCESS) return st;
+  if (c.has_cache) {
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t lc = m.cache_lens[b];
+      if (lc < 0) return fail(VPK_ERROR_INVALID_VALUE, "cache_seqlens must be >= 0");
+      const int64_t ln = c.has_new ? m.cu_kn[b + 1] - m.cu_kn[b] : 0;
+      const int64_t lk = lc + ln;
+      if (lk > static_cast<int64_t>(d->max_pages_per_seq) * c.page_size)
+        return fail(VPK_ERROR_CAPACITY, "sequence " + std::to_string(b) + " needs " +
+                                            std::to_string(lk) + " slots, block_table row holds " +
+                                            std::to_string(static_cast<int64_t>(d->max_pages_per_seq) * c.page_size));
+      if (m.block_table) {
+        const int64_t np = (lk + c.page_size - 1) / c.page_size;
+        const int32_t* row = m.block_table + static_cast<int64_t>(b) * d->max_pages_per_seq;
+        for (int64_t i = 0; i < np; ++i)
+          if (row[i] < 0 || row[i] >= d->num_pages)
+            return fail(VPK_ERROR_INVALID_VALUE, "block_table[" + std::to_string(b) + "][" +
+                                                     std::to_string(i) + "] = " + std::to_string(row[i]) +
+                                                     " is outside [0, num_pages)");
+      }
+    }
+  }
+  return VPK_SUCCESS;
+}
+
+int32_t device_cus() {
+  const int64_t forced = g_opt.num_cus.load();
+  if (forced > 0) return static_cast<int32_t>(forced);
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t num_cus, PlanInput& in) {
+  in.batch = c.d->batch;
+  in.hq = c.d->num_q_heads;
+  in.hkv = c.d->num_kv_heads;
+  in.head_dim = c.d->head_dim;
+  in.has_cache = c.has_cache;
+  in.has_new = c.has_new;
+  in.causal = causal != 0;
+  in.page_size = c.has_cache ? c.page_size : 1;
+  in.kv_bytes = c.fp8 ? 1 : 2;
+  in.cu_q = m.cu_q;
+  in.cu_kn = m.cu_kn;
+  in.cache_lens = m.cache_lens;
+  in.num_cus = num_cus;
+  in.force_splits = static_cast<int32_t>(g_opt.force_splits.load());
+  in.persistent = static_cast<int32_t>(g_opt.persistent.load());
+  in.split_min_keys = static_cast<int32_t>(g_opt.split_min_keys.load());
+}
+
+// Workspace layout: [flag][seqs][cu_knew][items][groups][queues] | [part_o][part_lse]
+struct Layout {
+  size_t seqs, cu_kn, items, groups, queues, plan_end, part_o, part_lse, total;
+};
+
+Layout layout_for(const Plan& p, int32_t B, int32_t D) {
+  Layout L;
+  L.seqs = kFlagBytes;
+  L.cu_kn = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
+  L.items = align_up(L.cu_kn + sizeof(int32_t) * (B + 1), 64);
+  L.groups = align_up(L.items + sizeof(WorkItem) * p.items.size(), 64);
+  L.queues = align_up(L.groups + sizeof(MergeGroup) * p.groups.size(), 64);
+  L.plan_end = align_up(L.queues + sizeof(int32_t) * p.queue_start.size(), 256);
+  L.part_o = L.plan_end;
+  L.part_lse = align_up(L.part_o + sizeof(float) * D * static_cast<size_t>(p.part_rows), 256);
+  L.total = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
+  return L;
+}
+
+int32_t upload_plan(Workspace* w, hipStream_t stream, const Plan& p, const Layout& L,
+                    const int32_t* cu_kn, int32_t B) {
+  std::vector<char> buf(L.plan_end - L.seqs, 0);
+  char* base = buf.data() - L.seqs;
+  if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
+  if (cu_kn) std::memcpy(base + L.cu_kn, cu_kn, sizeof(int32_t) * (B + 1));
+  if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
+  if (!p.groups.empty()) std::memcpy(base + L.groups, p.groups.data(), sizeof(MergeGroup) * p.groups.size());
+  if (!p.queue_start.empty())
+    std::memcpy(base + L.queues, p.queue_start.data(), sizeof(int32_t) * p.queue_start.size());
+  return stage_upload(w, stream, buf.data(), buf.size(), L.seqs);
+}
+
+int32_t enqueue_append(const Call& c, Workspace* w, const Layout& L, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache,
+                       const int32_t* block_table, hipStream_t stream) {
+  const vpk_dims* d = c.d;
+  AppendParams ap{};
+  ap.k_new = static_cast<const uint16_t*>(k_new);
+  ap.v_new = static_cast<const uint16_t*>(v_new);
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.block_table = block_table;
+  ap.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
+  ap.cu_knew = reinterpret_cast<const int32_t*>(w->dev + L.cu_kn);
+  ap.err_flag = reinterpret_cast<int32_t*>(w->dev);
+  ap.batch = d->batch;
+  ap.total_knew = d->total_knew;
+  ap.max_pages = d->max_pages_per_seq;
+  ap.num_pages = d->num_pages;
+  ap.page_size = c.page_size;
+  ap.row_elems = d->num_kv_heads * d->head_dim;
+  ap.fp8 = c.fp8 ? 1 : 0;
+  ap.k_inv_scale = c.fp8 ? 1.0f / c.kv_scale[0] : 1.0f;
+  ap.v_inv_scale = c.fp8 ? 1.0f / c.kv_scale[1] : 1.0f;
+  KernelTimer tm(1, stream);
+  const int rc = vpk::launch_append(ap, stream);
+  if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "append launch");
+  return VPK_SUCCESS;
+}
+
+int32_t check_ptr(const void* p, size_t a, const char* name) {
+  if (!p) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + " is NULL");
+  if (!aligned(p, a)) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + " is not " + std::to_string(a) + "-byte aligned");
+  return VPK_SUCCESS;
+}
+
+int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
+                  const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
+                  void* k_cache, void* v_cache, const int32_t* block_table,
+                  const int32_t* cache_seqlens, int32_t page_size, int32_t causal, float scale,
+                  const float* kv_scale, void* out, float* lse, const vpk_host_index* host,
+                  void* stream_v) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
+  Call c{dims, k_new != nullptr || v_new != nullptr, k_cache != nullptr || v_cache != nullptr,
+         dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN && (k_cache || v_cache), page_size, kv_scale};
+  int32_t st = check_dims(c);
+  if (st != VPK_SUCCESS) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_new and v_new must both be given or both be NULL");
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_cache and v_cache must both be given or both be NULL");
+  if (!c.has_new && !c.has_cache) return fail(VPK_ERROR_INVALID_VALUE, "no keys: give k_new/v_new, a cache, or both");
+  if (causal != 0 && causal != 1) return fail(VPK_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite");
+  if (!c.has_new && dims->total_knew != 0) return fail(VPK_ERROR_INVALID_VALUE, "total_knew must be 0 without k_new");
+  if (!c.has_cache && (dims->num_pages != 0)) return fail(VPK_ERROR_INVALID_VALUE, "num_pages must be 0 without a cache");
+  if (!c.fp8 && kv_scale && c.has_cache) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
+  const int32_t B = dims->batch;
+  if (!cu_seqlens_q && !(host && host->cu_seqlens_q)) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_q is NULL");
+  if (c.has_new) {
+    if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
+    if (!cu_seqlens_knew) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew is NULL while k_new is given");
+  } else if (cu_seqlens_knew) {
+    return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew must be NULL without k_new");
+  }
+  if (c.has_cache) {
+    if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
+    if ((st = check_ptr(block_table, 4, "block_table"))) return st;
+    if ((st = check_ptr(cache_seqlens, 4, "cache_seqlens"))) return st;
+  }
+  if (dims->total_q > 0) {
+    if ((st = check_ptr(q, 16, "q")) || (st = check_ptr(out, 16, "out"))) return st;
+    if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+  }
+  if (B == 0) return VPK_SUCCESS;
+
+  Mirrors m;
+  if ((st = get_mirrors(c, cu_seqlens_q, cu_seqlens_knew, cache_seqlens, host, stream, true, m))) return st;
+  if ((st = check_contents(c, m, true))) return st;
+
+  PlanInput in;
+  fill_plan_input(c, m, causal, device_cus(), in);
+  Plan plan;
+  try {
+    vpk::build_plan(in, plan);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
+  }
+  const Layout L = layout_for(plan, B, dims->head_dim);
+  Workspace* w = nullptr;
+  if ((st = get_workspace(stream, L.total, &w))) return st;
+  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B))) return st;
+
+  if (c.has_cache && c.has_new && dims->total_knew > 0) {
+    if ((st = enqueue_append(c, w, L, k_new, v_new, k_cache, v_cache, block_table, stream))) return st;
+  }
+  if (plan.grid > 0) {
+    AttnParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = c.has_cache ? k_cache : k_new;
+    p.v = c.has_cache ? v_cache : v_new;
+    p.block_table = block_table;
+    p.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
+    p.items = reinterpret_cast<const WorkItem*>(w->dev + L.items);
+    p.queue_start = reinterpret_cast<const int32_t*>(w->dev + L.queues);
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.part_o = reinterpret_cast<float*>(w->dev + L.part_o);
+    p.part_lse = reinterpret_cast<float*>(w->dev + L.part_lse);
+    p.err_flag = reinterpret_cast<int32_t*>(w->dev);
+    p.num_items = static_cast<int32_t>(plan.items.size());
+    p.persistent = plan.persistent ? 1 : 0;
+    p.max_pages = dims->max_pages_per_seq;
+    p.num_pages = dims->num_pages;
+    p.page_size = c.has_cache ? page_size : 1;
+    p.page_shift = -1;
+    if (c.has_cache && (page_size & (page_size - 1)) == 0) {
+      int s = 0;
+      while ((1 << s) < page_size) ++s;
+      p.page_shift = s;
+    }
+    p.hq = dims->num_q_heads;
+    p.hkv = dims->num_kv_heads;
+    p.g = dims->num_q_heads / dims->num_kv_heads;
+    p.total_q = dims->total_q;
+    p.causal = causal;
+    const double log2e = 1.4426950408889634;
+    p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
+                                         (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
+    p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
+    KernelTimer tm(0, stream);
+    const int rc = vpk::launch_attention(p, plan.grid, dims->head_dim,
+                                         c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16, c.has_cache, stream);
+    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
+  }
+  if (!plan.groups.empty()) {
+    MergeParams mp{};
+    mp.groups = reinterpret_cast<const MergeGroup*>(w->dev + L.groups);
+    mp.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
+    mp.part_o = reinterpret_cast<const float*>(w->dev + L.part_o);
+    mp.part_lse = reinterpret_cast<const float*>(w->dev + L.part_lse);
+    mp.out = static_cast<uint16_t*>(out);
+    mp.lse = lse;
+    mp.num_groups = static_cast<int32_t>(plan.groups.size());
+    mp.hq = dims->num_q_heads;
+    mp.g = dims->num_q_heads / dims->num_kv_heads;
+    mp.total_q = dims->total_q;
+    mp.head_dim = dims->head_dim;
+    KernelTimer tm(2, stream);
+    const int rc = vpk::launch_merge(mp, stream);
+    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
+  }
+  return VPK_SUCCESS;
+}
+
+int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
+                    const int32_t* cu_seqlens_knew, void* k_cache, void* v_cache,
+                    const int32_t* block_table, const int32_t* cache_seqlens, int32_t page_size,
+                    const float* kv_scale, const vpk_host_index* host, void* stream_v) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
+  Call c{dims, true, true, dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN, page_size, kv_scale};
+  int32_t st = check_dims(c);
+  if (st != VPK_SUCCESS) return st;
+  if (!c.fp8 && kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
+  if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
+  if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
+  if ((st = check_ptr(block_table, 4, "block_table")) || (st = check_ptr(cache_seqlens, 4, "cache_seqlens"))) return st;
+  if (!cu_seqlens_knew && !(host && host->cu_seqlens_knew)) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew is NULL");
+  const int32_t B = dims->batch;
+  if (B == 0 || dims->total_knew == 0) return VPK_SUCCESS;
+  Mirrors m;
+  if ((st = get_mirrors(c, nullptr, cu_seqlens_knew, cache_seqlens, host, stream, false, m))) return st;
+  if ((st = check_contents(c, m, false))) return st;
+  Plan plan;
+  plan.seqs.resize(B);
+  for (int32_t b = 0; b < B; ++b) {
+    SeqInfo s{};
+    s.new_len = m.cu_kn[b + 1] - m.cu_kn[b];
+    s.kn_start = m.cu_kn[b];
+    s.cache_len = m.cache_lens[b];
+    s.kv_len = s.cache_len + s.new_len;
+    plan.seqs[b] = s;
+  }
+  const Layout L = layout_for(plan, B, dims->head_dim);
+  Workspace* w = nullptr;
+  if ((st = get_workspace(stream, L.total, &w))) return st;
+  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B))) return st;
+  return enqueue_append(c, w, L, k_new, v_new, k_cache, v_cache, block_table, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_varlen_paged_fwd(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
+                              const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
+                              void* k_cache, void* v_cache, const int32_t* block_table,
+                              const int32_t* cache_seqlens, int32_t page_size, int32_t causal,
+                              float scale, const float* kv_scale, void* out, float* lse,
+                              const vpk_host_index* host, void* stream) {
+  try {
+    g_err.clear();
+    return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache,
+                     block_table, cache_seqlens, page_size, causal, scale, kv_scale, out, lse,
+                     host, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
+int32_t kv_cache_append(const vpk_dims* dims, const void* k_new, const void* v_new,
+                        const int32_t* cu_seqlens_knew, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* cache_seqlens,
+                        int32_t page_size, const float* kv_scale, const vpk_host_index* host,
+                        void* stream) {
+  try {
+    g_err.clear();
+    return append_impl(dims, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                       cache_seqlens, page_size, kv_scale, host, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
+const char* vpk_last_error(void) { return g_err.c_str(); }
+
+int32_t vpk_abi_version(void) { return VPK_ABI_VERSION; }
+
+int32_t vpk_set_option(const char* name, int64_t value) {
+  if (!name) return fail(VPK_ERROR_INVALID_VALUE, "option name is NULL");
+  const std::string n(name);
+  if (n == "force_splits") {
+    if (value < 0 || value > vpk::kMaxSplits) return fail(VPK_ERROR_INVALID_VALUE, "force_splits out of range");
+    g_opt.force_splits = value;
+  } else if (n == "persistent") {
+    if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "persistent must be -1, 0 or 1");
+    g_opt.persistent = value;
+  } else if (n == "split_min_keys") {
+    if (value < 1 || value > (1 << 24)) return fail(VPK_ERROR_INVALID_VALUE, "split_min_keys out of range");
+    g_opt.split_min_keys = value;
+  } else if (n == "num_cus") {
+    if (value < 0 || value > 4096) return fail(VPK_ERROR_INVALID_VALUE, "num_cus out of range");
+    g_opt.num_cus = value;
+  } else {
+    return fail(VPK_ERROR_INVALID_VALUE, "unknown option " + n);
+  }
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_timing_enable(int32_t enable) {
+  g_timing = enable != 0;
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (const TimingRec& r : g_tpending) {
+    (void)hipEventSynchronize(r.b);
+    g_tfree.push_back(r.a);
+    g_tfree.push_back(r.b);
+  }
+  g_tpending.clear();
+  for (int i = 0; i < 3; ++i) {
+    g_tms[i] = 0;
+    g_tcount[i] = 0;
+  }
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel > 2) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0, 1 or 2");
+  std::lock_guard<std::mutex> lk(g_tmu);
+  for (const TimingRec& r : g_tpending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (timing)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    g_tms[r.kernel] += ms;
+    g_tcount[r.kernel] += 1;
+    g_tfree.push_back(r.a);
+    g_tfree.push_back(r.b);
+  }
+  g_tpending.clear();
+  if (total_ms) *total_ms = g_tms[kernel];
+  if (launches) *launches = g_tcount[kernel];
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_device_error(void* stream_v, int32_t* flags) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  if (!flags) return fail(VPK_ERROR_INVALID_VALUE, "flags is NULL");
+  *flags = 0;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+  Workspace* w = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_wmu);
+    auto it = g_ws.find(std::make_pair(dev, stream_v));
+    if (it == g_ws.end() || !it->second->dev) return VPK_SUCCESS;
+    w = it->second;
+  }
+  int32_t v = 0;
+  if ((e = hipMemcpy(&v, w->dev, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy flag");
+  if ((e = hipMemset(w->dev, 0, sizeof(v))) != hipSuccess) return hip_fail(e, "hipMemset flag");
+  *flags = v;
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host, int32_t has_cache,
+                       int32_t has_new, int32_t page_size, int32_t causal, int32_t num_cus,
+                       int32_t* items, int32_t capacity, int32_t* n_items, int32_t* n_queues) {
+  try {
+    g_err.clear();
+    if (!dims || !host || !host->cu_seqlens_q) return fail(VPK_ERROR_INVALID_VALUE, "dims and host->cu_seqlens_q are required");
+    if (num_cus <= 0) return fail(VPK_ERROR_INVALID_VALUE, "num_cus must be > 0");
+    Call c{dims, has_new != 0, has_cache != 0, has_cache && dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN,
+           page_size, nullptr};
+    const float one[2] = {1.f, 1.f};
+    if (c.fp8) c.kv_scale = one;
+    int32_t st = check_dims(c);
+    if (st) return st;
+    if (c.has_new && !host->cu_seqlens_knew) return fail(VPK_ERROR_INVALID_VALUE, "host->cu_seqlens_knew is required");
+    if (c.has_cache && !host->cache_seqlens) return fail(VPK_ERROR_INVALID_VALUE, "host->cache_seqlens is required");
+    Mirrors m;
+    m.cu_q = host->cu_seqlens_q;
+    m.cu_kn = host->cu_seqlens_knew;
+    m.cache_lens = host->cache_seqlens;
+    m.block_table = host->block_table;
+    if ((st = check_contents(c, m, true))) return st;
+    PlanInput in;
+    fill_plan_input(c, m, causal, num_cus, in);
+    Plan plan;
+    vpk::build_plan(in, plan);
+    const int32_t n = static_cast<int32_t>(plan.items.size());
+    if (n_items) *n_items = n;
+    if (n_queues) *n_queues = plan.persistent ? static_cast<int32_t>(plan.queue_start.size()) - 1 : 0;
+    if (n > capacity) return fail(VPK_ERROR_CAPACITY, "items buffer too small");
+    for (int32_t i = 0; i < n; ++i) {
+      const WorkItem& it = plan.items[i];
+      int32_t* o = items + 8 * i;
+      o[0] = it.seq; o[1] = it.row0; o[2] = it.nrows; o[3] = it.kv_head;
+      o[4] = it.key_begin; o[5] = it.key_end; o[6] = it.part; o[7] = it.queue;
+    }
+    return VPK_SUCCESS;
+  } catch (...) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host exception in planner");
+  }
+}
+
+}  // extern "C"

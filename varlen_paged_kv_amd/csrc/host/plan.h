@@ -1,0 +1,47 @@
+// Host-side work planner for the attention launch (pure C++, no GPU needed).
+#pragma once
+
+#include <stdint.h>
+
+#include <vector>
+
+#include "../vpk_internal.h"
+
+namespace vpk {
+
+struct PlanInput {
+  int32_t batch = 0;
+  int32_t hq = 0;
+  int32_t hkv = 0;
+  int32_t head_dim = 0;
+  bool has_cache = false;
+  bool has_new = false;
+  bool causal = false;
+  int32_t page_size = 1;
+  int32_t kv_bytes = 2;                 // bytes per cached element (2 bf16, 1 fp8)
+  const int32_t* cu_q = nullptr;        // [B + 1] host
+  const int32_t* cu_kn = nullptr;       // [B + 1] host, or null
+  const int32_t* cache_lens = nullptr;  // [B] host, or null
+  int32_t num_cus = 256;
+  int32_t wg_per_cu = 2;                // resident attention workgroups per CU
+  // knobs
+  int32_t force_splits = 0;             // 0: planner decides
+  int32_t persistent = -1;              // -1 planner, 0 off, 1 on
+  int32_t split_min_keys = 256;
+};
+
+struct Plan {
+  std::vector<SeqInfo> seqs;
+  std::vector<WorkItem> items;          // launch order
+  std::vector<MergeGroup> groups;
+  std::vector<int32_t> queue_start;     // persistent only: num_queues + 1
+  int64_t part_rows = 0;                // rows of split partials
+  bool persistent = false;
+  int32_t grid = 0;                     // attention workgroups to launch
+};
+
+constexpr int32_t kMaxSplits = 64;
+
+void build_plan(const PlanInput& in, Plan& out);
+
+}  // namespace vpk

@@ -1,0 +1,127 @@
+// Internal structures shared by the host runtime and the HIP kernels of libvpk.
+#pragma once
+
+#include <stdint.h>
+
+namespace vpk {
+
+// Packed query rows handled by one workgroup: 4 wavefronts x 32 rows.  A row
+// is one (token, query head) pair of a sequence; the g = Hq / Hkv heads that
+// share a kv head are packed token-major (row = token * g + head_in_group), so
+// every K/V tile staged in LDS serves all of them.
+constexpr int kWaves = 4;
+constexpr int kWaveRows = 32;
+constexpr int kTileRows = kWaves * kWaveRows;   // 128
+constexpr int kThreads = kWaves * 64;           // 256
+constexpr int kBlockN = 64;                     // keys per inner iteration
+// Page ids of one work item are staged in LDS; an item may span at most this
+// many pages (the planner splits longer key ranges).
+constexpr int kMaxItemPages = 1024;
+
+// Per-sequence facts taken from the host mirrors (32 bytes).
+struct SeqInfo {
+  int32_t q_start;    // cu_seqlens_q[b]
+  int32_t q_len;      // Lq
+  int32_t kv_len;     // Lk = Lc + Ln (or Ln without a cache)
+  int32_t kn_start;   // cu_seqlens_knew[b] (0 without new K/V)
+  int32_t cache_len;  // Lc
+  int32_t new_len;    // Ln
+  int32_t pad0, pad1;
+};
+
+// One unit of attention work (32 bytes): packed rows [row0, row0 + nrows) of
+// sequence `seq` under kv head `kv_head`, keys [key_begin, key_end).
+struct WorkItem {
+  int32_t seq;
+  int32_t row0;
+  int32_t nrows;
+  int32_t kv_head;
+  int32_t key_begin;  // multiple of kBlockN
+  int32_t key_end;
+  int32_t part;       // -1: write out/lse; >= 0: first partial row of this part
+  int32_t queue;      // static queue (workgroup) of the persistent schedule
+};
+
+// A tile whose key range was split (32 bytes): parts s = 0..nsplit-1 wrote
+// partial rows part + s * nrows + r.
+struct MergeGroup {
+  int32_t seq;
+  int32_t row0;
+  int32_t nrows;
+  int32_t kv_head;
+  int32_t part;
+  int32_t nsplit;
+  int32_t pad0, pad1;
+};
+
+enum KvFormat : int32_t { kKvBf16 = 0, kKvFp8 = 1 };
+
+struct AttnParams {
+  const uint16_t* q;          // bf16 [Tq, Hq, D]
+  const void* k;              // cache [P, S, Hkv, D] or k_new [Tn, Hkv, D]
+  const void* v;
+  const int32_t* block_table; // [B, max_pages] (paged only)
+  const SeqInfo* seqs;
+  const WorkItem* items;
+  const int32_t* queue_start; // [num_queues + 1] (persistent only)
+  uint16_t* out;              // bf16 [Tq, Hq, D]
+  float* lse;                 // [Hq, Tq] or null
+  float* part_o;              // [rows, D] fp32, normalised partial outputs
+  float* part_lse;            // [rows]
+  int32_t* err_flag;
+  int32_t num_items;
+  int32_t persistent;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t page_shift;         // log2(page_size) or -1
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  int32_t total_q;
+  int32_t causal;
+  float qk_scale_log2;        // scale * log2(e) (* k_scale for fp8)
+  float v_scale;              // 1 (bf16) or v_scale (fp8)
+};
+
+struct AppendParams {
+  const uint16_t* k_new;      // bf16 [Tn, Hkv, D]
+  const uint16_t* v_new;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_table;
+  const SeqInfo* seqs;
+  const int32_t* cu_knew;     // [B + 1]
+  int32_t* err_flag;
+  int32_t batch;
+  int32_t total_knew;
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t row_elems;          // Hkv * D
+  int32_t fp8;
+  float k_inv_scale;          // fp32(1 / k_scale)
+  float v_inv_scale;
+};
+
+struct MergeParams {
+  const MergeGroup* groups;
+  const SeqInfo* seqs;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int32_t num_groups;
+  int32_t hq;
+  int32_t g;
+  int32_t total_q;
+  int32_t head_dim;
+};
+
+// Kernel launchers (defined in the .hip files); they return hipError_t as int.
+int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
+                     void* stream);
+int launch_append(const AppendParams& p, void* stream);
+int launch_merge(const MergeParams& p, void* stream);
+
+}  // namespace vpk
