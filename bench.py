@@ -219,28 +219,40 @@ def main():
     wall = time.perf_counter() - t0
     vpk.timing_enable(False)
     gpu_ms = start.elapsed_time(end)
-    attn_ms, attn_n = vpk.timing_read(vpk.KERNEL_ATTENTION)
+    pre_ms, pre_n = vpk.timing_read(vpk.KERNEL_ATTENTION)
+    dec_ms, dec_n = vpk.timing_read(vpk.KERNEL_ATTENTION_DECODE)
     app_ms, app_n = vpk.timing_read(vpk.KERNEL_APPEND)
     mrg_ms, mrg_n = vpk.timing_read(vpk.KERNEL_MERGE)
     elapsed = max(gpu_ms / 1e3, 1e-9)
     ms_per_step = gpu_ms / args.steps
-    attn_avg_ms = attn_ms / max(attn_n, 1)
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f}); "
-          f"attention {attn_avg_ms * 1e3:.1f} us x{attn_n}, append {app_ms / max(app_n, 1) * 1e3:.1f} us x{app_n}, "
-          f"merge {mrg_ms / max(mrg_n, 1) * 1e3:.1f} us x{mrg_n}", file=sys.stderr, flush=True)
+    avg = lambda ms, n: ms / max(n, 1)
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us); "
+          f"attention prefill-mode {avg(pre_ms, pre_n) * 1e3:.1f} us x{pre_n}, decode-mode "
+          f"{avg(dec_ms, dec_n) * 1e3:.1f} us x{dec_n}, append {avg(app_ms, app_n) * 1e3:.1f} us x{app_n}, "
+          f"merge {avg(mrg_ms, mrg_n) * 1e3:.1f} us x{mrg_n}", file=sys.stderr, flush=True)
 
+    # work of the sequences each grid serves (decode-mode: q_len * g <= 32 rows)
+    dec_seq = wl.q_lens() * (wl.Hq // wl.Hkv) <= 32
+    pre_flops = float(flops[~dec_seq].sum())
+    dec_bytes = float(kv_bytes[dec_seq].sum())
     if decode:
         value, unit = step_bytes * args.steps / elapsed / 1e9, "GB/s"
-        achieved = step_bytes / (attn_avg_ms / 1e3) / 1e9
+        kus = avg(dec_ms, dec_n) * 1e3
+        achieved = step_bytes / (kus / 1e6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
+                "frac": achieved / PEAK_HBM_GBS, "kernel": "attention (decode-mode grid)"}
     else:
         value, unit = step_flops * args.steps / elapsed / 1e12, "TFLOP/s"
-        achieved = step_flops / (attn_avg_ms / 1e3) / 1e12
+        kus = avg(pre_ms, pre_n) * 1e3
+        achieved = pre_flops / (kus / 1e6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS}
+                "frac": achieved / PEAK_BF16_TFLOPS, "kernel": "attention (prefill-mode grid)"}
+        if dec_n:
+            dus = avg(dec_ms, dec_n) * 1e3
+            roof["decode_grid"] = {"bound": "hbm", "achieved": dec_bytes / (dus / 1e6) / 1e9,
+                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "kernel_avg_us": dus}
     roof["traffic"] = load_traffic(args.workload)
-    roof["kernel_avg_us"] = attn_avg_ms * 1e3
+    roof["kernel_avg_us"] = kus
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -123,8 +123,9 @@ typedef struct {
  *   cu_seqlens_q    device int32 [B + 1].
  *   k_new, v_new    device bf16 [Tn, Hkv, D], or both NULL (attend over the
  *                   cache only, as the flash-attention page's Usage section
- *                   allows).
- *   cu_seqlens_knew device int32 [B + 1]; NULL iff k_new is NULL.
+ *                   allows).  With Tn == 0 they may be NULL while
+ *                   cu_seqlens_knew is given (every sequence adds nothing).
+ *   cu_seqlens_knew device int32 [B + 1]; NULL when there are no new tokens.
  *   k_cache,v_cache device [P, S, Hkv, D] in kv_cache_dtype, or both NULL: no
  *                   cache, attention runs over k_new/v_new of each sequence and
  *                   nothing is stored.  With a cache, new tokens are appended
@@ -134,7 +135,7 @@ typedef struct {
  *   cache_seqlens   device int32 [B] (NULL without a cache).
  *   page_size       S >= 1 tokens per page (ignored without a cache).
  *   causal          0 or 1.
- *   scale           softmax scale, finite.
+ *   scale           softmax scale, finite and > 0.
  *   kv_scale        host float[2] = {k_scale, v_scale} > 0 for an fp8 cache:
  *                   stored code c means c * scale; NULL for bf16.
  *   out             device bf16 [Tq, Hq, D].
@@ -192,7 +193,8 @@ int32_t vpk_set_option(const char* name, int64_t value);
  * bracketed by HIP events recorded on the launch stream.  vpk_timing_read
  * synchronises those events and returns the summed milliseconds and the
  * launch count per kernel since the last reset.
- *   kernel: 0 = attention, 1 = append, 2 = merge.
+ *   kernel: 0 = attention over prefill-mode items (more than 32 packed rows),
+ *           1 = append, 2 = merge, 3 = attention over decode-mode items.
  */
 int32_t vpk_timing_enable(int32_t enable);
 int32_t vpk_timing_reset(void);
@@ -204,10 +206,12 @@ int32_t vpk_device_error(void* stream, int32_t* flags);
 
 /*
  * Planner introspection (host only, needs no GPU): build the work list the
- * attention launch would use and copy it out.  Each item is 8 int32:
+ * attention launches would use and copy it out.  Each item is 8 int32:
  *   {seq, row0, nrows, kv_head, key_begin, key_end, part, queue}
  * where rows are packed (token * g + head-in-group) and part >= 0 marks a
- * split part whose result goes through the merge pass.  `num_cus` as for the
+ * split part whose result goes through the merge pass.  Items with more than
+ * 32 rows come first (prefill-mode grid), then the others (decode-mode grid);
+ * with the persistent schedule, queue numbers run over both grids.  `num_cus` as for the
  * "num_cus" option (> 0 here).  Returns VPK_ERROR_CAPACITY with *n_items set
  * when `capacity` is too small.
  */

@@ -57,8 +57,9 @@ std::mutex g_tmu;
 std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_tpending;
 std::vector<hipEvent_t> g_tfree;
-double g_tms[3] = {0, 0, 0};
-int64_t g_tcount[3] = {0, 0, 0};
+constexpr int kTimedKernels = 4;   // 0 prefill-mode attention, 1 append, 2 merge, 3 decode-mode attention
+double g_tms[kTimedKernels] = {0, 0, 0, 0};
+int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0};
 
 hipEvent_t take_event() {
   if (!g_tfree.empty()) {
@@ -92,6 +93,10 @@ struct KernelTimer {
 
 // --------------------------------------------------------------- workspace
 
+// workspace head: [0, 256) error flag, [256, 512) zeros (never written)
+constexpr size_t kFlagBytes = 512;
+constexpr size_t kZerosOffset = 256;
+
 struct Staging {
   void* host = nullptr;
   size_t bytes = 0;
@@ -103,18 +108,43 @@ struct Workspace {
   int device = -1;
   char* dev = nullptr;
   size_t bytes = 0;
-  Staging stage[4];
+  // device layout: [flag | zeros][plan region 0][plan region 1][partials]
+  size_t plan_cap = 0;       // bytes of each plan region
+  size_t part_cap = 0;       // bytes of the partials area
+  Staging stage[4];          // pinned host copies of uploaded plans
   int next = 0;
+  int flip = 0;              // plan region of the next call
+  bool used_valid[2] = {false, false};
+  hipEvent_t ev_used[2] = {nullptr, nullptr};   // kernels that read region r are done
+  // copy stream: the next call's plan upload overlaps the current call's kernels
+  hipStream_t copy = nullptr;
+  // side stream for running the decode-mode grid next to the prefill-mode grid
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr;
+  hipEvent_t ev_join = nullptr;
+  char* plan_region(int r) const { return dev + kFlagBytes + static_cast<size_t>(r) * plan_cap; }
+  char* parts() const { return dev + kFlagBytes + 2 * plan_cap; }
 };
+
+int32_t ensure_aux(Workspace* w) {
+  if (w->aux) return VPK_SUCCESS;
+  hipError_t e = hipStreamCreateWithFlags(&w->aux, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags (side stream)");
+  if ((e = hipEventCreateWithFlags(&w->ev_fork, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "hipEventCreate (fork)");
+  if ((e = hipEventCreateWithFlags(&w->ev_join, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "hipEventCreate (join)");
+  return VPK_SUCCESS;
+}
 
 std::mutex g_wmu;
 std::map<std::pair<int, void*>, Workspace*> g_ws;
 
-constexpr size_t kFlagBytes = 256;
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int32_t get_workspace(hipStream_t stream, size_t need, Workspace** out) {
+// The workspace of (current device, stream) with room for a plan of
+// `plan_need` bytes and `part_need` bytes of split partials.
+int32_t get_workspace(hipStream_t stream, size_t plan_need, size_t part_need, Workspace** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -124,16 +154,26 @@ int32_t get_workspace(hipStream_t stream, size_t need, Workspace** out) {
     w = new (std::nothrow) Workspace();
     if (!w) return fail(VPK_ERROR_OUT_OF_MEMORY, "workspace bookkeeping");
     w->device = dev;
+    if ((e = hipStreamCreateWithFlags(&w->copy, hipStreamNonBlocking)) != hipSuccess)
+      return hip_fail(e, "hipStreamCreateWithFlags (copy stream)");
+    for (int r = 0; r < 2; ++r)
+      if ((e = hipEventCreateWithFlags(&w->ev_used[r], hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate (plan region)");
   }
-  if (w->bytes < need) {
+  if (w->plan_cap < plan_need || w->part_cap < part_need) {
     if (w->dev) {
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (workspace growth)");
+      // everything that may still read the old buffer is on these streams
+      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (workspace growth)");
+      if ((e = hipStreamSynchronize(w->copy)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (copy stream)");
+      if (w->aux && (e = hipStreamSynchronize(w->aux)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (side stream)");
       (void)hipFree(w->dev);
       w->dev = nullptr;
       w->bytes = 0;
+      w->used_valid[0] = w->used_valid[1] = false;
     }
-    const size_t bytes = align_up(std::max(need + need / 2, static_cast<size_t>(1) << 20), 1 << 20);
+    const size_t pc = align_up(std::max(std::max(plan_need + plan_need / 2, w->plan_cap), static_cast<size_t>(64) << 10), 4096);
+    const size_t qc = align_up(std::max(part_need + part_need / 2, w->part_cap), 4096);
+    const size_t bytes = kFlagBytes + 2 * pc + qc;
     void* p = nullptr;
     e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
@@ -144,14 +184,21 @@ int32_t get_workspace(hipStream_t stream, size_t need, Workspace** out) {
     }
     w->dev = static_cast<char*>(p);
     w->bytes = bytes;
+    w->plan_cap = pc;
+    w->part_cap = qc;
   }
   *out = w;
   return VPK_SUCCESS;
 }
 
-// Copy `bytes` of host data into the workspace at `dst_off` through a pinned
-// staging buffer (4 in rotation; a buffer is reused once its copy finished).
-int32_t stage_upload(Workspace* w, hipStream_t stream, const void* src, size_t bytes, size_t dst_off) {
+// Copy a plan into the next plan region on the copy stream: the copy waits for
+// the kernels that last read that region, and `stream` waits for the copy.
+// Returns the region in *region.
+int32_t upload_plan_region(Workspace* w, hipStream_t stream, const void* src, size_t bytes,
+                           int* region) {
+  const int r = w->flip;
+  w->flip ^= 1;
+  *region = r;
   if (bytes == 0) return VPK_SUCCESS;
   Staging& st = w->stage[w->next];
   w->next = (w->next + 1) % 4;
@@ -175,11 +222,21 @@ int32_t stage_upload(Workspace* w, hipStream_t stream, const void* src, size_t b
     st.bytes = nb;
   }
   std::memcpy(st.host, src, bytes);
-  e = hipMemcpyAsync(w->dev + dst_off, st.host, bytes, hipMemcpyHostToDevice, stream);
+  if (w->used_valid[r] && (e = hipStreamWaitEvent(w->copy, w->ev_used[r], 0)) != hipSuccess)
+    return hip_fail(e, "hipStreamWaitEvent (plan region reuse)");
+  e = hipMemcpyAsync(w->plan_region(r), st.host, bytes, hipMemcpyHostToDevice, w->copy);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
-  e = hipEventRecord(st.ev, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
+  if ((e = hipEventRecord(st.ev, w->copy)) != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
   st.pending = true;
+  if ((e = hipStreamWaitEvent(stream, st.ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (plan ready)");
+  return VPK_SUCCESS;
+}
+
+// Mark plan region r as read by everything enqueued on `stream` so far.
+int32_t release_region(Workspace* w, hipStream_t stream, int r) {
+  hipError_t e = hipEventRecord(w->ev_used[r], stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan region)");
+  w->used_valid[r] = true;
   return VPK_SUCCESS;
 }
 
@@ -341,39 +398,46 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
   in.split_min_keys = static_cast<int32_t>(g_opt.split_min_keys.load());
 }
 
-// Workspace layout: [flag][seqs][cu_knew][items][groups][queues] | [part_o][part_lse]
+// Plan region layout (offsets from the region start):
+//   [seqs][cu_knew][units][merge groups][queue starts][queue work]
+// Partials area: [part_o fp32 rows x D][part_lse fp32 rows]
 struct Layout {
-  size_t seqs, cu_kn, items, groups, queues, plan_end, part_o, part_lse, total;
+  size_t seqs, cu_kn, items, groups, queues, work, plan_end, part_o, part_lse, part_end;
 };
 
 Layout layout_for(const Plan& p, int32_t B, int32_t D) {
   Layout L;
-  L.seqs = kFlagBytes;
+  L.seqs = 0;
   L.cu_kn = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
   L.items = align_up(L.cu_kn + sizeof(int32_t) * (B + 1), 64);
   L.groups = align_up(L.items + sizeof(WorkItem) * p.items.size(), 64);
   L.queues = align_up(L.groups + sizeof(MergeGroup) * p.groups.size(), 64);
-  L.plan_end = align_up(L.queues + sizeof(int32_t) * p.queue_start.size(), 256);
-  L.part_o = L.plan_end;
-  L.part_lse = align_up(L.part_o + sizeof(float) * D * static_cast<size_t>(p.part_rows), 256);
-  L.total = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
+  L.work = align_up(L.queues + sizeof(int32_t) * p.queue_start.size(), 64);
+  L.plan_end = align_up(L.work + sizeof(int32_t) * p.queue_work.size(), 256);
+  L.part_o = 0;
+  L.part_lse = align_up(sizeof(float) * D * static_cast<size_t>(p.part_rows), 256);
+  L.part_end = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
   return L;
 }
 
+// Serialise the plan (host) and upload it; *region receives the plan region used.
 int32_t upload_plan(Workspace* w, hipStream_t stream, const Plan& p, const Layout& L,
-                    const int32_t* cu_kn, int32_t B) {
-  std::vector<char> buf(L.plan_end - L.seqs, 0);
-  char* base = buf.data() - L.seqs;
+                    const int32_t* cu_kn, int32_t B, int* region) {
+  static thread_local std::vector<char> buf;
+  buf.assign(L.plan_end, 0);
+  char* base = buf.data();
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
   if (cu_kn) std::memcpy(base + L.cu_kn, cu_kn, sizeof(int32_t) * (B + 1));
   if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
   if (!p.groups.empty()) std::memcpy(base + L.groups, p.groups.data(), sizeof(MergeGroup) * p.groups.size());
   if (!p.queue_start.empty())
     std::memcpy(base + L.queues, p.queue_start.data(), sizeof(int32_t) * p.queue_start.size());
-  return stage_upload(w, stream, buf.data(), buf.size(), L.seqs);
+  if (!p.queue_work.empty())
+    std::memcpy(base + L.work, p.queue_work.data(), sizeof(int32_t) * p.queue_work.size());
+  return upload_plan_region(w, stream, buf.data(), buf.size(), region);
 }
 
-int32_t enqueue_append(const Call& c, Workspace* w, const Layout& L, const void* k_new,
+int32_t enqueue_append(const Call& c, Workspace* w, char* R, const Layout& L, const void* k_new,
                        const void* v_new, void* k_cache, void* v_cache,
                        const int32_t* block_table, hipStream_t stream) {
   const vpk_dims* d = c.d;
@@ -383,8 +447,8 @@ int32_t enqueue_append(const Call& c, Workspace* w, const Layout& L, const void*
   ap.k_cache = k_cache;
   ap.v_cache = v_cache;
   ap.block_table = block_table;
-  ap.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
-  ap.cu_knew = reinterpret_cast<const int32_t*>(w->dev + L.cu_kn);
+  ap.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
+  ap.cu_knew = reinterpret_cast<const int32_t*>(R + L.cu_kn);
   ap.err_flag = reinterpret_cast<int32_t*>(w->dev);
   ap.batch = d->batch;
   ap.total_knew = d->total_knew;
@@ -415,7 +479,10 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
                   void* stream_v) {
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
-  Call c{dims, k_new != nullptr || v_new != nullptr, k_cache != nullptr || v_cache != nullptr,
+  // new tokens are present when any of their arrays is given; with total_knew == 0
+  // the token arrays may be NULL (a zero-size tensor has no storage)
+  Call c{dims, k_new != nullptr || v_new != nullptr || cu_seqlens_knew != nullptr,
+         k_cache != nullptr || v_cache != nullptr,
          dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN && (k_cache || v_cache), page_size, kv_scale};
   int32_t st = check_dims(c);
   if (st != VPK_SUCCESS) return st;
@@ -423,17 +490,18 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   if ((k_cache == nullptr) != (v_cache == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_cache and v_cache must both be given or both be NULL");
   if (!c.has_new && !c.has_cache) return fail(VPK_ERROR_INVALID_VALUE, "no keys: give k_new/v_new, a cache, or both");
   if (causal != 0 && causal != 1) return fail(VPK_ERROR_INVALID_VALUE, "causal must be 0 or 1");
-  if (!std::isfinite(scale)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite and > 0");
   if (!c.has_new && dims->total_knew != 0) return fail(VPK_ERROR_INVALID_VALUE, "total_knew must be 0 without k_new");
   if (!c.has_cache && (dims->num_pages != 0)) return fail(VPK_ERROR_INVALID_VALUE, "num_pages must be 0 without a cache");
   if (!c.fp8 && kv_scale && c.has_cache) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
   const int32_t B = dims->batch;
   if (!cu_seqlens_q && !(host && host->cu_seqlens_q)) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_q is NULL");
   if (c.has_new) {
-    if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
-    if (!cu_seqlens_knew) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew is NULL while k_new is given");
-  } else if (cu_seqlens_knew) {
-    return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew must be NULL without k_new");
+    if (!cu_seqlens_knew && !(host && host->cu_seqlens_knew))
+      return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew is NULL while k_new is given");
+    if (dims->total_knew > 0 || k_new || v_new) {
+      if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
+    }
   }
   if (c.has_cache) {
     if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
@@ -460,27 +528,30 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   }
   const Layout L = layout_for(plan, B, dims->head_dim);
   Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.total, &w))) return st;
-  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B))) return st;
+  if ((st = get_workspace(stream, L.plan_end, L.part_end, &w))) return st;
+  int region = 0;
+  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B, &region))) return st;
+  char* const R = w->plan_region(region);
+  char* const PA = w->parts();
 
   if (c.has_cache && c.has_new && dims->total_knew > 0) {
-    if ((st = enqueue_append(c, w, L, k_new, v_new, k_cache, v_cache, block_table, stream))) return st;
+    if ((st = enqueue_append(c, w, R, L, k_new, v_new, k_cache, v_cache, block_table, stream))) return st;
   }
-  if (plan.grid > 0) {
+  const bool run_pre = plan.prefill.grid > 0;
+  const bool run_dec = plan.decode.grid > 0;
+  if (run_pre || run_dec) {
     AttnParams p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = c.has_cache ? k_cache : k_new;
     p.v = c.has_cache ? v_cache : v_new;
     p.block_table = block_table;
-    p.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
-    p.items = reinterpret_cast<const WorkItem*>(w->dev + L.items);
-    p.queue_start = reinterpret_cast<const int32_t*>(w->dev + L.queues);
+    p.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
-    p.part_o = reinterpret_cast<float*>(w->dev + L.part_o);
-    p.part_lse = reinterpret_cast<float*>(w->dev + L.part_lse);
+    p.part_o = reinterpret_cast<float*>(PA + L.part_o);
+    p.part_lse = reinterpret_cast<float*>(PA + L.part_lse);
     p.err_flag = reinterpret_cast<int32_t*>(w->dev);
-    p.num_items = static_cast<int32_t>(plan.items.size());
+    p.zeros = w->dev + kZerosOffset;
     p.persistent = plan.persistent ? 1 : 0;
     p.max_pages = dims->max_pages_per_seq;
     p.num_pages = dims->num_pages;
@@ -500,17 +571,41 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
                                          (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
     p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
-    KernelTimer tm(0, stream);
-    const int rc = vpk::launch_attention(p, plan.grid, dims->head_dim,
-                                         c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16, c.has_cache, stream);
-    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
+    const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
+    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s) -> int32_t {
+      AttnParams q = p;
+      q.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
+      q.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
+      q.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
+      q.num_items = Lc.count;
+      KernelTimer tm(dec ? 3 : 0, s);
+      const int rc = vpk::launch_attention(q, Lc.grid, dims->head_dim, fmt, c.has_cache, dec, s);
+      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
+      return VPK_SUCCESS;
+    };
+    if (run_pre && run_dec) {
+      // both grids at once: the decode-mode grid (HBM-bound) on the side
+      // stream next to the prefill-mode grid (MFMA-bound), joined before merge
+      if ((st = ensure_aux(w))) return st;
+      hipError_t e;
+      if ((e = hipEventRecord(w->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
+      if ((e = hipStreamWaitEvent(w->aux, w->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
+      if ((st = launch(plan.decode, true, w->aux))) return st;
+      if ((e = hipEventRecord(w->ev_join, w->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
+      if ((st = launch(plan.prefill, false, stream))) return st;
+      if ((e = hipStreamWaitEvent(stream, w->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
+    } else if (run_pre) {
+      if ((st = launch(plan.prefill, false, stream))) return st;
+    } else {
+      if ((st = launch(plan.decode, true, stream))) return st;
+    }
   }
   if (!plan.groups.empty()) {
     MergeParams mp{};
-    mp.groups = reinterpret_cast<const MergeGroup*>(w->dev + L.groups);
-    mp.seqs = reinterpret_cast<const SeqInfo*>(w->dev + L.seqs);
-    mp.part_o = reinterpret_cast<const float*>(w->dev + L.part_o);
-    mp.part_lse = reinterpret_cast<const float*>(w->dev + L.part_lse);
+    mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
+    mp.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
+    mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
+    mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
     mp.out = static_cast<uint16_t*>(out);
     mp.lse = lse;
     mp.num_groups = static_cast<int32_t>(plan.groups.size());
@@ -522,7 +617,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     const int rc = vpk::launch_merge(mp, stream);
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
   }
-  return VPK_SUCCESS;
+  return release_region(w, stream, region);
 }
 
 int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
@@ -535,6 +630,7 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   int32_t st = check_dims(c);
   if (st != VPK_SUCCESS) return st;
   if (!c.fp8 && kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
+  if (dims->total_knew == 0 && dims->batch >= 0) return VPK_SUCCESS;
   if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
   if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
   if ((st = check_ptr(block_table, 4, "block_table")) || (st = check_ptr(cache_seqlens, 4, "cache_seqlens"))) return st;
@@ -556,9 +652,13 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   }
   const Layout L = layout_for(plan, B, dims->head_dim);
   Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.total, &w))) return st;
-  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B))) return st;
-  return enqueue_append(c, w, L, k_new, v_new, k_cache, v_cache, block_table, stream);
+  if ((st = get_workspace(stream, L.plan_end, 0, &w))) return st;
+  int region = 0;
+  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B, &region))) return st;
+  if ((st = enqueue_append(c, w, w->plan_region(region), L, k_new, v_new, k_cache, v_cache,
+                           block_table, stream)))
+    return st;
+  return release_region(w, stream, region);
 }
 
 }  // namespace
@@ -637,7 +737,7 @@ int32_t vpk_timing_reset(void) {
     g_tfree.push_back(r.b);
   }
   g_tpending.clear();
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < kTimedKernels; ++i) {
     g_tms[i] = 0;
     g_tcount[i] = 0;
   }
@@ -645,7 +745,7 @@ int32_t vpk_timing_reset(void) {
 }
 
 int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel > 2) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0, 1 or 2");
+  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..3");
   std::lock_guard<std::mutex> lk(g_tmu);
   for (const TimingRec& r : g_tpending) {
     hipError_t e = hipEventSynchronize(r.b);
@@ -711,15 +811,32 @@ int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host, int32_t
     fill_plan_input(c, m, causal, num_cus, in);
     Plan plan;
     vpk::build_plan(in, plan);
-    const int32_t n = static_cast<int32_t>(plan.items.size());
+    // expand units to (unit, kv head) items in launch order
+    const int32_t hkv = dims->num_kv_heads;
+    const int32_t n = static_cast<int32_t>(plan.items.size()) * hkv;
     if (n_items) *n_items = n;
-    if (n_queues) *n_queues = plan.persistent ? static_cast<int32_t>(plan.queue_start.size()) - 1 : 0;
+    if (n_queues) *n_queues = plan.persistent ? plan.prefill.grid + plan.decode.grid : 0;
     if (n > capacity) return fail(VPK_ERROR_CAPACITY, "items buffer too small");
-    for (int32_t i = 0; i < n; ++i) {
-      const WorkItem& it = plan.items[i];
-      int32_t* o = items + 8 * i;
-      o[0] = it.seq; o[1] = it.row0; o[2] = it.nrows; o[3] = it.kv_head;
-      o[4] = it.key_begin; o[5] = it.key_end; o[6] = it.part; o[7] = it.queue;
+    int32_t k = 0;
+    int32_t qoff = 0;
+    for (const vpk::Launch* Lc : {&plan.prefill, &plan.decode}) {
+      auto emit = [&](int32_t work, int32_t queue) {
+        const int32_t u = work / hkv, h = work % hkv;
+        const WorkItem& it = plan.items[Lc->first + u];
+        int32_t* o = items + 8 * (k++);
+        o[0] = it.seq; o[1] = it.row0; o[2] = it.nrows; o[3] = h;
+        o[4] = it.key_begin; o[5] = it.key_end;
+        o[6] = it.part < 0 ? -1 : it.part + h * it.part_stride;
+        o[7] = queue;
+      };
+      if (!plan.persistent) {
+        for (int32_t wk = 0; wk < Lc->count * hkv; ++wk) emit(wk, 0);
+      } else {
+        for (int32_t q = 0; q < Lc->grid; ++q)
+          for (int32_t e = plan.queue_start[Lc->queue_first + q]; e < plan.queue_start[Lc->queue_first + q + 1]; ++e)
+            emit(plan.queue_work[Lc->work_first + e], qoff + q);
+        qoff += Lc->grid;
+      }
     }
     return VPK_SUCCESS;
   } catch (...) {

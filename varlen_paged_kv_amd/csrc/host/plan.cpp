@@ -30,20 +30,29 @@ namespace {
 struct Tile {
   int32_t seq, row0, nrows, kv_head, kend;
   double cost;
+  bool dec;   // decode mode: the whole sequence has at most 32 packed rows
 };
 
 // Relative time of one 64-key block: staging K/V is paid once per block, the
-// MFMA and softmax work once per active 32-row wave.
-double block_cost(int32_t nrows, int32_t kv_bytes) {
-  const int waves = (nrows + kWaveRows - 1) / kWaveRows;
+// MFMA and softmax work once per active 32-row wave; decode-mode tiles (a
+// sequence of at most 32 rows) spread their keys over the four waves.
+double block_cost(int32_t nrows, int32_t kv_bytes, bool decode_mode) {
   const double load = kv_bytes == 1 ? 0.6 : 1.0;
+  if (decode_mode) return load + 0.25;
+  const int waves = (nrows + kWaveRows - 1) / kWaveRows;
   return load + 1.0 * waves;
 }
 
 }  // namespace
 
 void build_plan(const PlanInput& in, Plan& out) {
-  out = Plan();
+  out.items.clear();
+  out.groups.clear();
+  out.queue_start.clear();
+  out.part_rows = 0;
+  out.persistent = false;
+  out.prefill = Launch();
+  out.decode = Launch();
   const int32_t B = in.batch;
   const int32_t g = in.hq / in.hkv;
   out.seqs.resize(B);
@@ -58,8 +67,9 @@ void build_plan(const PlanInput& in, Plan& out) {
     s.kv_len = s.cache_len + s.new_len;
   }
 
-  // ---- tiles
-  std::vector<Tile> tiles;
+  // ---- row tiles (shared by all kv heads: every head has the same rows and keys)
+  static thread_local std::vector<Tile> tiles;
+  tiles.clear();
   double total = 0.0;
   for (int32_t b = 0; b < B; ++b) {
     const SeqInfo& s = out.seqs[b];
@@ -72,26 +82,25 @@ void build_plan(const PlanInput& in, Plan& out) {
       if (in.causal) kend = std::min<int64_t>(kend, static_cast<int64_t>(t_last) + s.kv_len - s.q_len + 1);
       kend = std::max<int64_t>(kend, 0);
       const int32_t nblk = static_cast<int32_t>((kend + kBlockN - 1) / kBlockN);
-      const double c = 0.05 + nblk * block_cost(nr, in.kv_bytes);
-      for (int32_t h = 0; h < in.hkv; ++h) {
-        tiles.push_back(Tile{b, static_cast<int32_t>(r0), nr, h, static_cast<int32_t>(kend), c});
-        total += c;
-      }
+      const double c = 0.05 + nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
+      tiles.push_back(Tile{b, static_cast<int32_t>(r0), nr, 0, static_cast<int32_t>(kend), c, rows <= kWaveRows});
+      total += c * in.hkv;
     }
   }
 
-  // ---- split decision
+  // ---- split decision per tile -> units (tile, part)
   const int64_t slots = static_cast<int64_t>(std::max(1, in.num_cus)) * std::max(1, in.wg_per_cu);
   const double target = total / static_cast<double>(2 * slots);
   const int32_t min_blocks = std::max(1, (in.split_min_keys + kBlockN - 1) / kBlockN);
-
-  struct Pending {
-    WorkItem it;
+  struct Unit {
     double cost;
+    int32_t tile, part, b0, b1, nsplit, group;
   };
-  std::vector<Pending> items;
-  items.reserve(tiles.size());
-  for (const Tile& t : tiles) {
+  static thread_local std::vector<Unit> units;
+  units.clear();
+  int32_t ngroups = 0;
+  for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
+    const Tile& t = tiles[ti];
     const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;
     int32_t n = 1;
     if (in.force_splits > 0) {
@@ -110,61 +119,112 @@ void build_plan(const PlanInput& in, Plan& out) {
       n = std::max(n, need);
     }
     if (n <= 1) {
-      Pending p;
-      p.it = WorkItem{t.seq, t.row0, t.nrows, t.kv_head, 0, t.kend, -1, 0};
-      p.cost = t.cost;
-      items.push_back(p);
+      units.push_back(Unit{t.cost, ti, 0, 0, nblk, 1, -1});
       continue;
     }
-    MergeGroup gr{t.seq, t.row0, t.nrows, t.kv_head, static_cast<int32_t>(out.part_rows), n, 0, 0};
-    out.groups.push_back(gr);
     for (int32_t s = 0; s < n; ++s) {
       const int32_t b0 = static_cast<int32_t>(static_cast<int64_t>(nblk) * s / n);
       const int32_t b1 = static_cast<int32_t>(static_cast<int64_t>(nblk) * (s + 1) / n);
-      Pending p;
-      p.it = WorkItem{t.seq, t.row0, t.nrows, t.kv_head, b0 * kBlockN,
-                      std::min(t.kend, b1 * kBlockN),
-                      static_cast<int32_t>(out.part_rows + static_cast<int64_t>(s) * t.nrows), 0};
-      p.cost = 0.05 + (b1 - b0) * block_cost(t.nrows, in.kv_bytes);
-      items.push_back(p);
+      units.push_back(Unit{0.05 + (b1 - b0) * block_cost(t.nrows, in.kv_bytes, t.dec), ti, s, b0, b1, n, ngroups});
     }
-    out.part_rows += static_cast<int64_t>(n) * t.nrows;
+    ++ngroups;
   }
 
-  // ---- order: longest first (stable, so equal costs keep tile order)
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Pending& a, const Pending& b) { return a.cost > b.cost; });
+  // partial-row bases: group gi of tile ti covers nsplit * nrows rows per kv head
+  static thread_local std::vector<int64_t> group_base;
+  group_base.assign(ngroups, 0);
+  {
+    int32_t gi = 0;
+    for (const Unit& u : units) {
+      if (u.group < 0 || u.part != 0) continue;
+      const Tile& t = tiles[u.tile];
+      for (int32_t h = 0; h < in.hkv; ++h) {
+        out.groups.push_back(MergeGroup{t.seq, t.row0, t.nrows, h,
+                                        static_cast<int32_t>(out.part_rows + static_cast<int64_t>(h) * u.nsplit * t.nrows),
+                                        u.nsplit, 0, 0});
+      }
+      group_base[gi++] = out.part_rows;
+      out.part_rows += static_cast<int64_t>(in.hkv) * u.nsplit * t.nrows;
+    }
+  }
+
+  // ---- order: prefill-mode units, then decode-mode units; each longest
+  //      first, ties in tile / part order (deterministic)
+  static thread_local std::vector<int32_t> order;
+  order.resize(units.size());
+  std::iota(order.begin(), order.end(), 0);
+  // decode mode for sequences whose packed rows all fit one wave (q_len * g <=
+  // 32); a prefill sequence's short last tile stays with its other tiles
+  auto is_dec = [&](int32_t ui) { return tiles[units[ui].tile].dec; };
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    const bool da = is_dec(a), db = is_dec(b);
+    if (da != db) return !da;
+    if (units[a].cost != units[b].cost) return units[a].cost > units[b].cost;
+    return a < b;
+  });
+
+  out.items.reserve(units.size());
+  int32_t n_prefill_units = 0;
+  for (int32_t ui : order) {
+    const Unit& u = units[ui];
+    const Tile& t = tiles[u.tile];
+    if (!is_dec(ui)) ++n_prefill_units;
+    const int32_t kb = u.b0 * kBlockN;
+    const int32_t ke = u.group < 0 ? t.kend : std::min(t.kend, u.b1 * kBlockN);
+    int32_t part = -1, stride = 0;
+    if (u.group >= 0) {
+      part = static_cast<int32_t>(group_base[u.group] + static_cast<int64_t>(u.part) * t.nrows);
+      stride = u.nsplit * t.nrows;
+    }
+    out.items.push_back(WorkItem{t.seq, t.row0, t.nrows, stride, kb, ke, part, 0});
+  }
+  out.prefill.first = 0;
+  out.prefill.count = n_prefill_units;
+  out.decode.first = n_prefill_units;
+  out.decode.count = static_cast<int32_t>(out.items.size()) - n_prefill_units;
 
   const bool persistent = in.persistent == 1;
   out.persistent = persistent;
   if (!persistent) {
-    out.items.reserve(items.size());
-    for (const Pending& p : items) out.items.push_back(p.it);
-    out.grid = static_cast<int32_t>(out.items.size());
+    out.prefill.grid = out.prefill.count * in.hkv;
+    out.decode.grid = out.decode.count * in.hkv;
     return;
   }
 
-  // ---- persistent: greedy least-loaded queues
-  const int32_t nq = static_cast<int32_t>(std::min<int64_t>(slots, static_cast<int64_t>(items.size())));
-  out.grid = nq;
-  out.queue_start.assign(nq + 1, 0);
-  if (nq == 0) return;
-  using Load = std::pair<double, int32_t>;
-  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-  for (int32_t q = 0; q < nq; ++q) heap.push(Load{0.0, q});
-  std::vector<int32_t> count(nq, 0);
-  for (Pending& p : items) {
-    Load l = heap.top();
-    heap.pop();
-    p.it.queue = l.second;
-    ++count[l.second];
-    l.first += p.cost;
-    heap.push(l);
+  // ---- persistent: per launch, greedy least-loaded queues over its ordered
+  //      (unit, kv head) work
+  static thread_local std::vector<int32_t> owner;
+  static thread_local std::vector<int32_t> count;
+  static thread_local std::vector<int32_t> fill;
+  for (Launch* L : {&out.prefill, &out.decode}) {
+    const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
+    const int32_t nq = static_cast<int32_t>(std::min<int64_t>(slots, nwork));
+    L->grid = nq;
+    L->queue_first = static_cast<int32_t>(out.queue_start.size());
+    L->work_first = static_cast<int32_t>(out.queue_work.size());
+    if (nq == 0) continue;
+    const size_t q0 = out.queue_start.size();
+    out.queue_start.resize(q0 + nq + 1, 0);
+    using Load = std::pair<double, int32_t>;
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int32_t q = 0; q < nq; ++q) heap.push(Load{0.0, q});
+    count.assign(nq, 0);
+    owner.resize(nwork);
+    for (int64_t w = 0; w < nwork; ++w) {
+      const double cost = units[order[L->first + w / in.hkv]].cost;
+      Load l = heap.top();
+      heap.pop();
+      owner[w] = l.second;
+      ++count[l.second];
+      l.first += cost;
+      heap.push(l);
+    }
+    for (int32_t q = 0; q < nq; ++q) out.queue_start[q0 + q + 1] = out.queue_start[q0 + q] + count[q];
+    fill.assign(out.queue_start.begin() + q0, out.queue_start.begin() + q0 + nq);
+    const size_t w0 = out.queue_work.size();
+    out.queue_work.resize(w0 + nwork);
+    for (int64_t w = 0; w < nwork; ++w) out.queue_work[w0 + fill[owner[w]]++] = static_cast<int32_t>(w);
   }
-  for (int32_t q = 0; q < nq; ++q) out.queue_start[q + 1] = out.queue_start[q] + count[q];
-  out.items.resize(items.size());
-  std::vector<int32_t> fill(out.queue_start.begin(), out.queue_start.end() - 1);
-  for (const Pending& p : items) out.items[fill[p.it.queue]++] = p.it;
 }
 
 }  // namespace vpk

@@ -30,14 +30,26 @@ struct PlanInput {
   int32_t split_min_keys = 256;
 };
 
+// One attention grid: items [first, first + count) of Plan::items, run by the
+// prefill-mode kernel (tiles of more than 32 rows) or the decode-mode kernel
+// (tiles of at most 32 rows, keys split over the four waves).
+struct Launch {
+  int32_t first = 0;                    // first unit in Plan::items
+  int32_t count = 0;                    // units
+  int32_t grid = 0;                     // workgroups
+  int32_t queue_first = 0;              // persistent: its num_queues + 1 entries of queue_start
+  int32_t work_first = 0;               // persistent: its entries of queue_work
+};
+
 struct Plan {
   std::vector<SeqInfo> seqs;
-  std::vector<WorkItem> items;          // launch order
+  std::vector<WorkItem> items;          // prefill-mode units, then decode-mode units
   std::vector<MergeGroup> groups;
-  std::vector<int32_t> queue_start;     // persistent only: num_queues + 1
+  std::vector<int32_t> queue_start;     // persistent only; offsets into the launch's queue_work
+  std::vector<int32_t> queue_work;      // persistent only; unit (launch-relative) * hkv + kv head
   int64_t part_rows = 0;                // rows of split partials
   bool persistent = false;
-  int32_t grid = 0;                     // attention workgroups to launch
+  Launch prefill, decode;
 };
 
 constexpr int32_t kMaxSplits = 64;

@@ -30,16 +30,17 @@ struct SeqInfo {
 };
 
 // One unit of attention work (32 bytes): packed rows [row0, row0 + nrows) of
-// sequence `seq` under kv head `kv_head`, keys [key_begin, key_end).
+// sequence `seq` against keys [key_begin, key_end), for every kv head; the
+// grid index (or the persistent queue entry) picks the head.
 struct WorkItem {
   int32_t seq;
   int32_t row0;
   int32_t nrows;
-  int32_t kv_head;
-  int32_t key_begin;  // multiple of kBlockN
+  int32_t part_stride; // partial rows between consecutive kv heads of a split part
+  int32_t key_begin;   // multiple of kBlockN
   int32_t key_end;
-  int32_t part;       // -1: write out/lse; >= 0: first partial row of this part
-  int32_t queue;      // static queue (workgroup) of the persistent schedule
+  int32_t part;        // -1: write out/lse; >= 0: first partial row of kv head 0
+  int32_t pad;
 };
 
 // A tile whose key range was split (32 bytes): parts s = 0..nsplit-1 wrote
@@ -62,13 +63,15 @@ struct AttnParams {
   const void* v;
   const int32_t* block_table; // [B, max_pages] (paged only)
   const SeqInfo* seqs;
-  const WorkItem* items;
-  const int32_t* queue_start; // [num_queues + 1] (persistent only)
+  const WorkItem* items;      // this grid's units
+  const int32_t* queue_start; // persistent: [num_queues + 1] offsets into queue_work
+  const int32_t* queue_work;  // persistent: unit * hkv + kv_head, grouped by queue
   uint16_t* out;              // bf16 [Tq, Hq, D]
   float* lse;                 // [Hq, Tq] or null
   float* part_o;              // [rows, D] fp32, normalised partial outputs
   float* part_lse;            // [rows]
   int32_t* err_flag;
+  const void* zeros;          // >= 256 zero bytes: source of rows past the keys
   int32_t num_items;
   int32_t persistent;
   int32_t max_pages;
@@ -120,7 +123,7 @@ struct MergeParams {
 
 // Kernel launchers (defined in the .hip files); they return hipError_t as int.
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
-                     void* stream);
+                     bool decode, void* stream);
 int launch_append(const AppendParams& p, void* stream);
 int launch_merge(const MergeParams& p, void* stream);
 
