@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attn TFLOP/s + decode KV GB/s (% of MI355X peak), varlen paged"
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
-KERNEL_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/attn_fwd.hip", "varlen_paged_kv_amd/csrc/vpk_internal.h"]
+KERNEL_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/attn_fwd.hip", "varlen_paged_kv_amd/csrc/kernels/append_dev.h",
+                  "varlen_paged_kv_amd/csrc/vpk_internal.h"]
 
 
 def visible_pairs(ql, kl, causal):
@@ -228,7 +229,7 @@ def main():
     avg = lambda ms, n: ms / max(n, 1)
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us); "
           f"attention prefill-mode {avg(pre_ms, pre_n) * 1e3:.1f} us x{pre_n}, decode-mode "
-          f"{avg(dec_ms, dec_n) * 1e3:.1f} us x{dec_n}, append {avg(app_ms, app_n) * 1e3:.1f} us x{app_n}, "
+          f"{avg(dec_ms, dec_n) * 1e3:.1f} us x{dec_n}, standalone append {avg(app_ms, app_n) * 1e3:.1f} us x{app_n}, "
           f"merge {avg(mrg_ms, mrg_n) * 1e3:.1f} us x{mrg_n}", file=sys.stderr, flush=True)
 
     # work of the sequences each grid serves (decode-mode: q_len * g <= 32 rows)

@@ -193,8 +193,12 @@ int32_t vpk_set_option(const char* name, int64_t value);
  * bracketed by HIP events recorded on the launch stream.  vpk_timing_read
  * synchronises those events and returns the summed milliseconds and the
  * launch count per kernel since the last reset.
- *   kernel: 0 = attention over prefill-mode items (more than 32 packed rows),
- *           1 = append, 2 = merge, 3 = attention over decode-mode items.
+ *   kernel: 0 = attention grid of prefill-mode items (sequences with more
+ *               than 32 packed rows; may include the append of a bf16 cache),
+ *           1 = append launched on its own (fp8 cache, persistent schedule,
+ *               or kv_cache_append),
+ *           2 = attention grid of decode-mode items (likewise),
+ *           3 = LSE merge of split parts.
  */
 int32_t vpk_timing_enable(int32_t enable);
 int32_t vpk_timing_reset(void);

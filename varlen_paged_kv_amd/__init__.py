@@ -24,9 +24,11 @@ from ._lib import VpkDims, VpkHostIndex
 
 __all__ = ["attn_varlen_paged_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug",
-           "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_MERGE", "KERNEL_ATTENTION_DECODE"]
+           "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE"]
 
-KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_MERGE, KERNEL_ATTENTION_DECODE = 0, 1, 2, 3
+# kernel ids of the timing API: the prefill-mode attention grid, the standalone
+# append, the decode-mode attention grid, the split merge
+KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE = 0, 1, 2, 3
 
 
 class VpkError(RuntimeError):

@@ -57,7 +57,7 @@ std::mutex g_tmu;
 std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_tpending;
 std::vector<hipEvent_t> g_tfree;
-constexpr int kTimedKernels = 4;   // 0 prefill-mode attention, 1 append, 2 merge, 3 decode-mode attention
+constexpr int kTimedKernels = 4;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge
 double g_tms[kTimedKernels] = {0, 0, 0, 0};
 int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0};
 
@@ -177,10 +177,11 @@ int32_t get_workspace(hipStream_t stream, size_t plan_need, size_t part_need, Wo
     void* p = nullptr;
     e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
+    // error flag and zero rows
     e = hipMemset(p, 0, kFlagBytes);
     if (e != hipSuccess) {
       (void)hipFree(p);
-      return hip_fail(e, "hipMemset workspace flag");
+      return hip_fail(e, "hipMemset workspace head");
     }
     w->dev = static_cast<char*>(p);
     w->bytes = bytes;
@@ -437,9 +438,9 @@ int32_t upload_plan(Workspace* w, hipStream_t stream, const Plan& p, const Layou
   return upload_plan_region(w, stream, buf.data(), buf.size(), region);
 }
 
-int32_t enqueue_append(const Call& c, Workspace* w, char* R, const Layout& L, const void* k_new,
-                       const void* v_new, void* k_cache, void* v_cache,
-                       const int32_t* block_table, hipStream_t stream) {
+AppendParams append_params(const Call& c, Workspace* w, char* R, const Layout& L,
+                           const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* block_table) {
   const vpk_dims* d = c.d;
   AppendParams ap{};
   ap.k_new = static_cast<const uint16_t*>(k_new);
@@ -459,6 +460,10 @@ int32_t enqueue_append(const Call& c, Workspace* w, char* R, const Layout& L, co
   ap.fp8 = c.fp8 ? 1 : 0;
   ap.k_inv_scale = c.fp8 ? 1.0f / c.kv_scale[0] : 1.0f;
   ap.v_inv_scale = c.fp8 ? 1.0f / c.kv_scale[1] : 1.0f;
+  return ap;
+}
+
+int32_t enqueue_append(const AppendParams& ap, hipStream_t stream) {
   KernelTimer tm(1, stream);
   const int rc = vpk::launch_append(ap, stream);
   if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "append launch");
@@ -534,16 +539,26 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   char* const R = w->plan_region(region);
   char* const PA = w->parts();
 
-  if (c.has_cache && c.has_new && dims->total_knew > 0) {
-    if ((st = enqueue_append(c, w, R, L, k_new, v_new, k_cache, v_cache, block_table, stream))) return st;
-  }
+  const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
+  const AppendParams ap = append_params(c, w, R, L, k_new, v_new, k_cache, v_cache, block_table);
+  // bf16 cache: attention reads the new tokens from k_new / v_new (the same
+  // bytes the append stores), so the append can run inside an attention grid.
+  // fp8 cache: attention must see the quantised bytes, so the append runs first.
+  const bool new_direct = do_append && !c.fp8;
   const bool run_pre = plan.prefill.grid > 0;
   const bool run_dec = plan.decode.grid > 0;
+  const bool fuse_append = new_direct && !plan.persistent && (run_pre || run_dec);
+  if (do_append && !fuse_append) {
+    if ((st = enqueue_append(ap, stream))) return st;
+  }
   if (run_pre || run_dec) {
     AttnParams p{};
     p.q = static_cast<const uint16_t*>(q);
     p.k = c.has_cache ? k_cache : k_new;
     p.v = c.has_cache ? v_cache : v_new;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.new_direct = new_direct ? 1 : 0;
     p.block_table = block_table;
     p.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
     p.out = static_cast<uint16_t*>(out);
@@ -571,36 +586,42 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
                                          (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
     p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
+    p.app = ap;
     const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
-    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s) -> int32_t {
+    // `with_append`: this grid also runs one workgroup per new token
+    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s, bool with_append) -> int32_t {
       AttnParams q = p;
       q.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
       q.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
       q.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
       q.num_items = Lc.count;
-      KernelTimer tm(dec ? 3 : 0, s);
-      const int rc = vpk::launch_attention(q, Lc.grid, dims->head_dim, fmt, c.has_cache, dec, s);
+      q.attn_blocks = Lc.grid;
+      const int grid = Lc.grid + (with_append ? dims->total_knew : 0);
+      KernelTimer tm(dec ? 2 : 0, s);
+      const int rc = vpk::launch_attention(q, grid, dims->head_dim, fmt, c.has_cache, dec, s);
       if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
       return VPK_SUCCESS;
     };
     if (run_pre && run_dec) {
       // both grids at once: the decode-mode grid (HBM-bound) on the side
-      // stream next to the prefill-mode grid (MFMA-bound), joined before merge
+      // stream next to the prefill-mode grid (MFMA-bound), joined at the end
       if ((st = ensure_aux(w))) return st;
       hipError_t e;
       if ((e = hipEventRecord(w->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
       if ((e = hipStreamWaitEvent(w->aux, w->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
-      if ((st = launch(plan.decode, true, w->aux))) return st;
+      if ((st = launch(plan.decode, true, w->aux, fuse_append))) return st;
       if ((e = hipEventRecord(w->ev_join, w->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
-      if ((st = launch(plan.prefill, false, stream))) return st;
+      if ((st = launch(plan.prefill, false, stream, false))) return st;
       if ((e = hipStreamWaitEvent(stream, w->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
     } else if (run_pre) {
-      if ((st = launch(plan.prefill, false, stream))) return st;
+      if ((st = launch(plan.prefill, false, stream, fuse_append))) return st;
     } else {
-      if ((st = launch(plan.decode, true, stream))) return st;
+      if ((st = launch(plan.decode, true, stream, fuse_append))) return st;
     }
   }
   if (!plan.groups.empty()) {
+    // a8: LSE merge of split parts, after the grids (the kernel boundary makes
+    // the partials visible across the device without per-part fences)
     MergeParams mp{};
     mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
     mp.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
@@ -613,7 +634,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     mp.g = dims->num_q_heads / dims->num_kv_heads;
     mp.total_q = dims->total_q;
     mp.head_dim = dims->head_dim;
-    KernelTimer tm(2, stream);
+    KernelTimer tm(3, stream);
     const int rc = vpk::launch_merge(mp, stream);
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
   }
@@ -655,8 +676,9 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   if ((st = get_workspace(stream, L.plan_end, 0, &w))) return st;
   int region = 0;
   if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B, &region))) return st;
-  if ((st = enqueue_append(c, w, w->plan_region(region), L, k_new, v_new, k_cache, v_cache,
-                           block_table, stream)))
+  if ((st = enqueue_append(append_params(c, w, w->plan_region(region), L, k_new, v_new, k_cache,
+                                         v_cache, block_table),
+                           stream)))
     return st;
   return release_region(w, stream, region);
 }

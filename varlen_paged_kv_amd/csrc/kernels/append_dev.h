@@ -1,0 +1,97 @@
+// Device code of the in-place append, shared by the standalone append kernel
+// and the attention kernel (which runs the append as extra workgroups of its
+// grid when attention does not depend on the stored bytes).
+//
+// New token j of sequence b goes to logical position pos = Lc + j: page
+// block_table[b][pos / S], slot pos % S.  With the [P, S, Hkv, D] cache layout
+// all kv heads of one slot are contiguous, so each token is one contiguous row
+// of Hkv * D elements for K and one for V.  ("Add
+// flash_attn_varlen_func_with_kvcache", Usage: the cache is updated in place;
+// Minor Changes: the cache length is passed per sequence and the new tokens
+// carry their own cumulative offsets.)
+//
+// bf16 caches receive the bf16 bytes unchanged.  fp8 caches receive OCP
+// e4m3fn codes of fp32(x) * fp32(1 / scale), rounded to nearest with ties to
+// even, saturated to +-448, NaN kept with its sign (8-bit KV cache of the vLLM
+// Triton FAv2 PR page's feature list, per-tensor scale).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../vpk_internal.h"
+
+namespace vpk {
+namespace append_detail {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// float32 magnitude -> e4m3fn code: nearest, ties to even, satfinite.  The
+// sign bit comes from the unscaled input (1/scale > 0, so it is the product's
+// sign for every non-NaN input, and it keeps a NaN's sign deterministic).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x, uint32_t sign) {
+  const uint32_t a = __float_as_uint(x) & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (and inf): saturate
+  if (a >= 0x3C800000u) {                            // |x| >= 2^-6: normal code
+    // keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));
+  }
+  // subnormal code m * 2^-9, m = round-to-nearest-even(|x| * 2^9) in 0..8
+  const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | static_cast<uint32_t>(m);
+}
+
+__device__ __forceinline__ uint32_t enc2(uint32_t two_bf16, float inv) {
+  const float lo = __uint_as_float(two_bf16 << 16) * inv;
+  const float hi = __uint_as_float(two_bf16 & 0xFFFF0000u) * inv;
+  return f32_to_e4m3(lo, (two_bf16 >> 8) & 0x80u) | (f32_to_e4m3(hi, (two_bf16 >> 24) & 0x80u) << 8);
+}
+
+}  // namespace append_detail
+
+// Store new token t (0 <= t < total_knew) with `nthreads` threads of index
+// `tid`.  A page id outside [0, num_pages) drops the token and raises bit 0 of
+// the device error flag instead of writing out of bounds.
+__device__ __forceinline__ void append_token(const AppendParams& p, int t, int tid, int nthreads) {
+  using namespace append_detail;
+  // sequence of token t: largest b with cu_knew[b] <= t
+  int lo = 0, hi = p.batch;   // invariant: cu_knew[lo] <= t < cu_knew[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cu_knew[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int pos = p.seqs[b].cache_len + (t - p.cu_knew[b]);
+  const int pi = pos / p.page_size;
+  const int slot = pos - pi * p.page_size;
+  const int page = (pi < p.max_pages) ? p.block_table[static_cast<int64_t>(b) * p.max_pages + pi] : -1;
+  if (page < 0 || page >= p.num_pages) {
+    if (tid == 0) atomicOr(p.err_flag, 1);
+    return;
+  }
+  const int64_t dst_row = (static_cast<int64_t>(page) * p.page_size + slot) * p.row_elems;
+  const int64_t src_row = static_cast<int64_t>(t) * p.row_elems;
+  const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
+  for (int c = tid; c < 2 * chunks; c += nthreads) {
+    const bool is_v = c >= chunks;
+    const int cc = is_v ? c - chunks : c;
+    const uint16_t* src = (is_v ? p.v_new : p.k_new) + src_row + cc * 8;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+    if (p.fp8) {
+      const float inv = is_v ? p.v_inv_scale : p.k_inv_scale;
+      uint8_t* dst = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
+      u32x2 y;
+      y[0] = enc2(x[0], inv) | (enc2(x[1], inv) << 16);
+      y[1] = enc2(x[2], inv) | (enc2(x[3], inv) << 16);
+      *reinterpret_cast<u32x2*>(dst) = y;
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
+      *reinterpret_cast<u32x4*>(dst) = x;
+    }
+  }
+}
+
+}  // namespace vpk

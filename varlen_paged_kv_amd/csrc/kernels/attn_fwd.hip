@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include "../vpk_internal.h"
+#include "append_dev.h"
 
 namespace vpk {
 namespace {
@@ -122,20 +123,33 @@ struct Kernel {
   static_assert(kWaves * kWaveRows * D * 4 <= 2 * C::STAGE * 2, "combine area fits the stages");
 
   struct Item {
-    const char* kb;      // K base (bytes)
+    const char* kb;      // K base (bytes): cache, or the new tokens without a cache
     const char* vb;      // V base (bytes)
+    const char* knb;     // new-token K rows read directly (bf16 cache, new_direct)
+    const char* vnb;
     const int32_t* pids;
     int first_page;
     int kn_start;
+    int cache_len;
     int kvh;
     int kend;
+    bool new_direct;
   };
 
-  // Byte offset of key `key`'s row for the item's kv head, or -1 when the key
-  // is past the item's end or its page id is unusable.
-  __device__ static __forceinline__ int64_t row_off(const AttnParams& p, const Item& it, int key) {
-    if (key >= it.kend) return -1;
+  // Sources of key `key`'s K and V rows for the item's kv head; false when the
+  // key is past the item's end or its page id is unusable.
+  __device__ static __forceinline__ bool row_src(const AttnParams& p, const Item& it, int key,
+                                                 const char*& kp, const char*& vp) {
+    if (key >= it.kend) return false;
     if constexpr (PAGED) {
+      if (FMT == kKvBf16 && it.new_direct && key >= it.cache_len) {
+        // a new token: same bf16 bytes as the slot the append fills
+        const int64_t off =
+            (static_cast<int64_t>(it.kn_start + key - it.cache_len) * p.hkv + it.kvh) * (D * 2);
+        kp = it.knb + off;
+        vp = it.vnb + off;
+        return true;
+      }
       int pi, slot;
       if (p.page_shift >= 0) {
         pi = key >> p.page_shift;
@@ -145,10 +159,16 @@ struct Kernel {
         slot = key - pi * p.page_size;
       }
       const int page = it.pids[pi - it.first_page];
-      if (page < 0) return -1;
-      return ((static_cast<int64_t>(page) * p.page_size + slot) * p.hkv + it.kvh) * (D * ESIZE);
+      if (page < 0) return false;
+      const int64_t off = ((static_cast<int64_t>(page) * p.page_size + slot) * p.hkv + it.kvh) * (D * ESIZE);
+      kp = it.kb + off;
+      vp = it.vb + off;
+      return true;
     } else {
-      return (static_cast<int64_t>(it.kn_start + key) * p.hkv + it.kvh) * (D * ESIZE);
+      const int64_t off = (static_cast<int64_t>(it.kn_start + key) * p.hkv + it.kvh) * (D * ESIZE);
+      kp = it.kb + off;
+      vp = it.vb + off;
+      return true;
     }
   }
 
@@ -163,11 +183,10 @@ struct Kernel {
     for (int i = 0; i < nrows / RPI; ++i) {
       const int r = row0 + i * RPI + lane / C::CHUNKS;
       const int c = (lane % C::CHUNKS) ^ C::swz(r);          // global chunk for this LDS slot
-      const int64_t off = row_off(p, it, kbase + r);
-      const char* gk = off >= 0 ? it.kb + off + c * 16 : zeros;
-      const char* gv = off >= 0 ? it.vb + off + c * 16 : zeros;
-      dma16(gk, ktile + (row0 + i * RPI) * D);
-      dma16(gv, vtile + (row0 + i * RPI) * D);
+      const char *kp, *vp;
+      const bool ok = row_src(p, it, kbase + r, kp, vp);
+      dma16(ok ? kp + c * 16 : zeros, ktile + (row0 + i * RPI) * D);
+      dma16(ok ? vp + c * 16 : zeros, vtile + (row0 + i * RPI) * D);
     }
   }
 
@@ -187,11 +206,10 @@ struct Kernel {
       const int idx = tid + i * nthreads;
       const int row = row0 + idx / F8CH;
       const int c = idx % F8CH;
-      const int64_t off = (row < row0 + nrows) ? row_off(p, it, kbase + row) : -1;
-      const bool ok = off >= 0;
-      const int64_t o = ok ? off + c * 16 : 0;
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(it.kb + o);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(it.vb + o);
+      const char *kp = it.kb, *vp = it.vb;
+      const bool ok = row < row0 + nrows && row_src(p, it, kbase + row, kp, vp);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(ok ? kp + c * 16 : it.kb);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(ok ? vp + c * 16 : it.vb);
       r.k[i] = ok ? kv : z;
       r.v[i] = ok ? vv : z;
     }
@@ -590,6 +608,12 @@ struct Kernel {
     const int lg = lane >> 5;   // lane half
     const float c = p.qk_scale_log2;
 
+    // workgroups past the attention part of the grid store new tokens
+    if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
+      append_token(p.app, blockIdx.x - p.attn_blocks, t, kThreads);
+      return;
+    }
+
     int w_idx = blockIdx.x, w_end = blockIdx.x + 1;
     if (p.persistent) {
       w_idx = p.queue_start[blockIdx.x];
@@ -607,11 +631,15 @@ struct Kernel {
       Item it;
       it.kb = static_cast<const char*>(p.k);
       it.vb = static_cast<const char*>(p.v);
+      it.knb = static_cast<const char*>(p.k_new);
+      it.vnb = static_cast<const char*>(p.v_new);
       it.pids = pids;
       it.first_page = 0;
       it.kn_start = sq.kn_start;
+      it.cache_len = sq.cache_len;
       it.kvh = kvh;
       it.kend = item.key_end;
+      it.new_direct = p.new_direct != 0;
 
       // ---- page ids of the item's key range -> LDS
       if constexpr (PAGED) {

@@ -57,36 +57,6 @@ struct MergeGroup {
 
 enum KvFormat : int32_t { kKvBf16 = 0, kKvFp8 = 1 };
 
-struct AttnParams {
-  const uint16_t* q;          // bf16 [Tq, Hq, D]
-  const void* k;              // cache [P, S, Hkv, D] or k_new [Tn, Hkv, D]
-  const void* v;
-  const int32_t* block_table; // [B, max_pages] (paged only)
-  const SeqInfo* seqs;
-  const WorkItem* items;      // this grid's units
-  const int32_t* queue_start; // persistent: [num_queues + 1] offsets into queue_work
-  const int32_t* queue_work;  // persistent: unit * hkv + kv_head, grouped by queue
-  uint16_t* out;              // bf16 [Tq, Hq, D]
-  float* lse;                 // [Hq, Tq] or null
-  float* part_o;              // [rows, D] fp32, normalised partial outputs
-  float* part_lse;            // [rows]
-  int32_t* err_flag;
-  const void* zeros;          // >= 256 zero bytes: source of rows past the keys
-  int32_t num_items;
-  int32_t persistent;
-  int32_t max_pages;
-  int32_t num_pages;
-  int32_t page_size;
-  int32_t page_shift;         // log2(page_size) or -1
-  int32_t hq;
-  int32_t hkv;
-  int32_t g;
-  int32_t total_q;
-  int32_t causal;
-  float qk_scale_log2;        // scale * log2(e) (* k_scale for fp8)
-  float v_scale;              // 1 (bf16) or v_scale (fp8)
-};
-
 struct AppendParams {
   const uint16_t* k_new;      // bf16 [Tn, Hkv, D]
   const uint16_t* v_new;
@@ -106,6 +76,45 @@ struct AppendParams {
   float k_inv_scale;          // fp32(1 / k_scale)
   float v_inv_scale;
 };
+
+struct AttnParams {
+  const uint16_t* q;          // bf16 [Tq, Hq, D]
+  const void* k;              // cache [P, S, Hkv, D] or k_new [Tn, Hkv, D]
+  const void* v;
+  const int32_t* block_table; // [B, max_pages] (paged only)
+  const SeqInfo* seqs;
+  const WorkItem* items;      // this grid's units
+  const int32_t* queue_start; // persistent: [num_queues + 1] offsets into queue_work
+  const int32_t* queue_work;  // persistent: unit * hkv + kv_head, grouped by queue
+  const void* k_new;          // new tokens, read directly when new_direct is set
+  const void* v_new;
+  uint16_t* out;              // bf16 [Tq, Hq, D]
+  float* lse;                 // [Hq, Tq] or null
+  float* part_o;              // [rows, D] fp32, normalised partial outputs
+  float* part_lse;            // [rows]
+  int32_t* err_flag;
+  const void* zeros;          // >= 256 zero bytes: source of rows past the keys
+  int32_t num_items;
+  int32_t persistent;
+  int32_t new_direct;         // keys >= cache_len come from k_new / v_new (bf16 cache)
+  int32_t attn_blocks;        // workgroups past this index run the append instead
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t page_shift;         // log2(page_size) or -1
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  int32_t total_q;
+  int32_t causal;
+  float qk_scale_log2;        // scale * log2(e) (* k_scale for fp8)
+  float v_scale;              // 1 (bf16) or v_scale (fp8)
+  AppendParams app;           // the append, when it runs inside this grid
+};
+
+
+
+
 
 struct MergeParams {
   const MergeGroup* groups;
