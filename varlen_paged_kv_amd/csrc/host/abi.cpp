@@ -14,7 +14,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../../include/vpk.h"
+#include "vpk.h"
 #include "../vpk_internal.h"
 #include "plan.h"
 
@@ -97,33 +97,32 @@ struct KernelTimer {
 constexpr size_t kFlagBytes = 512;
 constexpr size_t kZerosOffset = 256;
 
-struct Staging {
-  void* host = nullptr;
+// Plans live in pinned host memory that the kernels read directly (each
+// workgroup reads its unit and sequence records once): no copy, no copy
+// stream, no cross-stream dependency on the critical path.  A ring of buffers
+// lets the host plan ahead of the GPU; a buffer is reused once the event
+// recorded behind the last kernel that read it has completed.
+constexpr int kPlanRing = 8;
+
+struct PlanBuf {
+  char* host = nullptr;      // pinned, device-accessible
   size_t bytes = 0;
-  hipEvent_t ev = nullptr;
+  hipEvent_t ev = nullptr;   // recorded after the kernels of the call that used it
   bool pending = false;
 };
 
 struct Workspace {
   int device = -1;
-  char* dev = nullptr;
+  char* dev = nullptr;       // [flag | zeros][split partials]
   size_t bytes = 0;
-  // device layout: [flag | zeros][plan region 0][plan region 1][partials]
-  size_t plan_cap = 0;       // bytes of each plan region
-  size_t part_cap = 0;       // bytes of the partials area
-  Staging stage[4];          // pinned host copies of uploaded plans
+  size_t part_cap = 0;
+  PlanBuf plan[kPlanRing];
   int next = 0;
-  int flip = 0;              // plan region of the next call
-  bool used_valid[2] = {false, false};
-  hipEvent_t ev_used[2] = {nullptr, nullptr};   // kernels that read region r are done
-  // copy stream: the next call's plan upload overlaps the current call's kernels
-  hipStream_t copy = nullptr;
   // side stream for running the decode-mode grid next to the prefill-mode grid
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_join = nullptr;
-  char* plan_region(int r) const { return dev + kFlagBytes + static_cast<size_t>(r) * plan_cap; }
-  char* parts() const { return dev + kFlagBytes + 2 * plan_cap; }
+  char* parts() const { return dev + kFlagBytes; }
 };
 
 int32_t ensure_aux(Workspace* w) {
@@ -142,9 +141,9 @@ std::map<std::pair<int, void*>, Workspace*> g_ws;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The workspace of (current device, stream) with room for a plan of
-// `plan_need` bytes and `part_need` bytes of split partials.
-int32_t get_workspace(hipStream_t stream, size_t plan_need, size_t part_need, Workspace** out) {
+// The workspace of (current device, stream) with `part_need` bytes of split
+// partials in device memory.
+int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -154,90 +153,65 @@ int32_t get_workspace(hipStream_t stream, size_t plan_need, size_t part_need, Wo
     w = new (std::nothrow) Workspace();
     if (!w) return fail(VPK_ERROR_OUT_OF_MEMORY, "workspace bookkeeping");
     w->device = dev;
-    if ((e = hipStreamCreateWithFlags(&w->copy, hipStreamNonBlocking)) != hipSuccess)
-      return hip_fail(e, "hipStreamCreateWithFlags (copy stream)");
-    for (int r = 0; r < 2; ++r)
-      if ((e = hipEventCreateWithFlags(&w->ev_used[r], hipEventDisableTiming)) != hipSuccess)
-        return hip_fail(e, "hipEventCreate (plan region)");
   }
-  if (w->plan_cap < plan_need || w->part_cap < part_need) {
+  if (!w->dev || w->part_cap < part_need) {
     if (w->dev) {
       // everything that may still read the old buffer is on these streams
       if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (workspace growth)");
-      if ((e = hipStreamSynchronize(w->copy)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (copy stream)");
       if (w->aux && (e = hipStreamSynchronize(w->aux)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize (side stream)");
       (void)hipFree(w->dev);
       w->dev = nullptr;
       w->bytes = 0;
-      w->used_valid[0] = w->used_valid[1] = false;
     }
-    const size_t pc = align_up(std::max(std::max(plan_need + plan_need / 2, w->plan_cap), static_cast<size_t>(64) << 10), 4096);
     const size_t qc = align_up(std::max(part_need + part_need / 2, w->part_cap), 4096);
-    const size_t bytes = kFlagBytes + 2 * pc + qc;
+    const size_t bytes = kFlagBytes + qc;
     void* p = nullptr;
     e = hipMalloc(&p, bytes);
     if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipMalloc workspace: ") + hipGetErrorString(e));
-    // error flag and zero rows
-    e = hipMemset(p, 0, kFlagBytes);
+    e = hipMemset(p, 0, kFlagBytes);   // error flag and zero rows
     if (e != hipSuccess) {
       (void)hipFree(p);
       return hip_fail(e, "hipMemset workspace head");
     }
     w->dev = static_cast<char*>(p);
     w->bytes = bytes;
-    w->plan_cap = pc;
     w->part_cap = qc;
   }
   *out = w;
   return VPK_SUCCESS;
 }
 
-// Copy a plan into the next plan region on the copy stream: the copy waits for
-// the kernels that last read that region, and `stream` waits for the copy.
-// Returns the region in *region.
-int32_t upload_plan_region(Workspace* w, hipStream_t stream, const void* src, size_t bytes,
-                           int* region) {
-  const int r = w->flip;
-  w->flip ^= 1;
-  *region = r;
-  if (bytes == 0) return VPK_SUCCESS;
-  Staging& st = w->stage[w->next];
-  w->next = (w->next + 1) % 4;
+// The next plan buffer with room for `bytes`, once the GPU is done with it.
+int32_t take_plan_buffer(Workspace* w, size_t bytes, int* index) {
+  const int k = w->next;
+  w->next = (w->next + 1) % kPlanRing;
+  PlanBuf& pb = w->plan[k];
   hipError_t e;
-  if (st.pending) {
-    e = hipEventSynchronize(st.ev);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging)");
-    st.pending = false;
+  if (pb.pending) {
+    e = hipEventSynchronize(pb.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (plan buffer)");
+    pb.pending = false;
   }
-  if (!st.ev) {
-    e = hipEventCreateWithFlags(&st.ev, hipEventDisableTiming);
-    if (e != hipSuccess) return hip_fail(e, "hipEventCreate (staging)");
-  }
-  if (st.bytes < bytes) {
-    if (st.host) (void)hipHostFree(st.host);
-    st.host = nullptr;
-    st.bytes = 0;
+  if (!pb.ev && (e = hipEventCreateWithFlags(&pb.ev, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "hipEventCreate (plan buffer)");
+  if (pb.bytes < bytes) {
+    if (pb.host) (void)hipHostFree(pb.host);
+    pb.host = nullptr;
+    pb.bytes = 0;
     const size_t nb = align_up(std::max(bytes + bytes / 2, static_cast<size_t>(64) << 10), 4096);
-    e = hipHostMalloc(&st.host, nb, hipHostMallocDefault);
+    e = hipHostMalloc(reinterpret_cast<void**>(&pb.host), nb, hipHostMallocDefault);
     if (e != hipSuccess) return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipHostMalloc: ") + hipGetErrorString(e));
-    st.bytes = nb;
+    pb.bytes = nb;
   }
-  std::memcpy(st.host, src, bytes);
-  if (w->used_valid[r] && (e = hipStreamWaitEvent(w->copy, w->ev_used[r], 0)) != hipSuccess)
-    return hip_fail(e, "hipStreamWaitEvent (plan region reuse)");
-  e = hipMemcpyAsync(w->plan_region(r), st.host, bytes, hipMemcpyHostToDevice, w->copy);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
-  if ((e = hipEventRecord(st.ev, w->copy)) != hipSuccess) return hip_fail(e, "hipEventRecord (staging)");
-  st.pending = true;
-  if ((e = hipStreamWaitEvent(stream, st.ev, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (plan ready)");
+  *index = k;
   return VPK_SUCCESS;
 }
 
-// Mark plan region r as read by everything enqueued on `stream` so far.
-int32_t release_region(Workspace* w, hipStream_t stream, int r) {
-  hipError_t e = hipEventRecord(w->ev_used[r], stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan region)");
-  w->used_valid[r] = true;
+// Mark plan buffer k as read by everything enqueued on `stream` so far.
+int32_t release_plan_buffer(Workspace* w, hipStream_t stream, int k) {
+  hipError_t e = hipEventRecord(w->plan[k].ev, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan buffer)");
+  w->plan[k].pending = true;
   return VPK_SUCCESS;
 }
 
@@ -399,9 +373,9 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
   in.split_min_keys = static_cast<int32_t>(g_opt.split_min_keys.load());
 }
 
-// Plan region layout (offsets from the region start):
+// Plan buffer layout (pinned host memory, offsets from its start):
 //   [seqs][cu_knew][units][merge groups][queue starts][queue work]
-// Partials area: [part_o fp32 rows x D][part_lse fp32 rows]
+// Partials area (device memory): [part_o fp32 rows x D][part_lse fp32 rows]
 struct Layout {
   size_t seqs, cu_kn, items, groups, queues, work, plan_end, part_o, part_lse, part_end;
 };
@@ -421,12 +395,12 @@ Layout layout_for(const Plan& p, int32_t B, int32_t D) {
   return L;
 }
 
-// Serialise the plan (host) and upload it; *region receives the plan region used.
-int32_t upload_plan(Workspace* w, hipStream_t stream, const Plan& p, const Layout& L,
-                    const int32_t* cu_kn, int32_t B, int* region) {
-  static thread_local std::vector<char> buf;
-  buf.assign(L.plan_end, 0);
-  char* base = buf.data();
+// Serialise the plan into the next pinned plan buffer; *index receives it.
+int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B,
+                   int* index) {
+  int32_t st = take_plan_buffer(w, L.plan_end, index);
+  if (st) return st;
+  char* base = w->plan[*index].host;
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
   if (cu_kn) std::memcpy(base + L.cu_kn, cu_kn, sizeof(int32_t) * (B + 1));
   if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
@@ -435,7 +409,7 @@ int32_t upload_plan(Workspace* w, hipStream_t stream, const Plan& p, const Layou
     std::memcpy(base + L.queues, p.queue_start.data(), sizeof(int32_t) * p.queue_start.size());
   if (!p.queue_work.empty())
     std::memcpy(base + L.work, p.queue_work.data(), sizeof(int32_t) * p.queue_work.size());
-  return upload_plan_region(w, stream, buf.data(), buf.size(), region);
+  return VPK_SUCCESS;
 }
 
 AppendParams append_params(const Call& c, Workspace* w, char* R, const Layout& L,
@@ -533,10 +507,10 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   }
   const Layout L = layout_for(plan, B, dims->head_dim);
   Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.plan_end, L.part_end, &w))) return st;
+  if ((st = get_workspace(stream, L.part_end, &w))) return st;
   int region = 0;
-  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B, &region))) return st;
-  char* const R = w->plan_region(region);
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
+  char* const R = w->plan[region].host;
   char* const PA = w->parts();
 
   const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
@@ -638,7 +612,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     const int rc = vpk::launch_merge(mp, stream);
     if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
   }
-  return release_region(w, stream, region);
+  return release_plan_buffer(w, stream, region);
 }
 
 int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
@@ -673,14 +647,14 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   }
   const Layout L = layout_for(plan, B, dims->head_dim);
   Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.plan_end, 0, &w))) return st;
+  if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
-  if ((st = upload_plan(w, stream, plan, L, m.cu_kn, B, &region))) return st;
-  if ((st = enqueue_append(append_params(c, w, w->plan_region(region), L, k_new, v_new, k_cache,
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
+  if ((st = enqueue_append(append_params(c, w, w->plan[region].host, L, k_new, v_new, k_cache,
                                          v_cache, block_table),
                            stream)))
     return st;
-  return release_region(w, stream, region);
+  return release_plan_buffer(w, stream, region);
 }
 
 }  // namespace
