@@ -148,17 +148,32 @@ void build_plan(const PlanInput& in, Plan& out) {
     }
   }
 
-  // ---- order: prefill-mode units, then decode-mode units; each longest
-  //      first, ties in tile / part order (deterministic)
+  // ---- order: prefill-mode units, then decode-mode units.  Prefill-mode
+  //      units are grouped by sequence (heaviest sequence first) and run
+  //      longest first inside it: the workgroups resident at one time then
+  //      share one sequence's keys and values, which stay in the L2 of their
+  //      XCD (workgroup w runs on XCD w mod 8 and the grid index is
+  //      unit * Hkv + kv head, so with 8 kv heads each XCD serves one head).
+  //      Decode-mode units run longest first.  Ties in tile / part order.
   static thread_local std::vector<int32_t> order;
+  static thread_local std::vector<double> seq_cost;
   order.resize(units.size());
   std::iota(order.begin(), order.end(), 0);
+  seq_cost.assign(B, 0.0);
+  for (const Unit& u : units) seq_cost[tiles[u.tile].seq] += u.cost;
   // decode mode for sequences whose packed rows all fit one wave (q_len * g <=
   // 32); a prefill sequence's short last tile stays with its other tiles
   auto is_dec = [&](int32_t ui) { return tiles[units[ui].tile].dec; };
   std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
     const bool da = is_dec(a), db = is_dec(b);
     if (da != db) return !da;
+    if (!da) {
+      const int32_t sa = tiles[units[a].tile].seq, sb = tiles[units[b].tile].seq;
+      if (sa != sb) {
+        if (seq_cost[sa] != seq_cost[sb]) return seq_cost[sa] > seq_cost[sb];
+        return sa < sb;
+      }
+    }
     if (units[a].cost != units[b].cost) return units[a].cost > units[b].cost;
     return a < b;
   });

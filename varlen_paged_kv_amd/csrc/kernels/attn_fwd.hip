@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../vpk_internal.h"
 #include "append_dev.h"
 
@@ -55,6 +57,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLazyLog2 = 8.f;   // log2 of the largest unnormalised p kept before rescaling
 
 template <int D>
 struct Cfg {
@@ -63,12 +66,17 @@ struct Cfg {
   static constexpr int STAGE = 2 * TILE;        // K tile then V tile
   static constexpr int KSTEPS = D / 16;         // MFMA k-steps over the head dim
   static constexpr int DBLK = D / 32;           // 32-wide output blocks over the head dim
-  // XOR swizzle of the chunk index by row: conflict-free for the K operand
-  // reads (16 consecutive rows, one chunk) and for the transposed V reads
-  // (4 consecutive rows, two adjacent chunks)
+  // XOR swizzle of the chunk index by row.  The K operand reads take one
+  // chunk of 16 consecutive rows per 16 lanes; the transposed V reads take
+  // chunks 0..3 (of one 64-byte column group) of 4 consecutive rows per 32
+  // lanes.  Both hit every LDS bank once when the swizzle is a bijection on
+  // any 16 aligned rows and puts the 4 rows of an aligned quad into different
+  // 64-byte bank groups (bits 2-3 of the chunk for 256-byte rows; for
+  // 128-byte rows, two rows share a 256-byte bank line, so the rows of one
+  // parity must differ in bit 2).
   __device__ static __forceinline__ int swz(int r) {
-    if constexpr (CHUNKS == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return ((r & 3) << 1) | ((r >> 2) & 1);
+    if constexpr (CHUNKS == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
   // element offset of chunk c of row r inside a tile
   __device__ static __forceinline__ int at(int r, int c) { return r * D + ((c ^ swz(r)) << 3); }
@@ -123,11 +131,13 @@ struct Kernel {
   static_assert(kWaves * kWaveRows * D * 4 <= 2 * C::STAGE * 2, "combine area fits the stages");
 
   struct Item {
-    const char* kb;      // K base (bytes): cache, or the new tokens without a cache
+    const char* kb;      // K base (bytes) at this item's kv head: cache, or the new tokens without a cache
     const char* vb;      // V base (bytes)
     const char* knb;     // new-token K rows read directly (bf16 cache, new_direct)
     const char* vnb;
     const int32_t* pids;
+    uint32_t row_bytes;  // bytes between consecutive token rows of kb / vb
+    uint32_t new_row_bytes;
     int first_page;
     int kn_start;
     int cache_len;
@@ -137,35 +147,40 @@ struct Kernel {
   };
 
   // Sources of key `key`'s K and V rows for the item's kv head; false when the
-  // key is past the item's end or its page id is unusable.
+  // key is past the item's end (tested only with CHECK) or its page id is
+  // unusable.  Token row indices fit 32 bits (the host rejects caches with
+  // 2^32 or more slots), so each address is one 32x32->64-bit multiply-add.
+  template <bool CHECK>
   __device__ static __forceinline__ bool row_src(const AttnParams& p, const Item& it, int key,
                                                  const char*& kp, const char*& vp) {
-    if (key >= it.kend) return false;
+    if (CHECK && key >= it.kend) return false;
     if constexpr (PAGED) {
       if (FMT == kKvBf16 && it.new_direct && key >= it.cache_len) {
         // a new token: same bf16 bytes as the slot the append fills
-        const int64_t off =
-            (static_cast<int64_t>(it.kn_start + key - it.cache_len) * p.hkv + it.kvh) * (D * 2);
+        const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(it.kn_start + key - it.cache_len)) *
+                             it.new_row_bytes;
         kp = it.knb + off;
         vp = it.vnb + off;
         return true;
       }
-      int pi, slot;
+      uint32_t pi, slot;
       if (p.page_shift >= 0) {
-        pi = key >> p.page_shift;
-        slot = key & (p.page_size - 1);
+        pi = static_cast<uint32_t>(key) >> p.page_shift;
+        slot = static_cast<uint32_t>(key) & (p.page_size - 1);
       } else {
-        pi = key / p.page_size;
-        slot = key - pi * p.page_size;
+        pi = static_cast<uint32_t>(key) / static_cast<uint32_t>(p.page_size);
+        slot = static_cast<uint32_t>(key) - pi * p.page_size;
       }
       const int page = it.pids[pi - it.first_page];
       if (page < 0) return false;
-      const int64_t off = ((static_cast<int64_t>(page) * p.page_size + slot) * p.hkv + it.kvh) * (D * ESIZE);
+      const uint64_t off =
+          static_cast<uint64_t>(static_cast<uint32_t>(page) * static_cast<uint32_t>(p.page_size) + slot) *
+          it.row_bytes;
       kp = it.kb + off;
       vp = it.vb + off;
       return true;
     } else {
-      const int64_t off = (static_cast<int64_t>(it.kn_start + key) * p.hkv + it.kvh) * (D * ESIZE);
+      const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(it.kn_start + key)) * it.row_bytes;
       kp = it.kb + off;
       vp = it.vb + off;
       return true;
@@ -175,6 +190,7 @@ struct Kernel {
   // ---- bf16: DMA `nrows` tile rows starting at `row0` (row r holds key
   //      kbase + r) into the K and V tiles; the calling wave issues nrows / RPI
   //      copies of each.
+  template <bool CHECK>
   __device__ static __forceinline__ void dma_rows(const AttnParams& p, const Item& it,
                                                   uint16_t* ktile, uint16_t* vtile, int kbase,
                                                   int row0, int nrows, int lane) {
@@ -184,7 +200,7 @@ struct Kernel {
       const int r = row0 + i * RPI + lane / C::CHUNKS;
       const int c = (lane % C::CHUNKS) ^ C::swz(r);          // global chunk for this LDS slot
       const char *kp, *vp;
-      const bool ok = row_src(p, it, kbase + r, kp, vp);
+      const bool ok = row_src<CHECK>(p, it, kbase + r, kp, vp);
       dma16(ok ? kp + c * 16 : zeros, ktile + (row0 + i * RPI) * D);
       dma16(ok ? vp + c * 16 : zeros, vtile + (row0 + i * RPI) * D);
     }
@@ -207,7 +223,7 @@ struct Kernel {
       const int row = row0 + idx / F8CH;
       const int c = idx % F8CH;
       const char *kp = it.kb, *vp = it.vb;
-      const bool ok = row < row0 + nrows && row_src(p, it, kbase + row, kp, vp);
+      const bool ok = row < row0 + nrows && row_src<true>(p, it, kbase + row, kp, vp);
       const u32x4 kv = *reinterpret_cast<const u32x4*>(ok ? kp + c * 16 : it.kb);
       const u32x4 vv = *reinterpret_cast<const u32x4*>(ok ? vp + c * 16 : it.vb);
       r.k[i] = ok ? kv : z;
@@ -240,13 +256,13 @@ struct Kernel {
   }
 
   // ---- a3..a6 for this wave's 32 query rows over keys [kbase, kbase + 32 NH)
-  //      held in tile rows [trow0, trow0 + 32 NH)
-  template <int NH>
+  //      held in tile rows [trow0, trow0 + 32 NH).  MASK: some key of the block
+  //      lies beyond `lim` (the item's end, or the causal bound of the row).
+  template <int NH, bool MASK>
   __device__ static __forceinline__ void compute(const uint16_t* ktile, const uint16_t* vtile,
                                                  int trow0, const bf16x8 (&qf)[C::KSTEPS],
                                                  f32x16 (&o)[C::DBLK], float& m_run, float& l_run,
-                                                 int kbase, int lim, bool mask, float c, int lr,
-                                                 int lg) {
+                                                 int kbase, int lim, float c, int lr, int lg) {
     // Operand fragments are read from LDS one round ahead of the MFMAs that
     // use them (two rounds per phase), so each read's latency hides behind
     // MFMA or softmax work while the live registers stay within budget.
@@ -304,24 +320,30 @@ struct Kernel {
     __builtin_amdgcn_sched_barrier(0);
 
     // a4: mask; running max of the raw scores (scale > 0 keeps the order)
+    if constexpr (MASK) {
+      const int rel = lim - kbase - lg * 4;   // last visible key, relative to this lane's first
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (h * 32 + (i >> 2) * 8 + (i & 3) > rel) acc[h][i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (mask) {
-          const int key = kbase + h * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          acc[h][i] = key <= lim ? acc[h][i] : -INFINITY;
-        }
-        mx = fmaxf(mx, acc[h][i]);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[h][i]);
     mx = wave_pair_max(mx);
 
-    // a5: p = 2^(c s - c m), one fma per score
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    const float neg_mc = -m_use * c;
+    // a5: p = 2^(c s - c m), one fma per score.  The reference max m moves
+    // only when the block's max exceeds it by more than 2^kLazyLog2 in p:
+    // until then p stays below 2^kLazyLog2 (fine for fp32 sums and for bf16
+    // P), and O and l need no rescaling.  The result after the final division
+    // by l is the same softmax.
+    const bool grow = mx * c > m_run * c + kLazyLog2;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
+    const float neg_mc = m_new == -INFINITY ? 0.f : -m_new * c;
     m_run = m_new;
     float psum = 0.f;
     bf16x8 pf[NH][2];
@@ -334,7 +356,7 @@ struct Kernel {
         pf[h][i >> 3][i & 7] = static_cast<__bf16>(pv);
       }
     l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
+    if (__any(grow)) {
 #pragma unroll
       for (int d = 0; d < C::DBLK; ++d)
 #pragma unroll
@@ -408,7 +430,7 @@ struct Kernel {
       if constexpr (FMT == kKvFp8) {
         f8_load(p, it, fr, kbeg, 0, kBlockN, t, kThreads);
       } else {
-        dma_rows(p, it, st0, st0 + C::TILE, kbeg, wave * 16, 16, lane);
+        dma_rows<true>(p, it, st0, st0 + C::TILE, kbeg, wave * 16, 16, lane);
       }
     }
 
@@ -442,16 +464,21 @@ struct Kernel {
       }
       __syncthreads();
     }
-    for (int n = 0; n < nblk; ++n) {
+    // one block: stage block n + 1 while block n is computed
+    auto step = [&](int n, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       uint16_t* const cur = (n & 1) ? st1 : st0;
       uint16_t* const nxt = (n & 1) ? st0 : st1;
       const int kbase = kbeg + n * kBlockN;
       if constexpr (FMT != kKvFp8) {
-        if (n + 1 < nblk) dma_rows(p, it, nxt, nxt + C::TILE, kbase + kBlockN, wave * 16, 16, lane);
+        if (n + 1 < nblk) {
+          if (kbase + 2 * kBlockN <= it.kend)
+            dma_rows<false>(p, it, nxt, nxt + C::TILE, kbase + kBlockN, wave * 16, 16, lane);
+          else
+            dma_rows<true>(p, it, nxt, nxt + C::TILE, kbase + kBlockN, wave * 16, 16, lane);
+        }
       }
-      if (wave_active)
-        compute<2>(cur, cur + C::TILE, 0, qf, o, m_run, l_run, kbase, lim,
-                   kbase + kBlockN - 1 > tile_lim, c, lr, lg);
+      if (wave_active) compute<2, MASK>(cur, cur + C::TILE, 0, qf, o, m_run, l_run, kbase, lim, c, lr, lg);
       if constexpr (FMT == kKvFp8) {
         if (n + 1 < nblk) {
           f8_store(fr, nxt, nxt + C::TILE, 0, kBlockN, t, kThreads);
@@ -461,7 +488,12 @@ struct Kernel {
         wait_vmem();
       }
       __syncthreads();   // stage `cur` is free, stage `nxt` is complete
-    }
+    };
+    // blocks entirely at or below the tile's smallest key bound need no mask
+    const int n_full = min(nblk, max(0, (tile_lim - kbeg + 1) / kBlockN));
+    int n = 0;
+    for (; n < n_full; ++n) step(n, std::false_type{});
+    for (; n < nblk; ++n) step(n, std::true_type{});
 
     if (wave_active) {
       const float l_tot = wave_pair_sum(l_run);
@@ -516,7 +548,8 @@ struct Kernel {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    for (int j = wave; j < nb; j += kWaves) {
+    auto step = [&](int j, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int kbase = kbeg + j * DK;
       wait_lds();   // this wave's reads of its previous block are complete
       if constexpr (FMT == kKvFp8) {
@@ -530,12 +563,20 @@ struct Kernel {
         }
         wait_lds();
       } else {
-        dma_rows(p, it, ktile, vtile, kbase - trow0, trow0, DK, lane);
+        if (kbase + DK <= it.kend)
+          dma_rows<false>(p, it, ktile, vtile, kbase - trow0, trow0, DK, lane);
+        else
+          dma_rows<true>(p, it, ktile, vtile, kbase - trow0, trow0, DK, lane);
         wait_vmem();
       }
-      compute<1>(ktile, vtile, trow0, qf, o, m_run, l_run, kbase, lim, kbase + DK - 1 > tile_lim,
-                 c, lr, lg);
-    }
+      compute<1, MASK>(ktile, vtile, trow0, qf, o, m_run, l_run, kbase, lim, c, lr, lg);
+    };
+    // this wave's blocks j = wave, wave + 4, ...: unmasked while at or below
+    // the item's smallest key bound
+    const int nb_full = min(nb, max(0, (tile_lim - kbeg + 1) / DK));
+    int j = wave;
+    for (; j < nb_full; j += kWaves) step(j, std::false_type{});
+    for (; j < nb; j += kWaves) step(j, std::true_type{});
 
     // ---- combine the four waves' states through LDS
     __syncthreads();                     // every wave is done with its stage
@@ -629,10 +670,12 @@ struct Kernel {
       if (item.part >= 0) item.part += kvh * item.part_stride;
       const SeqInfo sq = p.seqs[item.seq];
       Item it;
-      it.kb = static_cast<const char*>(p.k);
-      it.vb = static_cast<const char*>(p.v);
-      it.knb = static_cast<const char*>(p.k_new);
-      it.vnb = static_cast<const char*>(p.v_new);
+      it.row_bytes = static_cast<uint32_t>(p.hkv) * (D * ESIZE);
+      it.new_row_bytes = static_cast<uint32_t>(p.hkv) * (D * 2);
+      it.kb = static_cast<const char*>(p.k) + kvh * (D * ESIZE);
+      it.vb = static_cast<const char*>(p.v) + kvh * (D * ESIZE);
+      it.knb = static_cast<const char*>(p.k_new) + kvh * (D * 2);
+      it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
       it.pids = pids;
       it.first_page = 0;
       it.kn_start = sq.kn_start;
