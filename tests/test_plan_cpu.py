@@ -39,7 +39,7 @@ def _check_coverage(wl, items, causal, nq=0):
     for it in items:
         seq, row0, nrows, kvh, kb, ke, part, queue = (int(x) for x in it)
         assert 0 <= seq < wl.B and 0 <= kvh < wl.Hkv
-        assert 1 <= nrows <= 128 and 0 <= row0 and row0 + nrows <= ql[seq] * g
+        assert 1 <= nrows <= 256 and 0 <= row0 and row0 + nrows <= ql[seq] * g   # prefill tiles: 256 rows
         assert kb % BLOCK_N == 0 and 0 <= kb and kb <= ke <= kl[seq]
         if nq:
             assert 0 <= queue < nq
@@ -128,7 +128,7 @@ def test_persistent_queues_partition_items():
     vpk.set_option("persistent", 1)
     wl = make_workload("mixed_fp8", lengths_only=True)
     items, nq = _plan(wl, num_cus=64)
-    assert 0 < nq <= 2 * 128                   # one set of queues per grid (prefill- and decode-mode)
+    assert 0 < nq <= 64 + 128                  # queues: one per prefill-mode slot (1 per CU), one per decode-mode slot (2 per CU)
     _check_coverage(wl, items, True, nq=nq)
     q = items[:, 7]
     assert np.all(np.diff(q) >= 0)            # grouped by queue, in queue order

@@ -1,7 +1,7 @@
 // Host-side work planner for the attention launch.
 //
 // Tiles every sequence's packed query rows (token * g + head_in_group) into
-// items of at most 128 rows per kv head, gives each item the keys its rows can
+// items of at most 256 rows per kv head, gives each item the keys its rows can
 // see (the causal bound of its last token), splits items whose cost is far
 // above the average share of a workgroup slot into key-range parts that the
 // merge pass recombines, orders the items longest-first, and (persistent mode)
@@ -70,13 +70,13 @@ void build_plan(const PlanInput& in, Plan& out) {
   // ---- row tiles (shared by all kv heads: every head has the same rows and keys)
   static thread_local std::vector<Tile> tiles;
   tiles.clear();
-  double total = 0.0;
+  double total_pre = 0.0, total_dec = 0.0;
   for (int32_t b = 0; b < B; ++b) {
     const SeqInfo& s = out.seqs[b];
     if (s.q_len <= 0) continue;
     const int64_t rows = static_cast<int64_t>(s.q_len) * g;
-    for (int64_t r0 = 0; r0 < rows; r0 += kTileRows) {
-      const int32_t nr = static_cast<int32_t>(std::min<int64_t>(kTileRows, rows - r0));
+    for (int64_t r0 = 0; r0 < rows; r0 += kPrefillRows) {
+      const int32_t nr = static_cast<int32_t>(std::min<int64_t>(kPrefillRows, rows - r0));
       const int32_t t_last = static_cast<int32_t>((r0 + nr - 1) / g);
       int64_t kend = s.kv_len;
       if (in.causal) kend = std::min<int64_t>(kend, static_cast<int64_t>(t_last) + s.kv_len - s.q_len + 1);
@@ -84,13 +84,19 @@ void build_plan(const PlanInput& in, Plan& out) {
       const int32_t nblk = static_cast<int32_t>((kend + kBlockN - 1) / kBlockN);
       const double c = 0.05 + nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
       tiles.push_back(Tile{b, static_cast<int32_t>(r0), nr, 0, static_cast<int32_t>(kend), c, rows <= kWaveRows});
-      total += c * in.hkv;
+      (rows <= kWaveRows ? total_dec : total_pre) += c * in.hkv;
     }
   }
 
-  // ---- split decision per tile -> units (tile, part)
-  const int64_t slots = static_cast<int64_t>(std::max(1, in.num_cus)) * std::max(1, in.wg_per_cu);
-  const double target = total / static_cast<double>(2 * slots);
+  // ---- split decision per tile -> units (tile, part).  Longest-first
+  //      dealing ends a grid evenly when no tile is much above the average
+  //      load of a workgroup slot; a tile above that (3/4 of the average for
+  //      the MFMA-bound prefill-mode grid, whose partials cost a merge over
+  //      up to 256 rows, 1/2 for the decode-mode grid, whose sequences are
+  //      few and long) is split into parts near that size.
+  const int64_t cus = std::max(1, in.num_cus);
+  const double target_pre = 0.75 * total_pre / static_cast<double>(cus * std::max(1, in.pre_wg_per_cu));
+  const double target_dec = total_dec / static_cast<double>(2 * cus * std::max(1, in.wg_per_cu));
   const int32_t min_blocks = std::max(1, (in.split_min_keys + kBlockN - 1) / kBlockN);
   struct Unit {
     double cost;
@@ -105,7 +111,8 @@ void build_plan(const PlanInput& in, Plan& out) {
     int32_t n = 1;
     if (in.force_splits > 0) {
       n = std::min(in.force_splits, std::max(nblk, 1));
-    } else if (t.cost > target && nblk > min_blocks) {
+    } else if (t.cost > (t.dec ? target_dec : target_pre) && nblk > min_blocks) {
+      const double target = t.dec ? target_dec : target_pre;
       n = static_cast<int32_t>(std::ceil(t.cost / std::max(target, 1e-9)));
       n = std::min(n, nblk / min_blocks);
       n = std::min(n, kMaxSplits);
@@ -213,7 +220,9 @@ void build_plan(const PlanInput& in, Plan& out) {
   static thread_local std::vector<int32_t> fill;
   for (Launch* L : {&out.prefill, &out.decode}) {
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
-    const int32_t nq = static_cast<int32_t>(std::min<int64_t>(slots, nwork));
+    const int64_t lslots = static_cast<int64_t>(std::max(1, in.num_cus)) *
+                           std::max(1, L == &out.prefill ? in.pre_wg_per_cu : in.wg_per_cu);
+    const int32_t nq = static_cast<int32_t>(std::min<int64_t>(lslots, nwork));
     L->grid = nq;
     L->queue_first = static_cast<int32_t>(out.queue_start.size());
     L->work_first = static_cast<int32_t>(out.queue_work.size());

@@ -23,7 +23,8 @@ struct PlanInput {
   const int32_t* cu_kn = nullptr;       // [B + 1] host, or null
   const int32_t* cache_lens = nullptr;  // [B] host, or null
   int32_t num_cus = 256;
-  int32_t wg_per_cu = 2;                // resident attention workgroups per CU
+  int32_t wg_per_cu = 2;                // resident decode-mode workgroups per CU
+  int32_t pre_wg_per_cu = 1;            // resident prefill-mode workgroups per CU
   // knobs
   int32_t force_splits = 0;             // 0: planner decides
   int32_t persistent = -1;              // -1 planner, 0 off, 1 on

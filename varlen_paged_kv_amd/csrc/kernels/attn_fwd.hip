@@ -1,42 +1,46 @@
 // Attention over a paged KV cache for packed variable-length queries, gfx950.
 //
-// One workgroup (4 wavefronts, 256 threads) processes one work item at a time:
-// up to 128 packed query rows of one sequence under one kv head, against the
-// keys [key_begin, key_end) of that sequence.  Rows are (token, query head)
-// pairs packed token-major, so the g query heads that share a kv head
-// (grouped-query attention, vLLM Triton FAv2 PR page, feature list) all use
-// each K/V tile staged in LDS.
+// Rows are (token, query head) pairs packed token-major, so the g query heads
+// that share a kv head (grouped-query attention, vLLM Triton FAv2 PR page,
+// feature list) all use each K/V tile staged in LDS.  A work item is a tile of
+// packed rows of one sequence under one kv head, against the keys
+// [key_begin, key_end) of that sequence.  Two kernels serve the two kinds of
+// items:
 //
-// Per 64-key block (a2..a6):
+// Prefill mode (items of up to 256 rows; 8 wavefronts of 32 rows, one
+// workgroup per CU).  Per 64-key block:
 //   a2  K and V rows of the block are gathered through the item's page ids
 //       (one page table for K and V: TransformerEngine KV-cache PR page,
 //       Description).  bf16 rows go straight from HBM to LDS with
 //       global_load_lds (16 bytes per lane, no registers); fp8 e4m3fn rows go
-//       through registers and are widened to bf16 exactly on the way.  Both K
-//       and V are stored row-major with the 16-byte chunks of each row
-//       XOR-swizzled, and rows past the item's keys are loaded from a zero
-//       region.  The next block is in flight while the current one computes.
+//       through registers and are widened to bf16 exactly on the way.  Tiles
+//       are row-major with the 16-byte chunks of each row XOR-swizzled; rows
+//       past the item's keys are loaded from a zero region.  Blocks rotate
+//       through a four-stage ring, staged up to three blocks ahead.
 //   a3  S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane owns one query
 //       column and 32 of the block's 64 keys, the other 32 sit in lane ^ 32.
 //   a4  keys beyond the item's end, or (causal) beyond token + Lk - Lq, get
-//       -inf; only blocks that cross that bound are masked.
+//       -inf; only blocks that cross the bound of some row of a wave are
+//       masked, and blocks no row of a wave can see are skipped by that wave.
 //   a5  online softmax in base 2 on the raw scores: row max over registers
 //       plus one permlane32 swap, p = 2^(s c - m c) with one fma, running
-//       sum per lane, output rescaled only when some row's max moved.
+//       sum per lane; the reference max only moves when the block max
+//       exceeds it by 2^8 in p, so O is rarely rescaled.
 //   a6  O^T += V^T P^T on the same MFMA; the V^T operand comes from
 //       ds_read_b64_tr_b16 transposed LDS reads of the row-major V tile, P is
 //       rounded to bf16 in registers.
 //   a7  out = O / l (bf16) and lse = m c ln 2 + ln l, or for a split part the
 //       fp32 normalised partial and its lse for the merge pass.
-// Items of at most 32 rows (decode) instead split their keys over the four
-// waves, each with its own 32-key half stage, and merge the four partial
-// states through LDS at the end.
+// Decode mode (items of at most 32 rows: a decode step's q_len * g rows).  The
+// four waves of a 256-thread workgroup split the item's 32-key blocks, each
+// with its own LDS half stage, and merge their partial states through LDS at
+// the end, the same LSE merge the split pass uses.
 //
 // The online softmax and the split of the key range into parts merged by LSE
 // follow the FlashAttention-2 design the pages build on ("Add
 // flash_attn_varlen_func_with_kvcache", Limitation and the discussion of
-// split-KV for decoding); the tiling, the transposed S layout and the LDS
-// layout are this library's own for CDNA4.
+// split-KV for decoding); the tiling, the transposed S layout, the LDS layout
+// and the pipelining are this library's own for CDNA4.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,26 +113,31 @@ __device__ __forceinline__ float wave_pair_sum(float x) {
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// wait until at most n (0..4) vector-memory instructions of this wave are in
+// flight; larger n waits for at most 4
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+  }
+}
+
 // 16-byte global -> LDS copy; `lds` is the wave's destination base, lane l's
 // bytes land at lds + 16 * l.
 __device__ __forceinline__ void dma16(const void* g, uint16_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds), 16, 0, 0);
 }
 
-template <int D, int FMT, bool PAGED, bool DEC>
-struct Kernel {
+// ---------------------------------------------------------------- shared parts
+template <int D, int FMT, bool PAGED>
+struct Src {
   using C = Cfg<D>;
   static constexpr int ESIZE = FMT == kKvFp8 ? 1 : 2;   // bytes per stored element
   static constexpr int RPI = 64 / C::CHUNKS;            // rows per DMA instruction (bf16)
-  // fp8 register path: 16-code chunks per row and per-thread work of a block
-  static constexpr int F8CH = D / 16;
-  static constexpr int F8PASS = kBlockN * F8CH / kThreads;
-  static_assert(FMT != kKvFp8 || F8PASS >= 1, "fp8 load split");
-  static_assert(FMT != kKvFp8 || F8PASS * 64 == 16 * F8CH, "a wave moves 16 fp8 rows per call");
-  // the decode combine area is [4][32][D] fp32 outputs plus [4][32] maxima and
-  // [4][32] sums: the two stages hold the outputs, this tail the rest
-  static constexpr int kCombineExtra = 2 * kWaves * kWaveRows * 2;   // bf16 elements
-  static_assert(kWaves * kWaveRows * D * 4 <= 2 * C::STAGE * 2, "combine area fits the stages");
+  static constexpr int F8CH = D / 16;                   // 16-code chunks of an fp8 row
 
   struct Item {
     const char* kb;      // K base (bytes) at this item's kv head: cache, or the new tokens without a cache
@@ -149,7 +158,7 @@ struct Kernel {
   // Sources of key `key`'s K and V rows for the item's kv head; false when the
   // key is past the item's end (tested only with CHECK) or its page id is
   // unusable.  Token row indices fit 32 bits (the host rejects caches with
-  // 2^32 or more slots), so each address is one 32x32->64-bit multiply-add.
+  // 2^31 or more slots), so each address is one 32x32->64-bit multiply-add.
   template <bool CHECK>
   __device__ static __forceinline__ bool row_src(const AttnParams& p, const Item& it, int key,
                                                  const char*& kp, const char*& vp) {
@@ -187,13 +196,12 @@ struct Kernel {
     }
   }
 
-  // ---- bf16: DMA `nrows` tile rows starting at `row0` (row r holds key
-  //      kbase + r) into the K and V tiles; the calling wave issues nrows / RPI
-  //      copies of each.
-  template <bool CHECK>
-  __device__ static __forceinline__ void dma_rows(const AttnParams& p, const Item& it,
-                                                  uint16_t* ktile, uint16_t* vtile, int kbase,
-                                                  int row0, int nrows, int lane) {
+  // ---- bf16: DMA tile rows [row0, row0 + nrows) (row r holds key kbase + r)
+  //      of K (V_ROWS false) or V into `tile`; the calling wave issues
+  //      nrows / RPI copies.
+  template <bool CHECK, bool V_ROWS>
+  __device__ static __forceinline__ void dma_tile(const AttnParams& p, const Item& it, uint16_t* tile,
+                                                  int kbase, int row0, int nrows, int lane) {
     const char* zeros = static_cast<const char*>(p.zeros);
 #pragma unroll
     for (int i = 0; i < nrows / RPI; ++i) {
@@ -201,183 +209,53 @@ struct Kernel {
       const int c = (lane % C::CHUNKS) ^ C::swz(r);          // global chunk for this LDS slot
       const char *kp, *vp;
       const bool ok = row_src<CHECK>(p, it, kbase + r, kp, vp);
-      dma16(ok ? kp + c * 16 : zeros, ktile + (row0 + i * RPI) * D);
-      dma16(ok ? vp + c * 16 : zeros, vtile + (row0 + i * RPI) * D);
+      dma16(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, tile + (row0 + i * RPI) * D);
     }
   }
 
-  // ---- fp8: rows through registers, widened to bf16 when stored
+  // ---- fp8: rows through registers, widened to bf16 when stored.  `n`
+  //      threads of index `tid` move rows [row0, row0 + nrows) of one tile;
+  //      each thread holds up to NPASS 16-code chunks.
+  template <int NPASS>
   struct F8Regs {
-    u32x4 k[F8PASS];
-    u32x4 v[F8PASS];
+    u32x4 x[NPASS];
   };
 
-  // rows [row0, row0 + nrows) of the tile, `nthreads` threads with index `tid`
-  __device__ static __forceinline__ void f8_load(const AttnParams& p, const Item& it, F8Regs& r,
-                                                 int kbase, int row0, int nrows, int tid,
-                                                 int nthreads) {
+  template <int NPASS, bool V_ROWS>
+  __device__ static __forceinline__ void f8_load(const AttnParams& p, const Item& it, F8Regs<NPASS>& r,
+                                                 int kbase, int row0, int nrows, int tid, int n) {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < F8PASS; ++i) {
-      const int idx = tid + i * nthreads;
+    for (int i = 0; i < NPASS; ++i) {
+      const int idx = tid + i * n;
       const int row = row0 + idx / F8CH;
       const int c = idx % F8CH;
       const char *kp = it.kb, *vp = it.vb;
       const bool ok = row < row0 + nrows && row_src<true>(p, it, kbase + row, kp, vp);
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(ok ? kp + c * 16 : it.kb);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(ok ? vp + c * 16 : it.vb);
-      r.k[i] = ok ? kv : z;
-      r.v[i] = ok ? vv : z;
+      const char* src = V_ROWS ? vp : kp;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ok ? src + c * 16 : (V_ROWS ? it.vb : it.kb));
+      r.x[i] = ok ? x : z;
     }
   }
 
-  __device__ static __forceinline__ void f8_store_one(const u32x4& x, uint16_t* tile, int row, int c) {
-    uint32_t w[8];
+  template <int NPASS>
+  __device__ static __forceinline__ void f8_store(const F8Regs<NPASS>& r, uint16_t* tile, int row0,
+                                                  int nrows, int tid, int n) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) e4m3x4_to_bf16x4(x[q], w[2 * q], w[2 * q + 1]);
-    const u32x4 lo = {w[0], w[1], w[2], w[3]};
-    const u32x4 hi = {w[4], w[5], w[6], w[7]};
-    *reinterpret_cast<u32x4*>(tile + C::at(row, 2 * c)) = lo;
-    *reinterpret_cast<u32x4*>(tile + C::at(row, 2 * c + 1)) = hi;
-  }
-
-  __device__ static __forceinline__ void f8_store(const F8Regs& r, uint16_t* ktile, uint16_t* vtile,
-                                                  int row0, int nrows, int tid, int nthreads) {
-#pragma unroll
-    for (int i = 0; i < F8PASS; ++i) {
-      const int idx = tid + i * nthreads;
+    for (int i = 0; i < NPASS; ++i) {
+      const int idx = tid + i * n;
       const int row = row0 + idx / F8CH;
       const int c = idx % F8CH;
       if (row < row0 + nrows) {
-        f8_store_one(r.k[i], ktile, row, c);
-        f8_store_one(r.v[i], vtile, row, c);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) e4m3x4_to_bf16x4(r.x[i][q], w[2 * q], w[2 * q + 1]);
+        const u32x4 lo = {w[0], w[1], w[2], w[3]};
+        const u32x4 hi = {w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u32x4*>(tile + C::at(row, 2 * c)) = lo;
+        *reinterpret_cast<u32x4*>(tile + C::at(row, 2 * c + 1)) = hi;
       }
     }
-  }
-
-  // ---- a3..a6 for this wave's 32 query rows over keys [kbase, kbase + 32 NH)
-  //      held in tile rows [trow0, trow0 + 32 NH).  MASK: some key of the block
-  //      lies beyond `lim` (the item's end, or the causal bound of the row).
-  template <int NH, bool MASK>
-  __device__ static __forceinline__ void compute(const uint16_t* ktile, const uint16_t* vtile,
-                                                 int trow0, const bf16x8 (&qf)[C::KSTEPS],
-                                                 f32x16 (&o)[C::DBLK], float& m_run, float& l_run,
-                                                 int kbase, int lim, float c, int lr, int lg) {
-    // Operand fragments are read from LDS one round ahead of the MFMAs that
-    // use them (two rounds per phase), so each read's latency hides behind
-    // MFMA or softmax work while the live registers stay within budget.
-    constexpr int KH = C::KSTEPS / 2;                    // k-steps per K round
-    // a3: S^T = K Q^T, NH independent 32-key accumulators interleaved
-    f32x16 acc[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
-    bf16x8 kf[2][NH][KH];
-#pragma unroll
-    for (int s = 0; s < KH; ++s)
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        kf[0][h][s] = *reinterpret_cast<const bf16x8*>(ktile + C::at(trow0 + h * 32 + lr, 2 * s + lg));
-#pragma unroll
-    for (int s = 0; s < KH; ++s)
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        kf[1][h][s] =
-            *reinterpret_cast<const bf16x8*>(ktile + C::at(trow0 + h * 32 + lr, 2 * (s + KH) + lg));
-#pragma unroll
-    for (int rnd = 0; rnd < 2; ++rnd)
-#pragma unroll
-      for (int s = 0; s < KH; ++s)
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[rnd][h][s], qf[rnd * KH + s], acc[h], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // V^T fragments for a6.  Key step j covers tile rows 16j..16j+15; lane
-    // (lr, lg) feeds keys 16j + 4lg + e and 16j + 8 + 4lg + e (e = 0..3) for
-    // head-dim element lr of the output block, which two transposed reads
-    // deliver: in each quarter wave the 16 lanes address 8 bytes (4 head-dim
-    // elements) of 4 consecutive V rows, and lane i receives element i of each
-    // of those 4 rows.
-    const int vrow = lg * 4 + ((lr & 15) >> 2);          // row this lane addresses
-    const int vd = (lr & 16) + 4 * (lr & 3);             // first head-dim element it addresses
-    auto vread = [&](int j, int d) {
-      const int dd = d * 32 + vd;
-      const int r1 = trow0 + j * 16 + vrow;
-      const uint16_t* a1 = vtile + C::at(r1, dd >> 3) + (dd & 4);
-      const uint16_t* a2 = vtile + C::at(r1 + 8, dd >> 3) + (dd & 4);
-      const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
-      const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a2));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int JH = NH;                               // key steps per V round
-    bf16x8 vf[2][JH][C::DBLK];
-#pragma unroll
-    for (int j = 0; j < JH; ++j)
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d) vf[0][j][d] = vread(j, d);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // a4: mask; running max of the raw scores (scale > 0 keeps the order)
-    if constexpr (MASK) {
-      const int rel = lim - kbase - lg * 4;   // last visible key, relative to this lane's first
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (h * 32 + (i >> 2) * 8 + (i & 3) > rel) acc[h][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[h][i]);
-    mx = wave_pair_max(mx);
-
-    // a5: p = 2^(c s - c m), one fma per score.  The reference max m moves
-    // only when the block's max exceeds it by more than 2^kLazyLog2 in p:
-    // until then p stays below 2^kLazyLog2 (fine for fp32 sums and for bf16
-    // P), and O and l need no rescaling.  The result after the final division
-    // by l is the same softmax.
-    const bool grow = mx * c > m_run * c + kLazyLog2;
-    const float m_new = grow ? mx : m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
-    const float neg_mc = m_new == -INFINITY ? 0.f : -m_new * c;
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pf[NH][2];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][i], c, neg_mc));
-        psum += pv;
-        pf[h][i >> 3][i & 7] = static_cast<__bf16>(pv);
-      }
-    l_run = l_run * alpha + psum;
-    if (__any(grow)) {
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // a6: O^T += V^T P^T, second V round read ahead of the first round's MFMAs
-#pragma unroll
-    for (int j = 0; j < JH; ++j)
-#pragma unroll
-      for (int d = 0; d < C::DBLK; ++d) vf[1][j][d] = vread(JH + j, d);
-#pragma unroll
-    for (int rnd = 0; rnd < 2; ++rnd)
-#pragma unroll
-      for (int j = 0; j < JH; ++j)
-#pragma unroll
-        for (int d = 0; d < C::DBLK; ++d) {
-          const int jj = rnd * JH + j;
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[rnd][j][d], pf[jj >> 1][jj & 1], o[d], 0, 0, 0);
-        }
   }
 
   __device__ static __forceinline__ void load_q(const AttnParams& p, const SeqInfo& sq, int kvh,
@@ -414,115 +292,258 @@ struct Kernel {
     }
   }
 
-  // ------------------------------------------------------------- prefill
-  __device__ static void prefill_item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq,
-                                      const Item& it, uint16_t* smem, float c, int wave, int lr,
-                                      int lg, int t) {
-    const int lane = t & 63;
-    const int kbeg = item.key_begin;
-    const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
-    uint16_t* const st0 = smem;
-    uint16_t* const st1 = smem + C::STAGE;
-
-    // stage the first block (each wave copies 16 of the 64 rows)
-    F8Regs fr;
-    if (nblk > 0) {
-      if constexpr (FMT == kKvFp8) {
-        f8_load(p, it, fr, kbeg, 0, kBlockN, t, kThreads);
-      } else {
-        dma_rows<true>(p, it, st0, st0 + C::TILE, kbeg, wave * 16, 16, lane);
-      }
-    }
-
-    const int wrow = wave * kWaveRows + lr;
-    const bool row_ok = wrow < item.nrows;
-    const bool wave_active = wave * kWaveRows < item.nrows;
-    bf16x8 qf[C::KSTEPS];
-    int token, qh;
-    load_q(p, sq, it.kvh, item.row0 + wrow, row_ok, lg, qf, token, qh);
-
-    const int shift = sq.kv_len - sq.q_len;
-    int lim = it.kend - 1;
-    if (p.causal) lim = min(lim, token + shift);
-    int tile_lim = it.kend - 1;
-    if (p.causal) tile_lim = min(tile_lim, item.row0 / p.g + shift);
-
-    f32x16 o[C::DBLK];
-#pragma unroll
-    for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    if (nblk > 0) {
-      if constexpr (FMT == kKvFp8) {
-        f8_store(fr, st0, st0 + C::TILE, 0, kBlockN, t, kThreads);
-        if (nblk > 1) f8_load(p, it, fr, kbeg + kBlockN, 0, kBlockN, t, kThreads);
-      } else {
-        wait_vmem();
-      }
-      __syncthreads();
-    }
-    // one block: stage block n + 1 while block n is computed
-    auto step = [&](int n, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      uint16_t* const cur = (n & 1) ? st1 : st0;
-      uint16_t* const nxt = (n & 1) ? st0 : st1;
-      const int kbase = kbeg + n * kBlockN;
-      if constexpr (FMT != kKvFp8) {
-        if (n + 1 < nblk) {
-          if (kbase + 2 * kBlockN <= it.kend)
-            dma_rows<false>(p, it, nxt, nxt + C::TILE, kbase + kBlockN, wave * 16, 16, lane);
-          else
-            dma_rows<true>(p, it, nxt, nxt + C::TILE, kbase + kBlockN, wave * 16, 16, lane);
+  // Work item `w_idx` of the grid: its item, sequence, kv head and sources;
+  // with a cache, its page ids are staged in `pids` (LDS) by all `nt` threads.
+  __device__ static __forceinline__ void setup_item(const AttnParams& p, int w_idx, int32_t* pids, int t,
+                                                    int nt, WorkItem& item, SeqInfo& sq, Item& it) {
+    // work = unit * hkv + kv head
+    const int work = p.persistent ? p.queue_work[w_idx] : w_idx;
+    const int unit = work / p.hkv;
+    const int kvh = work - unit * p.hkv;
+    item = p.items[unit];
+    if (item.part >= 0) item.part += kvh * item.part_stride;
+    sq = p.seqs[item.seq];
+    it.row_bytes = static_cast<uint32_t>(p.hkv) * (D * ESIZE);
+    it.new_row_bytes = static_cast<uint32_t>(p.hkv) * (D * 2);
+    it.kb = static_cast<const char*>(p.k) + kvh * (D * ESIZE);
+    it.vb = static_cast<const char*>(p.v) + kvh * (D * ESIZE);
+    it.knb = static_cast<const char*>(p.k_new) + kvh * (D * 2);
+    it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
+    it.pids = pids;
+    it.first_page = 0;
+    it.kn_start = sq.kn_start;
+    it.cache_len = sq.cache_len;
+    it.kvh = kvh;
+    it.kend = item.key_end;
+    it.new_direct = p.new_direct != 0;
+    // page ids of the item's key range -> LDS
+    if constexpr (PAGED) {
+      if (item.key_end > item.key_begin) {
+        it.first_page = item.key_begin / p.page_size;
+        const int last_page = (item.key_end - 1) / p.page_size;
+        const int32_t* bt = p.block_table + static_cast<int64_t>(item.seq) * p.max_pages;
+        for (int i = t; i <= last_page - it.first_page; i += nt) {
+          int pg = bt[it.first_page + i];
+          if (pg < 0 || pg >= p.num_pages) {
+            atomicOr(p.err_flag, 1);
+            pg = -1;
+          }
+          pids[i] = pg;
         }
-      }
-      if (wave_active) compute<2, MASK>(cur, cur + C::TILE, 0, qf, o, m_run, l_run, kbase, lim, c, lr, lg);
-      if constexpr (FMT == kKvFp8) {
-        if (n + 1 < nblk) {
-          f8_store(fr, nxt, nxt + C::TILE, 0, kBlockN, t, kThreads);
-          if (n + 2 < nblk) f8_load(p, it, fr, kbase + 2 * kBlockN, 0, kBlockN, t, kThreads);
-        }
-      } else {
-        wait_vmem();
-      }
-      __syncthreads();   // stage `cur` is free, stage `nxt` is complete
-    };
-    // blocks entirely at or below the tile's smallest key bound need no mask
-    const int n_full = min(nblk, max(0, (tile_lim - kbeg + 1) / kBlockN));
-    int n = 0;
-    for (; n < n_full; ++n) step(n, std::false_type{});
-    for (; n < nblk; ++n) step(n, std::true_type{});
-
-    if (wave_active) {
-      const float l_tot = wave_pair_sum(l_run);
-      const bool live = l_tot > 0.f;
-      const float inv = live ? p.v_scale / l_tot : 0.f;
-      const float lse_v = live ? m_run * c * kLn2 + __logf(l_tot) : -INFINITY;
-      if (row_ok) {
-#pragma unroll
-        for (int d = 0; d < C::DBLK; ++d)
-#pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4)
-            store4(p, item, sq, wrow, token, qh, d * 32 + i4 * 8 + lg * 4, o[d][i4 * 4 + 0] * inv,
-                   o[d][i4 * 4 + 1] * inv, o[d][i4 * 4 + 2] * inv, o[d][i4 * 4 + 3] * inv, lse_v,
-                   lg == 0 && d == 0 && i4 == 0);
+        __syncthreads();
       }
     }
   }
 
-  // -------------------------------------------------------------- decode
+  // a4 + a5 on a 32-query x 32 NH-key score block `acc` (S^T layout): mask,
+  // running max with the lazy reference, p = 2^(c s - c m) rounded to bf16
+  // into pf, running sum, and the O rescale when some row's reference moved.
+  template <int NH, bool MASK>
+  __device__ static __forceinline__ void softmax(f32x16 (&acc)[NH], bf16x8 (&pf)[NH][2],
+                                                 f32x16 (&o)[C::DBLK], float& m_run, float& l_run,
+                                                 int kbase, int lim, float c, int lg) {
+    if constexpr (MASK) {
+      const int rel = lim - kbase - lg * 4;   // last visible key, relative to this lane's first
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (h * 32 + (i >> 2) * 8 + (i & 3) > rel) acc[h][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[h][i]);
+    mx = wave_pair_max(mx);
+    // The reference max m moves only when the block's max exceeds it by more
+    // than 2^kLazyLog2 in p: until then p stays below 2^kLazyLog2 (fine for
+    // fp32 sums and for bf16 P), and O and l need no rescaling.  The result
+    // after the final division by l is the same softmax.
+    const bool grow = mx * c > m_run * c + kLazyLog2;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c) : 1.f;
+    const float neg_mc = m_new == -INFINITY ? 0.f : -m_new * c;
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][i], c, neg_mc));
+        psum += pv;
+        pf[h][i >> 3][i & 7] = static_cast<__bf16>(pv);
+      }
+    l_run = l_run * alpha + psum;
+    if (__any(grow)) {
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+    }
+  }
+
+  // V^T operand fragment of key step j (tile rows trow0 + 16j .. + 15) and
+  // output block d.  Lane (lr, lg) feeds keys 16j + 4lg + e and 16j + 8 + 4lg
+  // + e (e = 0..3) for head-dim element lr of block d, which two transposed
+  // reads deliver: in each quarter wave the 16 lanes address 8 bytes (4
+  // head-dim elements) of 4 consecutive V rows, and lane i receives element i
+  // of each of those 4 rows.  This key order matches the P^T operand built
+  // from the S^T accumulator layout.
+  __device__ static __forceinline__ bf16x8 vread(const uint16_t* vtile, int trow0, int j, int d, int lr,
+                                                 int lg) {
+    const int vrow = lg * 4 + ((lr & 15) >> 2);          // row this lane addresses
+    const int vd = (lr & 16) + 4 * (lr & 3);             // first head-dim element it addresses
+    const int dd = d * 32 + vd;
+    const int r1 = trow0 + j * 16 + vrow;
+    const uint16_t* a1 = vtile + C::at(r1, dd >> 3) + (dd & 4);
+    const uint16_t* a2 = vtile + C::at(r1 + 8, dd >> 3) + (dd & 4);
+    const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
+    const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a2));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // K operand fragment: key row r of the tile, head-dim chunk pair k-step s
+  __device__ static __forceinline__ bf16x8 kread(const uint16_t* ktile, int r, int s, int lg) {
+    return *reinterpret_cast<const bf16x8*>(ktile + C::at(r, 2 * s + lg));
+  }
+
+  // ---- a3 alone: S^T of this wave's 32 query rows against tile rows
+  //      [trow0, trow0 + 32 NH) into acc; all K fragments are read first.
+  template <int NH>
+  __device__ static __forceinline__ void qk(const uint16_t* ktile, int trow0, const bf16x8 (&qf)[C::KSTEPS],
+                                            f32x16 (&acc)[NH], int lr, int lg) {
+    constexpr int KH = C::KSTEPS / 2;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+    bf16x8 kf[2][NH][KH];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) kf[rnd][h][s] = kread(ktile, trow0 + h * 32 + lr, rnd * KH + s, lg);
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[rnd][h][s], qf[rnd * KH + s], acc[h], 0, 0, 0);
+  }
+
+  // ---- a6 alone: O^T += V^T P^T over tile rows [trow0, trow0 + 32 NH); the
+  //      second round of V fragments is read while the first round's MFMAs run
+  template <int NH>
+  __device__ static __forceinline__ void pv(const uint16_t* vtile, int trow0, const bf16x8 (&pf)[NH][2],
+                                            f32x16 (&o)[C::DBLK], int lr, int lg) {
+    constexpr int JH = NH;
+    bf16x8 vf[2][JH][C::DBLK];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int j = 0; j < JH; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) vf[rnd][j][d] = vread(vtile, trow0, rnd * JH + j, d, lr, lg);
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int j = 0; j < JH; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const int jj = rnd * JH + j;
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[rnd][j][d], pf[jj >> 1][jj & 1], o[d], 0, 0, 0);
+        }
+  }
+
+  // ---- a3..a6 for this wave's 32 query rows over keys [kbase, kbase + 32 NH)
+  //      held in tile rows [trow0, trow0 + 32 NH).  MASK: some key of the block
+  //      lies beyond `lim` (the item's end, or the causal bound of the row).
+  //      Operand fragments are read from LDS one round ahead of the MFMAs that
+  //      use them (two rounds per phase), so each read's latency hides behind
+  //      MFMA or softmax work while the live registers stay within budget.
+  template <int NH, bool MASK>
+  __device__ static __forceinline__ void compute(const uint16_t* ktile, const uint16_t* vtile,
+                                                 int trow0, const bf16x8 (&qf)[C::KSTEPS],
+                                                 f32x16 (&o)[C::DBLK], float& m_run, float& l_run,
+                                                 int kbase, int lim, float c, int lr, int lg) {
+    constexpr int KH = C::KSTEPS / 2;                    // k-steps per K round
+    // a3: S^T = K Q^T, NH independent 32-key accumulators interleaved
+    f32x16 acc[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+    bf16x8 kf[2][NH][KH];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) kf[rnd][h][s] = kread(ktile, trow0 + h * 32 + lr, rnd * KH + s, lg);
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[rnd][h][s], qf[rnd * KH + s], acc[h], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // first V round, read while the softmax runs
+    constexpr int JH = NH;                               // key steps per V round
+    bf16x8 vf[2][JH][C::DBLK];
+#pragma unroll
+    for (int j = 0; j < JH; ++j)
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d) vf[0][j][d] = vread(vtile, trow0, j, d, lr, lg);
+    __builtin_amdgcn_sched_barrier(0);
+
+    bf16x8 pf[NH][2];
+    softmax<NH, MASK>(acc, pf, o, m_run, l_run, kbase, lim, c, lg);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // a6: O^T += V^T P^T, second V round read ahead of the first round's MFMAs
+#pragma unroll
+    for (int j = 0; j < JH; ++j)
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d) vf[1][j][d] = vread(vtile, trow0, JH + j, d, lr, lg);
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int j = 0; j < JH; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const int jj = rnd * JH + j;
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[rnd][j][d], pf[jj >> 1][jj & 1], o[d], 0, 0, 0);
+        }
+  }
+};
+
+// ------------------------------------------------------------------ decode mode
+template <int D, int FMT, bool PAGED>
+struct Decode : Src<D, FMT, PAGED> {
+  using B = Src<D, FMT, PAGED>;
+  using C = Cfg<D>;
+  using Item = typename B::Item;
+  static constexpr int NT = kThreads;               // 4 waves
+  static constexpr int DK = 32;                     // keys per wave block
+  static constexpr int F8PASS = (DK * B::F8CH + 63) / 64;   // per lane, one wave moving 32 rows
+  // the combine area is [4][32][D] fp32 outputs plus [4][32] maxima and
+  // [4][32] sums: the two stages hold the outputs, this tail the rest
+  static constexpr int kCombineExtra = 2 * kWaves * kWaveRows * 2;   // bf16 elements
+  static_assert(kWaves * kWaveRows * D * 4 <= 2 * C::STAGE * 2, "combine area fits the stages");
+
   // Items with at most 32 packed rows (decode steps: q_len * g rows) would
   // leave three of four waves without rows, so the waves split the keys
   // instead: wave w takes the 32-key blocks w, w + 4, ... of the item, staged
   // in its own half of an LDS stage (no workgroup barrier in the loop), and
   // keeps its own running max / sum / output; the four partial states are
-  // merged through LDS at the end, the same LSE merge the split pass uses.
-  __device__ static void decode_item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq,
-                                     const Item& it, uint16_t* smem, float c, int wave, int lr,
-                                     int lg, int t) {
-    constexpr int DK = 32;
+  // merged through LDS at the end.
+  __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
+                              uint16_t* smem, float c, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nb = it.kend > kbeg ? (it.kend - kbeg + DK - 1) / DK : 0;
@@ -533,7 +554,7 @@ struct Kernel {
     const bool row_ok = lr < item.nrows;
     bf16x8 qf[C::KSTEPS];
     int token, qh;
-    load_q(p, sq, it.kvh, item.row0 + lr, row_ok, lg, qf, token, qh);
+    B::load_q(p, sq, it.kvh, item.row0 + lr, row_ok, lg, qf, token, qh);
     const int shift = sq.kv_len - sq.q_len;
     int lim = it.kend - 1;
     if (p.causal) lim = min(lim, token + shift);
@@ -553,23 +574,23 @@ struct Kernel {
       const int kbase = kbeg + j * DK;
       wait_lds();   // this wave's reads of its previous block are complete
       if constexpr (FMT == kKvFp8) {
-        // one wave moves its 32 rows in two halves of 16 (the per-thread
-        // register set is sized for 64 rows over 256 threads)
-#pragma unroll
-        for (int hr = 0; hr < DK; hr += 16) {
-          F8Regs fr;
-          f8_load(p, it, fr, kbase - trow0, trow0 + hr, 16, lane, 64);
-          f8_store(fr, ktile, vtile, trow0 + hr, 16, lane, 64);
-        }
+        typename B::template F8Regs<F8PASS> fk, fv;
+        B::template f8_load<F8PASS, false>(p, it, fk, kbase - trow0, trow0, DK, lane, 64);
+        B::template f8_load<F8PASS, true>(p, it, fv, kbase - trow0, trow0, DK, lane, 64);
+        B::template f8_store<F8PASS>(fk, ktile, trow0, DK, lane, 64);
+        B::template f8_store<F8PASS>(fv, vtile, trow0, DK, lane, 64);
         wait_lds();
       } else {
-        if (kbase + DK <= it.kend)
-          dma_rows<false>(p, it, ktile, vtile, kbase - trow0, trow0, DK, lane);
-        else
-          dma_rows<true>(p, it, ktile, vtile, kbase - trow0, trow0, DK, lane);
+        if (kbase + DK <= it.kend) {
+          B::template dma_tile<false, false>(p, it, ktile, kbase - trow0, trow0, DK, lane);
+          B::template dma_tile<false, true>(p, it, vtile, kbase - trow0, trow0, DK, lane);
+        } else {
+          B::template dma_tile<true, false>(p, it, ktile, kbase - trow0, trow0, DK, lane);
+          B::template dma_tile<true, true>(p, it, vtile, kbase - trow0, trow0, DK, lane);
+        }
         wait_vmem();
       }
-      compute<1, MASK>(ktile, vtile, trow0, qf, o, m_run, l_run, kbase, lim, c, lr, lg);
+      B::template compute<1, MASK>(ktile, vtile, trow0, qf, o, m_run, l_run, kbase, lim, c, lr, lg);
     };
     // this wave's blocks j = wave, wave + 4, ...: unmasked while at or below
     // the item's smallest key bound
@@ -600,7 +621,7 @@ struct Kernel {
     }
     __syncthreads();
     const int per_row = D / 4;
-    for (int idx = t; idx < item.nrows * per_row; idx += kThreads) {
+    for (int idx = t; idx < item.nrows * per_row; idx += NT) {
       const int r = idx / per_row;
       const int d0 = (idx - r * per_row) * 4;
       float mw[kWaves];
@@ -630,100 +651,284 @@ struct Kernel {
       const int pr = item.row0 + r;
       const int tok = pr / p.g;
       const int h = it.kvh * p.g + (pr - tok * p.g);
-      store4(p, item, sq, r, tok, h, d0, acc4.x * inv, acc4.y * inv, acc4.z * inv, acc4.w * inv,
-             lse_v, d0 == 0);
+      B::store4(p, item, sq, r, tok, h, d0, acc4.x * inv, acc4.y * inv, acc4.z * inv, acc4.w * inv,
+                lse_v, d0 == 0);
     }
   }
 
   __device__ static void run(const AttnParams& p) {
-    // two K/V stages (the block being computed and the block being staged);
-    // decode items use them as four per-wave half stages, then as the area
+    // two K/V stages used as four per-wave half stages, then as the area
     // where the waves combine their partial softmax states
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE + (DEC ? kCombineExtra : 0)];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE + kCombineExtra];
     __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
-
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
     const int lr = lane & 31;   // query column of this lane
     const int lg = lane >> 5;   // lane half
-    const float c = p.qk_scale_log2;
-
     // workgroups past the attention part of the grid store new tokens
     if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
-      append_token(p.app, blockIdx.x - p.attn_blocks, t, kThreads);
+      append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
       return;
     }
-
     int w_idx = blockIdx.x, w_end = blockIdx.x + 1;
     if (p.persistent) {
       w_idx = p.queue_start[blockIdx.x];
       w_end = p.queue_start[blockIdx.x + 1];
     }
-
     for (; w_idx < w_end; ++w_idx) {
-      // work = unit * hkv + kv head
-      const int work = p.persistent ? p.queue_work[w_idx] : w_idx;
-      const int unit = work / p.hkv;
-      const int kvh = work - unit * p.hkv;
-      WorkItem item = p.items[unit];
-      if (item.part >= 0) item.part += kvh * item.part_stride;
-      const SeqInfo sq = p.seqs[item.seq];
+      WorkItem wi;
+      SeqInfo sq;
       Item it;
-      it.row_bytes = static_cast<uint32_t>(p.hkv) * (D * ESIZE);
-      it.new_row_bytes = static_cast<uint32_t>(p.hkv) * (D * 2);
-      it.kb = static_cast<const char*>(p.k) + kvh * (D * ESIZE);
-      it.vb = static_cast<const char*>(p.v) + kvh * (D * ESIZE);
-      it.knb = static_cast<const char*>(p.k_new) + kvh * (D * 2);
-      it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
-      it.pids = pids;
-      it.first_page = 0;
-      it.kn_start = sq.kn_start;
-      it.cache_len = sq.cache_len;
-      it.kvh = kvh;
-      it.kend = item.key_end;
-      it.new_direct = p.new_direct != 0;
-
-      // ---- page ids of the item's key range -> LDS
-      if constexpr (PAGED) {
-        if (item.key_end > item.key_begin) {
-          it.first_page = item.key_begin / p.page_size;
-          const int last_page = (item.key_end - 1) / p.page_size;
-          const int32_t* bt = p.block_table + static_cast<int64_t>(item.seq) * p.max_pages;
-          for (int i = t; i <= last_page - it.first_page; i += kThreads) {
-            int pg = bt[it.first_page + i];
-            if (pg < 0 || pg >= p.num_pages) {
-              atomicOr(p.err_flag, 1);
-              pg = -1;
-            }
-            pids[i] = pg;
-          }
-          __syncthreads();
-        }
-      }
-
-      if constexpr (DEC)
-        decode_item(p, item, sq, it, smem, c, wave, lr, lg, t);
-      else
-        prefill_item(p, item, sq, it, smem, c, wave, lr, lg, t);
+      B::setup_item(p, w_idx, pids, t, NT, wi, sq, it);
+      item(p, wi, sq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
       __syncthreads();   // LDS (stages, page ids, combine area) free for the next item
     }
   }
 };
 
-// One kernel per item mode: prefill-mode items (more than 32 rows) and
-// decode-mode items each get the full register budget of two waves per SIMD.
-template <int D, int FMT, bool PAGED, bool DEC>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const AttnParams p) {
-  Kernel<D, FMT, PAGED, DEC>::run(p);
+// ----------------------------------------------------------------- prefill mode
+template <int D, int FMT, bool PAGED>
+struct Prefill : Src<D, FMT, PAGED> {
+  using B = Src<D, FMT, PAGED>;
+  using C = Cfg<D>;
+  using Item = typename B::Item;
+  static constexpr int NW = kPrefillWaves;
+  static constexpr int NT = NW * 64;
+  static constexpr int NS = 4;                        // ring stages (K and V of one block each)
+  static constexpr int WROWS = kBlockN / NW;          // tile rows each wave stages
+  static constexpr int DMA_PER_TILE = WROWS / B::RPI; // bf16 copies per wave and tile
+  static_assert(WROWS % B::RPI == 0, "whole DMA rows per wave");
+  static_assert(2 * DMA_PER_TILE <= 4, "in-flight copies of one block fit wait_vmem_upto");
+  static constexpr int KSTEPS = C::KSTEPS;
+  static constexpr int DBLK = C::DBLK;
+  static constexpr int F8PASS = (kBlockN * B::F8CH + NT - 1) / NT;
+
+  __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
+                              uint16_t* smem, float c, int wave, int lr, int lg, int t) {
+    const int lane = t & 63;
+    const int kbeg = item.key_begin;
+    const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
+
+    // ---- staging of block j into stage j mod NS: this wave's WROWS rows of K
+    //      and V (bf16), or the block through registers (fp8)
+    auto stage_of = [&](int j) { return smem + (j & (NS - 1)) * C::STAGE; };
+    auto stage_dma = [&](int j) {
+      const int kbase = kbeg + j * kBlockN;
+      uint16_t* const kt = stage_of(j);
+      if (kbase + kBlockN <= it.kend) {
+        B::template dma_tile<false, false>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<false, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
+      } else {
+        B::template dma_tile<true, false>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<true, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
+      }
+    };
+    using F8 = typename B::template F8Regs<F8PASS>;
+    F8 fk, fv;
+    auto f8_load = [&](int j) {
+      B::template f8_load<F8PASS, false>(p, it, fk, kbeg + j * kBlockN, 0, kBlockN, t, NT);
+      B::template f8_load<F8PASS, true>(p, it, fv, kbeg + j * kBlockN, 0, kBlockN, t, NT);
+    };
+    auto f8_store = [&](int j) {
+      B::template f8_store<F8PASS>(fk, stage_of(j), 0, kBlockN, t, NT);
+      B::template f8_store<F8PASS>(fv, stage_of(j) + C::TILE, 0, kBlockN, t, NT);
+    };
+
+    // Q rows first: their loads are older than the staging copies, so the
+    // copy waits below also cover them
+    const int wrow = wave * kWaveRows + lr;
+    const bool row_ok = wrow < item.nrows;
+    bf16x8 qf[KSTEPS];
+    int token, qh;
+    B::load_q(p, sq, it.kvh, item.row0 + wrow, row_ok, lg, qf, token, qh);
+
+    // per-row and per-wave key bounds
+    const int shift = sq.kv_len - sq.q_len;
+    int lim = it.kend - 1;
+    if (p.causal) lim = min(lim, token + shift);
+    const int wr0 = wave * kWaveRows;
+    const int wr1 = min(item.nrows, wr0 + kWaveRows) - 1;          // last valid row of the wave
+    int wlo = it.kend - 1, whi = it.kend - 1;
+    if (p.causal) {
+      wlo = min(wlo, (item.row0 + wr0) / p.g + shift);
+      whi = min(whi, (item.row0 + wr1) / p.g + shift);
+    }
+    // this wave computes blocks [0, nb_w); blocks below n_full need no mask
+    const int nb_w = (wr1 < wr0 || whi < kbeg) ? 0 : min(nblk, (whi - kbeg) / kBlockN + 1);
+    const int n_full = min(nb_w, max(0, (wlo - kbeg + 1) / kBlockN));
+
+    f32x16 o[DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x16 acc[2];
+    bf16x8 pf[2][2];
+
+    // ---- prologue: blocks 0..2 staged, 0 and 1 complete before the first
+    //      barrier (fp8: all three stored)
+    if constexpr (FMT == kKvFp8) {
+      for (int j = 0; j < 3 && j < nblk; ++j) {
+        f8_load(j);
+        f8_store(j);
+      }
+    } else {
+      for (int j = 0; j < 3 && j < nblk; ++j) stage_dma(j);
+      wait_vmem_upto(nblk > 2 ? 2 * DMA_PER_TILE : 0);
+    }
+    if (nblk > 0) __syncthreads();
+
+    // Two wave groups share each SIMD: group A (waves 0-3) and group B (waves
+    // 4-7).  Both pass one barrier per block, at skewed points: after barrier
+    // n, A computes block n (scores, softmax, P V); B finishes block n (P V)
+    // and computes scores and softmax of block n + 1.  One wave of a SIMD
+    // thus runs its softmax while the other issues MFMAs.  Between barriers n
+    // and n + 1 the stages of blocks n and n + 1 are read, and block n + 3 is
+    // staged into the stage block n - 1 left (four stages); it must be
+    // complete at barrier n + 2.
+    const bool group_b = wave >= NW / 2;
+    auto sm = [&](int n, auto mask_tag) {
+      B::template softmax<2, decltype(mask_tag)::value>(acc, pf, o, m_run, l_run, kbeg + n * kBlockN, lim, c,
+                                                         lg);
+    };
+    // interval after barrier n: the caller's first MFMA phase, then start
+    // staging block n + 3 (the copies of all eight waves are then not issued
+    // at the same moment), the rest of the work, then wait for block n + 2
+    // (bf16) or store block n + 3 (fp8)
+    auto interval = [&](int n, auto&& first, auto&& rest) {
+      first();
+      int issued = 0;
+      if constexpr (FMT == kKvFp8) {
+        if (n + 3 < nblk) f8_load(n + 3);
+      } else {
+        if (n + 3 < nblk) {
+          stage_dma(n + 3);
+          issued = 2 * DMA_PER_TILE;
+        }
+      }
+      rest();
+      if constexpr (FMT == kKvFp8) {
+        if (n + 3 < nblk) f8_store(n + 3);
+      } else {
+        wait_vmem_upto(issued);
+      }
+    };
+
+    // (an item without keys skips both: its rows get out = 0, lse = -inf)
+    if (nblk > 0 && !group_b) {
+      auto body = [&](int n, auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;   // 0 unmasked, 1 masked, 2 none
+        __syncthreads();                                    // barrier n
+        uint16_t* const kt = stage_of(n);
+        interval(
+            n,
+            [&] {
+              if constexpr (MODE != 2) B::template qk<2>(kt, 0, qf, acc, lr, lg);
+            },
+            [&] {
+              if constexpr (MODE != 2) {
+                sm(n, std::bool_constant<MODE == 1>{});
+                B::template pv<2>(kt + C::TILE, 0, pf, o, lr, lg);
+              }
+            });
+      };
+      int n = 0;
+      for (; n < n_full; ++n) body(n, std::integral_constant<int, 0>{});
+      for (; n < nb_w; ++n) body(n, std::integral_constant<int, 1>{});
+      for (; n < nblk; ++n) body(n, std::integral_constant<int, 2>{});
+    } else if (nblk > 0) {
+      // scores and softmax of block 0 before barrier 0
+      if (nb_w > 0) {
+        B::template qk<2>(stage_of(0), 0, qf, acc, lr, lg);
+        if (n_full > 0) sm(0, std::false_type{});
+        else sm(0, std::true_type{});
+      }
+      auto body = [&](int n, auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;   // of block n + 1: 0 unmasked, 1 masked, 2 none
+        __syncthreads();                                    // barrier n
+        interval(
+            n,
+            [&] {
+              if (n < nb_w) B::template pv<2>(stage_of(n) + C::TILE, 0, pf, o, lr, lg);
+            },
+            [&] {
+              if constexpr (MODE != 2) {
+                B::template qk<2>(stage_of(n + 1), 0, qf, acc, lr, lg);
+                sm(n + 1, std::bool_constant<MODE == 1>{});
+              }
+            });
+      };
+      int n = 0;
+      for (; n + 1 < n_full; ++n) body(n, std::integral_constant<int, 0>{});
+      for (; n + 1 < nb_w; ++n) body(n, std::integral_constant<int, 1>{});
+      for (; n < nblk; ++n) body(n, std::integral_constant<int, 2>{});
+    }
+
+    if (wr1 >= wr0) {
+      const float l_tot = wave_pair_sum(l_run);
+      const bool live = l_tot > 0.f;
+      const float inv = live ? p.v_scale / l_tot : 0.f;
+      const float lse_v = live ? m_run * c * kLn2 + __logf(l_tot) : -INFINITY;
+      if (row_ok) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            B::store4(p, item, sq, wrow, token, qh, d * 32 + i4 * 8 + lg * 4, o[d][i4 * 4 + 0] * inv,
+                      o[d][i4 * 4 + 1] * inv, o[d][i4 * 4 + 2] * inv, o[d][i4 * 4 + 3] * inv, lse_v,
+                      lg == 0 && d == 0 && i4 == 0);
+      }
+    }
+  }
+
+  __device__ static void run(const AttnParams& p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * C::STAGE];
+    __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int lr = lane & 31;
+    const int lg = lane >> 5;
+    // workgroups past the attention part of the grid store new tokens
+    if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
+      append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
+      return;
+    }
+    int w_idx = blockIdx.x, w_end = blockIdx.x + 1;
+    if (p.persistent) {
+      w_idx = p.queue_start[blockIdx.x];
+      w_end = p.queue_start[blockIdx.x + 1];
+    }
+    for (; w_idx < w_end; ++w_idx) {
+      WorkItem wi;
+      SeqInfo sq;
+      Item it;
+      B::setup_item(p, w_idx, pids, t, NT, wi, sq, it);
+      item(p, wi, sq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+      __syncthreads();   // LDS (ring, page ids) free for the next item
+    }
+  }
+};
+
+template <int D, int FMT, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(const AttnParams p) {
+  Decode<D, FMT, PAGED>::run(p);
+}
+
+template <int D, int FMT, bool PAGED>
+__global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_prefill_kernel(const AttnParams p) {
+  Prefill<D, FMT, PAGED>::run(p);
 }
 
 template <int D, int FMT, bool PAGED>
 int launch_t(const AttnParams& p, int grid, bool decode, hipStream_t s) {
   if (decode)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, FMT, PAGED, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, FMT, PAGED, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_prefill_kernel<D, FMT, PAGED>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -5,14 +5,17 @@
 
 namespace vpk {
 
-// Packed query rows handled by one workgroup: 4 wavefronts x 32 rows.  A row
-// is one (token, query head) pair of a sequence; the g = Hq / Hkv heads that
-// share a kv head are packed token-major (row = token * g + head_in_group), so
-// every K/V tile staged in LDS serves all of them.
-constexpr int kWaves = 4;
+// A row is one (token, query head) pair of a sequence; the g = Hq / Hkv heads
+// that share a kv head are packed token-major (row = token * g +
+// head_in_group), so every K/V tile staged in LDS serves all of them.  Each
+// wavefront owns 32 rows.  Prefill-mode items (more than 32 rows) run on 8
+// wavefronts, 256 rows per item; decode-mode items (at most 32 rows) on 4
+// wavefronts that split the keys.
 constexpr int kWaveRows = 32;
-constexpr int kTileRows = kWaves * kWaveRows;   // 128
+constexpr int kWaves = 4;                       // decode-mode workgroup
 constexpr int kThreads = kWaves * 64;           // 256
+constexpr int kPrefillWaves = 8;                // prefill-mode workgroup
+constexpr int kPrefillRows = kPrefillWaves * kWaveRows;   // 256
 constexpr int kBlockN = 64;                     // keys per inner iteration
 // Page ids of one work item are staged in LDS; an item may span at most this
 // many pages (the planner splits longer key ranges).
