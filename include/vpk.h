@@ -180,7 +180,8 @@ int32_t vpk_abi_version(void);
  * Tuning / test knobs (process-wide).  Names:
  *   "force_splits"     0 = planner decides; n >= 1 = split every work item's
  *                      key range into n parts (tests of the merge pass).
- *   "persistent"       -1 = planner decides, 0 = one work item per workgroup,
+ *   "persistent"       -1 = planner decides (default; persistent grids), 0 = one
+ *                      work item per workgroup,
  *                      1 = persistent grid with static per-workgroup queues.
  *   "split_min_keys"   smallest key range of a split part (default 256).
  *   "num_cus"          compute units assumed by the planner (0 = query device).
@@ -214,10 +215,12 @@ int32_t vpk_device_error(void* stream, int32_t* flags);
  *   {seq, row0, nrows, kv_head, key_begin, key_end, part, queue}
  * where rows are packed (token * g + head-in-group) and part >= 0 marks a
  * split part whose result goes through the merge pass.  Items with more than
- * 32 rows come first (prefill-mode grid), then the others (decode-mode grid);
- * with the persistent schedule, queue numbers run over both grids.  `num_cus` as for the
- * "num_cus" option (> 0 here).  Returns VPK_ERROR_CAPACITY with *n_items set
- * when `capacity` is too small.
+ * 32 rows come first (prefill-mode grid), then the others (decode-mode grid).
+ * Each grid is either persistent (static per-workgroup queues) or runs one
+ * workgroup per item: `queue` is the item's queue, numbered over the
+ * persistent grids in launch order, or -1; *n_queues counts the queues.
+ * `num_cus` as for the "num_cus" option (> 0 here).  Returns
+ * VPK_ERROR_CAPACITY with *n_items set when `capacity` is too small.
  */
 int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host,
                        int32_t has_cache, int32_t has_new, int32_t page_size,

@@ -28,6 +28,7 @@ def _reset_options():
     yield
     vpk.set_option("force_splits", 0)
     vpk.set_option("persistent", -1)
+    vpk.set_option("num_cus", 0)
 
 
 def _run_and_check(wl, label, with_new=True):
@@ -122,6 +123,18 @@ def test_persistent_schedule_is_bitwise_identical():
         torch.cuda.synchronize()
         outs.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_long_persistent_queues(cache):
+    """One CU assumed: every workgroup's queue spans several chunks of entries
+    (the queue metadata is staged through LDS chunk by chunk), with splits."""
+    wl = make_custom(q_lens=[1, 40, 300, 3, 1, 77], new_lens=[1, 40, 300, 3, 1, 77],
+                     cache_lens=[2000, 700, 900, 64, 5000, 0], Hq=8, Hkv=2, D=128, page_size=16,
+                     cache_dtype=cache, seed=17)
+    vpk.set_option("num_cus", 1)
+    vpk.set_option("force_splits", 7)
+    _run_and_check(wl, f"long_queues_{cache}")
 
 
 def test_deterministic_and_idempotent_append():

@@ -41,8 +41,7 @@ def _check_coverage(wl, items, causal, nq=0):
         assert 0 <= seq < wl.B and 0 <= kvh < wl.Hkv
         assert 1 <= nrows <= 256 and 0 <= row0 and row0 + nrows <= ql[seq] * g   # prefill tiles: 256 rows
         assert kb % BLOCK_N == 0 and 0 <= kb and kb <= ke <= kl[seq]
-        if nq:
-            assert 0 <= queue < nq
+        assert queue == -1 or 0 <= queue < nq
         tiles.setdefault((seq, kvh, row0, nrows), []).append((kb, ke, part))
     # rows: for each (seq, kv head) the tiles partition [0, Lq * g)
     for b in range(wl.B):
@@ -81,7 +80,7 @@ def _check_coverage(wl, items, causal, nq=0):
 def test_workload_plans_cover_every_row_once(name):
     wl = make_workload(name, lengths_only=True)
     items, nq = _plan(wl)
-    _check_coverage(wl, items, wl.causal)
+    _check_coverage(wl, items, wl.causal, nq=nq)
 
 
 def test_decode_is_split_to_fill_the_gpu():
@@ -97,8 +96,8 @@ def test_edge_lengths(causal):
     for S in (1, 5, 16):
         wl = make_custom(q_lens=[0, 3, 7, 1, 130], new_lens=[0, 0, 2, 1, 130],
                          cache_lens=[5, 0, 0, 300, 17], Hq=4, Hkv=2, D=64, page_size=S, seed=3, lengths_only=True)
-        items, _ = _plan(wl, causal=causal)
-        _check_coverage(wl, items, causal)
+        items, nq = _plan(wl, causal=causal)
+        _check_coverage(wl, items, causal, nq=nq)
         # the sequence with no keys still gets items (they write zeros / -inf)
         assert any(int(it[0]) == 1 for it in items)
 
@@ -108,8 +107,8 @@ def test_forced_splits(n):
     vpk.set_option("force_splits", n)
     wl = make_custom(q_lens=[1, 40, 3], new_lens=[1, 40, 3], cache_lens=[700, 100, 0], Hq=8, Hkv=2,
                      D=128, page_size=16, seed=4, lengths_only=True)
-    items, _ = _plan(wl)
-    _check_coverage(wl, items, True)
+    items, nq = _plan(wl)
+    _check_coverage(wl, items, True, nq=nq)
     for (seq, kvh, row0, nrows) in {tuple(int(x) for x in it[:4]) for it in items}:
         parts = [it for it in items if tuple(int(x) for x in it[:4]) == (seq, kvh, row0, nrows)]
         nblk = -(-int(max(it[5] for it in parts)) // BLOCK_N)
@@ -119,8 +118,8 @@ def test_forced_splits(n):
 def test_long_ranges_are_split_for_the_page_list():
     # page_size 1: one item may not span more than 1024 pages
     wl = make_custom(q_lens=[1], new_lens=[1], cache_lens=[5000], Hq=2, Hkv=1, D=64, page_size=1, seed=5, lengths_only=True)
-    items, _ = _plan(wl)
-    _check_coverage(wl, items, True)
+    items, nq = _plan(wl)
+    _check_coverage(wl, items, True, nq=nq)
     assert len(items) >= 5
 
 

@@ -521,7 +521,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   const bool new_direct = do_append && !c.fp8;
   const bool run_pre = plan.prefill.grid > 0;
   const bool run_dec = plan.decode.grid > 0;
-  const bool fuse_append = new_direct && !plan.persistent && (run_pre || run_dec);
+  const bool fuse_append = new_direct && (run_pre || run_dec);
   if (do_append && !fuse_append) {
     if ((st = enqueue_append(ap, stream))) return st;
   }
@@ -541,7 +541,6 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     p.part_lse = reinterpret_cast<float*>(PA + L.part_lse);
     p.err_flag = reinterpret_cast<int32_t*>(w->dev);
     p.zeros = w->dev + kZerosOffset;
-    p.persistent = plan.persistent ? 1 : 0;
     p.max_pages = dims->max_pages_per_seq;
     p.num_pages = dims->num_pages;
     p.page_size = c.has_cache ? page_size : 1;
@@ -568,6 +567,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
       q.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
       q.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
       q.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
+      q.persistent = Lc.persistent ? 1 : 0;
       q.num_items = Lc.count;
       q.attn_blocks = Lc.grid;
       const int grid = Lc.grid + (with_append ? dims->total_knew : 0);
@@ -811,7 +811,8 @@ int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host, int32_t
     const int32_t hkv = dims->num_kv_heads;
     const int32_t n = static_cast<int32_t>(plan.items.size()) * hkv;
     if (n_items) *n_items = n;
-    if (n_queues) *n_queues = plan.persistent ? plan.prefill.grid + plan.decode.grid : 0;
+    if (n_queues)
+      *n_queues = (plan.prefill.persistent ? plan.prefill.grid : 0) + (plan.decode.persistent ? plan.decode.grid : 0);
     if (n > capacity) return fail(VPK_ERROR_CAPACITY, "items buffer too small");
     int32_t k = 0;
     int32_t qoff = 0;
@@ -825,8 +826,8 @@ int32_t vpk_plan_debug(const vpk_dims* dims, const vpk_host_index* host, int32_t
         o[6] = it.part < 0 ? -1 : it.part + h * it.part_stride;
         o[7] = queue;
       };
-      if (!plan.persistent) {
-        for (int32_t wk = 0; wk < Lc->count * hkv; ++wk) emit(wk, 0);
+      if (!Lc->persistent) {
+        for (int32_t wk = 0; wk < Lc->count * hkv; ++wk) emit(wk, -1);
       } else {
         for (int32_t q = 0; q < Lc->grid; ++q)
           for (int32_t e = plan.queue_start[Lc->queue_first + q]; e < plan.queue_start[Lc->queue_first + q + 1]; ++e)

@@ -205,27 +205,30 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.decode.first = n_prefill_units;
   out.decode.count = static_cast<int32_t>(out.items.size()) - n_prefill_units;
 
-  const bool persistent = in.persistent == 1;
-  out.persistent = persistent;
-  if (!persistent) {
-    out.prefill.grid = out.prefill.count * in.hkv;
-    out.decode.grid = out.decode.count * in.hkv;
-    return;
-  }
-
-  // ---- persistent: per launch, greedy least-loaded queues over its ordered
-  //      (unit, kv head) work
+  // ---- per launch: one workgroup per (unit, kv head), or (persistent)
+  //      greedy least-loaded queues over its ordered work.  A persistent grid
+  //      reads its queue's metadata once per workgroup instead of once per
+  //      item, which pays off when each workgroup slot gets several items;
+  //      with few items per slot the hardware's dynamic dispatch balances
+  //      better than the static queues.
   static thread_local std::vector<int32_t> owner;
   static thread_local std::vector<int32_t> count;
   static thread_local std::vector<int32_t> fill;
+  out.persistent = false;
   for (Launch* L : {&out.prefill, &out.decode}) {
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
     const int64_t lslots = static_cast<int64_t>(std::max(1, in.num_cus)) *
                            std::max(1, L == &out.prefill ? in.pre_wg_per_cu : in.wg_per_cu);
-    const int32_t nq = static_cast<int32_t>(std::min<int64_t>(lslots, nwork));
-    L->grid = nq;
+    L->persistent = in.persistent == 1 || (in.persistent == -1 && nwork >= 4 * lslots);
     L->queue_first = static_cast<int32_t>(out.queue_start.size());
     L->work_first = static_cast<int32_t>(out.queue_work.size());
+    if (!L->persistent) {
+      L->grid = static_cast<int32_t>(nwork);
+      continue;
+    }
+    out.persistent = true;
+    const int32_t nq = static_cast<int32_t>(std::min<int64_t>(lslots, nwork));
+    L->grid = nq;
     if (nq == 0) continue;
     const size_t q0 = out.queue_start.size();
     out.queue_start.resize(q0 + nq + 1, 0);

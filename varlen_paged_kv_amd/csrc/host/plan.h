@@ -40,6 +40,7 @@ struct Launch {
   int32_t grid = 0;                     // workgroups
   int32_t queue_first = 0;              // persistent: its num_queues + 1 entries of queue_start
   int32_t work_first = 0;               // persistent: its entries of queue_work
+  bool persistent = false;              // static per-workgroup queues
 };
 
 struct Plan {

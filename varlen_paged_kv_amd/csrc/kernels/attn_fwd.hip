@@ -125,10 +125,28 @@ __device__ __forceinline__ void wait_vmem_upto(int n) {
   }
 }
 
-// 16-byte global -> LDS copy; `lds` is the wave's destination base, lane l's
-// bytes land at lds + 16 * l.
+// 16-byte global -> LDS copy; `lds` is the wave's destination base (uniform),
+// lane l's bytes land at lds + 16 * l.  ASYNC: issued as inline assembly, so
+// the compiler does not treat the copy as an LDS store that every later LDS
+// read must wait for (it would wait for all copies in flight, including the
+// ones staged blocks ahead); completion is then ordered only by the explicit
+// vmcnt waits and barriers of the caller.  Loads complete in issue order, so
+// the compiler's own vmcnt waits for its loads stay correct with these in the
+// queue.  M0 holds the LDS base; one wait state separates its write from the
+// copy.  Without ASYNC the compiler's builtin is used and orders the copy
+// itself.
+template <bool ASYNC>
 __device__ __forceinline__ void dma16(const void* g, uint16_t* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds), 16, 0, 0);
+  if constexpr (!ASYNC) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds), 16, 0, 0);
+    return;
+  }
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(base)
+               : "memory", "m0");
 }
 
 // ---------------------------------------------------------------- shared parts
@@ -199,7 +217,7 @@ struct Src {
   // ---- bf16: DMA tile rows [row0, row0 + nrows) (row r holds key kbase + r)
   //      of K (V_ROWS false) or V into `tile`; the calling wave issues
   //      nrows / RPI copies.
-  template <bool CHECK, bool V_ROWS>
+  template <bool CHECK, bool V_ROWS, bool ASYNC = false>
   __device__ static __forceinline__ void dma_tile(const AttnParams& p, const Item& it, uint16_t* tile,
                                                   int kbase, int row0, int nrows, int lane) {
     const char* zeros = static_cast<const char*>(p.zeros);
@@ -209,7 +227,7 @@ struct Src {
       const int c = (lane % C::CHUNKS) ^ C::swz(r);          // global chunk for this LDS slot
       const char *kp, *vp;
       const bool ok = row_src<CHECK>(p, it, kbase + r, kp, vp);
-      dma16(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, tile + (row0 + i * RPI) * D);
+      dma16<ASYNC>(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, tile + (row0 + i * RPI) * D);
     }
   }
 
@@ -292,17 +310,39 @@ struct Src {
     }
   }
 
-  // Work item `w_idx` of the grid: its item, sequence, kv head and sources;
-  // with a cache, its page ids are staged in `pids` (LDS) by all `nt` threads.
-  __device__ static __forceinline__ void setup_item(const AttnParams& p, int w_idx, int32_t* pids, int t,
-                                                    int nt, WorkItem& item, SeqInfo& sq, Item& it) {
-    // work = unit * hkv + kv head
-    const int work = p.persistent ? p.queue_work[w_idx] : w_idx;
-    const int unit = work / p.hkv;
-    const int kvh = work - unit * p.hkv;
-    item = p.items[unit];
-    if (item.part >= 0) item.part += kvh * item.part_stride;
-    sq = p.seqs[item.seq];
+  // Work-queue entries of a workgroup, read from the plan once per chunk of
+  // the queue into LDS (the plan lives in pinned host memory, so each read
+  // crosses PCIe: one round trip per chunk instead of one per item).
+  struct QEntry {
+    WorkItem item;
+    SeqInfo seq;
+    int32_t kvh;
+    int32_t pad[3];
+  };
+  static constexpr int kQueueChunk = 48;
+
+  // Entries [w0, w0 + n) of the grid's work list (the workgroup's queue when
+  // persistent) -> q[0, n), by `nt` threads; the caller synchronises.
+  __device__ static __forceinline__ void load_queue(const AttnParams& p, int w0, int n, QEntry* q, int t,
+                                                    int nt) {
+    for (int i = t; i < n; i += nt) {
+      // work = unit * hkv + kv head
+      const int work = p.persistent ? p.queue_work[w0 + i] : w0 + i;
+      const int unit = work / p.hkv;
+      const int kvh = work - unit * p.hkv;
+      WorkItem item = p.items[unit];
+      if (item.part >= 0) item.part += kvh * item.part_stride;
+      q[i].item = item;
+      q[i].seq = p.seqs[item.seq];
+      q[i].kvh = kvh;
+    }
+  }
+
+  // Sources of an entry's keys and values; with a cache, its page ids are
+  // staged in `pids` (LDS) by all `nt` threads.
+  __device__ static __forceinline__ void setup_item(const AttnParams& p, const QEntry& e, int32_t* pids, int t,
+                                                    int nt, Item& it) {
+    const int kvh = e.kvh;
     it.row_bytes = static_cast<uint32_t>(p.hkv) * (D * ESIZE);
     it.new_row_bytes = static_cast<uint32_t>(p.hkv) * (D * 2);
     it.kb = static_cast<const char*>(p.k) + kvh * (D * ESIZE);
@@ -311,17 +351,17 @@ struct Src {
     it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
     it.pids = pids;
     it.first_page = 0;
-    it.kn_start = sq.kn_start;
-    it.cache_len = sq.cache_len;
+    it.kn_start = e.seq.kn_start;
+    it.cache_len = e.seq.cache_len;
     it.kvh = kvh;
-    it.kend = item.key_end;
+    it.kend = e.item.key_end;
     it.new_direct = p.new_direct != 0;
     // page ids of the item's key range -> LDS
     if constexpr (PAGED) {
-      if (item.key_end > item.key_begin) {
-        it.first_page = item.key_begin / p.page_size;
-        const int last_page = (item.key_end - 1) / p.page_size;
-        const int32_t* bt = p.block_table + static_cast<int64_t>(item.seq) * p.max_pages;
+      if (e.item.key_end > e.item.key_begin) {
+        it.first_page = e.item.key_begin / p.page_size;
+        const int last_page = (e.item.key_end - 1) / p.page_size;
+        const int32_t* bt = p.block_table + static_cast<int64_t>(e.item.seq) * p.max_pages;
         for (int i = t; i <= last_page - it.first_page; i += nt) {
           int pg = bt[it.first_page + i];
           if (pg < 0 || pg >= p.num_pages) {
@@ -331,6 +371,30 @@ struct Src {
           pids[i] = pg;
         }
         __syncthreads();
+      }
+    }
+  }
+
+  // The workgroup's items: [blockIdx, blockIdx + 1) of the grid, or its queue
+  // when persistent; `body(entry, item)` runs each, all threads together.
+  template <typename Body>
+  __device__ static __forceinline__ void for_each_item(const AttnParams& p, QEntry* qbuf, int32_t* pids, int t,
+                                                       int nt, Body&& body) {
+    int w0 = blockIdx.x, w_end = blockIdx.x + 1;
+    if (p.persistent) {
+      w0 = p.queue_start[blockIdx.x];
+      w_end = p.queue_start[blockIdx.x + 1];
+    }
+    for (; w0 < w_end; w0 += kQueueChunk) {
+      const int n = min(kQueueChunk, w_end - w0);
+      load_queue(p, w0, n, qbuf, t, nt);
+      __syncthreads();
+      for (int k = 0; k < n; ++k) {
+        const QEntry& e = qbuf[k];
+        Item it;
+        setup_item(p, e, pids, t, nt, it);
+        body(e, it);
+        __syncthreads();   // LDS (stages, page ids) free for the next item
       }
     }
   }
@@ -671,19 +735,10 @@ struct Decode : Src<D, FMT, PAGED> {
       append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
       return;
     }
-    int w_idx = blockIdx.x, w_end = blockIdx.x + 1;
-    if (p.persistent) {
-      w_idx = p.queue_start[blockIdx.x];
-      w_end = p.queue_start[blockIdx.x + 1];
-    }
-    for (; w_idx < w_end; ++w_idx) {
-      WorkItem wi;
-      SeqInfo sq;
-      Item it;
-      B::setup_item(p, w_idx, pids, t, NT, wi, sq, it);
-      item(p, wi, sq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
-      __syncthreads();   // LDS (stages, page ids, combine area) free for the next item
-    }
+    __shared__ typename B::QEntry qbuf[B::kQueueChunk];
+    B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      item(p, e.item, e.seq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+    });
   }
 };
 
@@ -717,11 +772,11 @@ struct Prefill : Src<D, FMT, PAGED> {
       const int kbase = kbeg + j * kBlockN;
       uint16_t* const kt = stage_of(j);
       if (kbase + kBlockN <= it.kend) {
-        B::template dma_tile<false, false>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
-        B::template dma_tile<false, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<false, false, true>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<false, true, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
       } else {
-        B::template dma_tile<true, false>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
-        B::template dma_tile<true, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<true, false, true>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
+        B::template dma_tile<true, true, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
       }
     };
     using F8 = typename B::template F8Regs<F8PASS>;
@@ -779,6 +834,11 @@ struct Prefill : Src<D, FMT, PAGED> {
       for (int j = 0; j < 3 && j < nblk; ++j) stage_dma(j);
       wait_vmem_upto(nblk > 2 ? 2 * DMA_PER_TILE : 0);
     }
+    // Q is complete here (its loads are older than the copies just waited
+    // for); an empty use tells the compiler so, which keeps it from placing a
+    // wait for all vector memory, in-flight copies included, inside the loop
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : : "v"(qf[s]));
     if (nblk > 0) __syncthreads();
 
     // Two wave groups share each SIMD: group A (waves 0-3) and group B (waves
@@ -897,19 +957,10 @@ struct Prefill : Src<D, FMT, PAGED> {
       append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
       return;
     }
-    int w_idx = blockIdx.x, w_end = blockIdx.x + 1;
-    if (p.persistent) {
-      w_idx = p.queue_start[blockIdx.x];
-      w_end = p.queue_start[blockIdx.x + 1];
-    }
-    for (; w_idx < w_end; ++w_idx) {
-      WorkItem wi;
-      SeqInfo sq;
-      Item it;
-      B::setup_item(p, w_idx, pids, t, NT, wi, sq, it);
-      item(p, wi, sq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
-      __syncthreads();   // LDS (ring, page ids) free for the next item
-    }
+    __shared__ typename B::QEntry qbuf[B::kQueueChunk];
+    B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      item(p, e.item, e.seq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+    });
   }
 };
 
