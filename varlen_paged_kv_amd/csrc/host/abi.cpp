@@ -534,7 +534,6 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     p.v_new = v_new;
     p.new_direct = new_direct ? 1 : 0;
     p.block_table = block_table;
-    p.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     p.part_o = reinterpret_cast<float*>(PA + L.part_o);
@@ -598,7 +597,6 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     // the partials visible across the device without per-part fences)
     MergeParams mp{};
     mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
-    mp.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
     mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
     mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
     mp.out = static_cast<uint16_t*>(out);

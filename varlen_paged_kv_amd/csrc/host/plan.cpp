@@ -148,7 +148,7 @@ void build_plan(const PlanInput& in, Plan& out) {
       for (int32_t h = 0; h < in.hkv; ++h) {
         out.groups.push_back(MergeGroup{t.seq, t.row0, t.nrows, h,
                                         static_cast<int32_t>(out.part_rows + static_cast<int64_t>(h) * u.nsplit * t.nrows),
-                                        u.nsplit, 0, 0});
+                                        u.nsplit, 0, 0, out.seqs[t.seq]});
       }
       group_base[gi++] = out.part_rows;
       out.part_rows += static_cast<int64_t>(in.hkv) * u.nsplit * t.nrows;
@@ -198,7 +198,7 @@ void build_plan(const PlanInput& in, Plan& out) {
       part = static_cast<int32_t>(group_base[u.group] + static_cast<int64_t>(u.part) * t.nrows);
       stride = u.nsplit * t.nrows;
     }
-    out.items.push_back(WorkItem{t.seq, t.row0, t.nrows, stride, kb, ke, part, 0});
+    out.items.push_back(WorkItem{t.seq, t.row0, t.nrows, stride, kb, ke, part, 0, out.seqs[t.seq]});
   }
   out.prefill.first = 0;
   out.prefill.count = n_prefill_units;

@@ -314,8 +314,7 @@ struct Src {
   // the queue into LDS (the plan lives in pinned host memory, so each read
   // crosses PCIe: one round trip per chunk instead of one per item).
   struct QEntry {
-    WorkItem item;
-    SeqInfo seq;
+    WorkItem item;       // with its sequence's facts in item.s
     int32_t kvh;
     int32_t pad[3];
   };
@@ -333,7 +332,6 @@ struct Src {
       WorkItem item = p.items[unit];
       if (item.part >= 0) item.part += kvh * item.part_stride;
       q[i].item = item;
-      q[i].seq = p.seqs[item.seq];
       q[i].kvh = kvh;
     }
   }
@@ -351,8 +349,8 @@ struct Src {
     it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
     it.pids = pids;
     it.first_page = 0;
-    it.kn_start = e.seq.kn_start;
-    it.cache_len = e.seq.cache_len;
+    it.kn_start = e.item.s.kn_start;
+    it.cache_len = e.item.s.cache_len;
     it.kvh = kvh;
     it.kend = e.item.key_end;
     it.new_direct = p.new_direct != 0;
@@ -737,7 +735,7 @@ struct Decode : Src<D, FMT, PAGED> {
     }
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
-      item(p, e.item, e.seq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+      item(p, e.item, e.item.s, it, smem, p.qk_scale_log2, wave, lr, lg, t);
     });
   }
 };
@@ -959,7 +957,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     }
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
-      item(p, e.item, e.seq, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+      item(p, e.item, e.item.s, it, smem, p.qk_scale_log2, wave, lr, lg, t);
     });
   }
 };

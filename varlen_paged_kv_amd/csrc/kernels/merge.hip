@@ -25,7 +25,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const MergeGroup gr = p.groups[blockIdx.x];
-  const SeqInfo sq = p.seqs[gr.seq];
+  const SeqInfo sq = gr.s;
   const int D = p.head_dim;
   const int per_row = D / 4;
   const int total = gr.nrows * per_row;

@@ -32,9 +32,11 @@ struct SeqInfo {
   int32_t pad0, pad1;
 };
 
-// One unit of attention work (32 bytes): packed rows [row0, row0 + nrows) of
+// One unit of attention work (64 bytes): packed rows [row0, row0 + nrows) of
 // sequence `seq` against keys [key_begin, key_end), for every kv head; the
-// grid index (or the persistent queue entry) picks the head.
+// grid index (or the persistent queue entry) picks the head.  The sequence's
+// facts travel with the item, so a workgroup learns everything about its
+// work in one read of the plan.
 struct WorkItem {
   int32_t seq;
   int32_t row0;
@@ -44,9 +46,10 @@ struct WorkItem {
   int32_t key_end;
   int32_t part;        // -1: write out/lse; >= 0: first partial row of kv head 0
   int32_t pad;
+  SeqInfo s;           // copy of the sequence's SeqInfo
 };
 
-// A tile whose key range was split (32 bytes): parts s = 0..nsplit-1 wrote
+// A tile whose key range was split (64 bytes): parts s = 0..nsplit-1 wrote
 // partial rows part + s * nrows + r.
 struct MergeGroup {
   int32_t seq;
@@ -56,6 +59,7 @@ struct MergeGroup {
   int32_t part;
   int32_t nsplit;
   int32_t pad0, pad1;
+  SeqInfo s;           // copy of the sequence's SeqInfo
 };
 
 enum KvFormat : int32_t { kKvBf16 = 0, kKvFp8 = 1 };
@@ -85,7 +89,6 @@ struct AttnParams {
   const void* k;              // cache [P, S, Hkv, D] or k_new [Tn, Hkv, D]
   const void* v;
   const int32_t* block_table; // [B, max_pages] (paged only)
-  const SeqInfo* seqs;
   const WorkItem* items;      // this grid's units
   const int32_t* queue_start; // persistent: [num_queues + 1] offsets into queue_work
   const int32_t* queue_work;  // persistent: unit * hkv + kv_head, grouped by queue
@@ -121,7 +124,6 @@ struct AttnParams {
 
 struct MergeParams {
   const MergeGroup* groups;
-  const SeqInfo* seqs;
   const float* part_o;
   const float* part_lse;
   uint16_t* out;
