@@ -43,6 +43,11 @@ double block_cost(int32_t nrows, int32_t kv_bytes, bool decode_mode) {
   return load + 1.0 * waves;
 }
 
+// Fixed cost of one work item (its metadata, page ids, Q rows, the final
+// combine and stores), in the units of block_cost: about 1.6 blocks of a
+// decode-mode item, measured on MI355X.
+constexpr double kItemCost = 1.6;
+
 }  // namespace
 
 void build_plan(const PlanInput& in, Plan& out) {
@@ -82,22 +87,58 @@ void build_plan(const PlanInput& in, Plan& out) {
       if (in.causal) kend = std::min<int64_t>(kend, static_cast<int64_t>(t_last) + s.kv_len - s.q_len + 1);
       kend = std::max<int64_t>(kend, 0);
       const int32_t nblk = static_cast<int32_t>((kend + kBlockN - 1) / kBlockN);
-      const double c = 0.05 + nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
+      const double c = kItemCost + nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
       tiles.push_back(Tile{b, static_cast<int32_t>(r0), nr, 0, static_cast<int32_t>(kend), c, rows <= kWaveRows});
       (rows <= kWaveRows ? total_dec : total_pre) += c * in.hkv;
     }
   }
 
-  // ---- split decision per tile -> units (tile, part).  Longest-first
-  //      dealing ends a grid evenly when no tile is much above the average
-  //      load of a workgroup slot; a tile above that (3/4 of the average for
-  //      the MFMA-bound prefill-mode grid, whose partials cost a merge over
-  //      up to 256 rows, 1/2 for the decode-mode grid, whose sequences are
-  //      few and long) is split into parts near that size.
+  // ---- split decision per tile -> units (tile, part).
+  //      Prefill-mode grid (MFMA-bound, many items): longest-first dealing
+  //      ends the grid evenly when no tile is much above the average load of
+  //      a workgroup slot; a tile above 3/4 of that average (its partials cost
+  //      a merge over up to 256 rows) is split into parts near that size.
+  //      Decode-mode grid (HBM-bound, few long sequences): every item of a
+  //      dispatch round takes about as long, so the grid lasts about
+  //      ceil(items / slots) rounds of (work per item + fixed cost per item);
+  //      tiles are cut into parts of a common size chosen so that the item
+  //      count fills whole rounds of the slots.
   const int64_t cus = std::max(1, in.num_cus);
   const double target_pre = 0.75 * total_pre / static_cast<double>(cus * std::max(1, in.pre_wg_per_cu));
-  const double target_dec = total_dec / static_cast<double>(2 * cus * std::max(1, in.wg_per_cu));
   const int32_t min_blocks = std::max(1, (in.split_min_keys + kBlockN - 1) / kBlockN);
+  auto split_limit = [&](const Tile& t) {
+    const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;
+    return std::max(1, std::min(nblk / min_blocks, kMaxSplits));
+  };
+  double part_dec = 0.0;   // decode-mode part size (cost units), 0: no split
+  bool ceil_dec = false;   // split only tiles above part_dec, into ceil(cost / part_dec) parts
+  if (total_dec > 0.0 && total_pre > 0.0) {
+    // both grids share the device, so the decode grid has no fixed number of
+    // slots: parts of half the average load of a decode slot
+    part_dec = total_dec / static_cast<double>(2 * cus * std::max(1, in.wg_per_cu));
+    ceil_dec = true;
+  } else if (total_dec > 0.0) {
+    const int64_t slots_dec = cus * std::max(1, in.wg_per_cu);
+    const double work = total_dec - kItemCost * static_cast<double>(in.hkv) *
+                                        std::count_if(tiles.begin(), tiles.end(), [](const Tile& t) { return t.dec; });
+    double best = 0.0;
+    for (int32_t m = 1; m <= 8; ++m) {
+      const double w = work / static_cast<double>(m * slots_dec);
+      if (w <= 0.0) break;
+      int64_t n = 0;
+      for (const Tile& t : tiles) {
+        if (!t.dec) continue;
+        const double parts = std::round((t.cost - kItemCost) / w);
+        n += std::min<int64_t>(std::max<int64_t>(1, static_cast<int64_t>(parts)), split_limit(t)) * in.hkv;
+      }
+      const double rounds = std::ceil(static_cast<double>(n) / static_cast<double>(slots_dec));
+      const double est = rounds * (work / static_cast<double>(n) + kItemCost);
+      if (m == 1 || est < best) {
+        best = est;
+        part_dec = w;
+      }
+    }
+  }
   struct Unit {
     double cost;
     int32_t tile, part, b0, b1, nsplit, group;
@@ -111,12 +152,17 @@ void build_plan(const PlanInput& in, Plan& out) {
     int32_t n = 1;
     if (in.force_splits > 0) {
       n = std::min(in.force_splits, std::max(nblk, 1));
-    } else if (t.cost > (t.dec ? target_dec : target_pre) && nblk > min_blocks) {
-      const double target = t.dec ? target_dec : target_pre;
-      n = static_cast<int32_t>(std::ceil(t.cost / std::max(target, 1e-9)));
-      n = std::min(n, nblk / min_blocks);
-      n = std::min(n, kMaxSplits);
-      n = std::max(n, 1);
+    } else if (t.dec) {
+      if (ceil_dec) {
+        if (t.cost > part_dec && nblk > min_blocks)
+          n = std::min(static_cast<int32_t>(std::ceil(t.cost / part_dec)), split_limit(t));
+      } else if (part_dec > 0.0) {
+        const double parts = std::round((t.cost - kItemCost) / part_dec);
+        n = static_cast<int32_t>(std::min<double>(std::max(1.0, parts), split_limit(t)));
+      }
+    } else if (t.cost > target_pre && nblk > min_blocks) {
+      n = static_cast<int32_t>(std::ceil(t.cost / std::max(target_pre, 1e-9)));
+      n = std::min(n, split_limit(t));
     }
     // every part must fit the LDS page-id list
     if (in.has_cache && nblk > 0) {
@@ -132,7 +178,7 @@ void build_plan(const PlanInput& in, Plan& out) {
     for (int32_t s = 0; s < n; ++s) {
       const int32_t b0 = static_cast<int32_t>(static_cast<int64_t>(nblk) * s / n);
       const int32_t b1 = static_cast<int32_t>(static_cast<int64_t>(nblk) * (s + 1) / n);
-      units.push_back(Unit{0.05 + (b1 - b0) * block_cost(t.nrows, in.kv_bytes, t.dec), ti, s, b0, b1, n, ngroups});
+      units.push_back(Unit{kItemCost + (b1 - b0) * block_cost(t.nrows, in.kv_bytes, t.dec), ti, s, b0, b1, n, ngroups});
     }
     ++ngroups;
   }
