@@ -125,6 +125,15 @@ __device__ __forceinline__ void wait_vmem_upto(int n) {
   }
 }
 
+// a ^ b computed where it is used: the compiler cannot hoist it out of a
+// loop (hoisted lane-dependent addresses would not fit the register budget,
+// and their spill reloads would wait for all vector memory)
+__device__ __forceinline__ int xor_here(int a, int b) {
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // 16-byte global -> LDS copy; `lds` is the wave's destination base (uniform),
 // lane l's bytes land at lds + 16 * l.  ASYNC: issued as inline assembly, so
 // the compiler does not treat the copy as an LDS store that every later LDS
@@ -520,6 +529,86 @@ struct Src {
         }
   }
 
+  // ---- a3 and a6 as above for tile rows from 0, with the LDS addresses
+  //      formed where they are used.  The swizzle only XORs the chunk index,
+  //      so the address of k-step s is the k-step 0 address XOR 32 s bytes,
+  //      and that of V output block d the block 0 address XOR 64 d bytes;
+  //      rows 32 (K) or 16 (V) further on are plain immediate offsets.  The
+  //      XORs run next to their reads, so no per-step address stays live
+  //      across the key loop.
+  __device__ static __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+  }
+  template <typename T>
+  __device__ static __forceinline__ T lds_read(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>(static_cast<uintptr_t>(a));
+  }
+  template <int NH>
+  __device__ static __forceinline__ void qk0(const uint16_t* ktile, const bf16x8 (&qf)[C::KSTEPS],
+                                             f32x16 (&acc)[NH], int lr, int lg) {
+    constexpr int KH = C::KSTEPS / 2;
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+    const uint32_t a0 = lds_addr(ktile + C::at(lr, lg));
+    bf16x8 kf[2][NH][KH];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s) {
+        const int ks = rnd * KH + s;
+        const uint32_t a = ks ? static_cast<uint32_t>(xor_here(static_cast<int>(a0), 32 * ks)) : a0;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) kf[rnd][h][s] = lds_read<bf16x8>(a + h * 32 * D * 2);
+      }
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[rnd][h][s], qf[rnd * KH + s], acc[h], 0, 0, 0);
+  }
+  template <int NH>
+  __device__ static __forceinline__ void pv0(const uint16_t* vtile, const bf16x8 (&pf)[NH][2],
+                                             f32x16 (&o)[C::DBLK], int lr, int lg) {
+    constexpr int JH = NH;
+    const int vrow = lg * 4 + ((lr & 15) >> 2);
+    const int vd = (lr & 16) + 4 * (lr & 3);
+    const uint32_t b1 = lds_addr(vtile + C::at(vrow, vd >> 3) + (vd & 4));
+    const uint32_t b2 = lds_addr(vtile + C::at(vrow + 8, vd >> 3) + (vd & 4));
+    uint32_t a1[C::DBLK], a2[C::DBLK];
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d) {
+      a1[d] = d ? static_cast<uint32_t>(xor_here(static_cast<int>(b1), 64 * d)) : b1;
+      a2[d] = d ? static_cast<uint32_t>(xor_here(static_cast<int>(b2), 64 * d)) : b2;
+    }
+    bf16x8 vf[2][JH][C::DBLK];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int j = 0; j < JH; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const uint32_t off = (rnd * JH + j) * 16 * D * 2;
+          const i16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<lds_i16x4*>(static_cast<uintptr_t>(a1[d] + off)));
+          const i16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<lds_i16x4*>(static_cast<uintptr_t>(a2[d] + off)));
+          vf[rnd][j][d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x1, x2, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int j = 0; j < JH; ++j)
+#pragma unroll
+        for (int d = 0; d < C::DBLK; ++d) {
+          const int jj = rnd * JH + j;
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[rnd][j][d], pf[jj >> 1][jj & 1], o[d], 0, 0, 0);
+        }
+  }
+
   // ---- a3..a6 for this wave's 32 query rows over keys [kbase, kbase + 32 NH)
   //      held in tile rows [trow0, trow0 + 32 NH).  MASK: some key of the block
   //      lies beyond `lim` (the item's end, or the causal bound of the row).
@@ -843,7 +932,9 @@ struct Prefill : Src<D, FMT, PAGED> {
     // 4-7).  Both pass one barrier per block, at skewed points: after barrier
     // n, A computes block n (scores, softmax, P V); B finishes block n (P V)
     // and computes scores and softmax of block n + 1.  One wave of a SIMD
-    // thus runs its softmax while the other issues MFMAs.  Between barriers n
+    // thus runs its softmax while the other issues MFMAs; MFMA phases run at
+    // raised wave priority, so the pipe is fed first whenever the MFMA wave
+    // is ready and the softmax takes the remaining issue slots.  Between barriers n
     // and n + 1 the stages of blocks n and n + 1 are read, and block n + 3 is
     // staged into the stage block n - 1 left (four stages); it must be
     // complete at barrier n + 2.
@@ -884,12 +975,15 @@ struct Prefill : Src<D, FMT, PAGED> {
         interval(
             n,
             [&] {
-              if constexpr (MODE != 2) B::template qk<2>(kt, 0, qf, acc, lr, lg);
+              __builtin_amdgcn_s_setprio(1);
+              if constexpr (MODE != 2) B::template qk0<2>(kt, qf, acc, lr, lg);
             },
             [&] {
               if constexpr (MODE != 2) {
+                __builtin_amdgcn_s_setprio(0);
                 sm(n, std::bool_constant<MODE == 1>{});
-                B::template pv<2>(kt + C::TILE, 0, pf, o, lr, lg);
+                __builtin_amdgcn_s_setprio(1);
+                B::template pv0<2>(kt + C::TILE, pf, o, lr, lg);
               }
             });
       };
@@ -900,7 +994,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     } else if (nblk > 0) {
       // scores and softmax of block 0 before barrier 0
       if (nb_w > 0) {
-        B::template qk<2>(stage_of(0), 0, qf, acc, lr, lg);
+        B::template qk0<2>(stage_of(0), qf, acc, lr, lg);
         if (n_full > 0) sm(0, std::false_type{});
         else sm(0, std::true_type{});
       }
@@ -910,11 +1004,13 @@ struct Prefill : Src<D, FMT, PAGED> {
         interval(
             n,
             [&] {
-              if (n < nb_w) B::template pv<2>(stage_of(n) + C::TILE, 0, pf, o, lr, lg);
+              __builtin_amdgcn_s_setprio(1);
+              if (n < nb_w) B::template pv0<2>(stage_of(n) + C::TILE, pf, o, lr, lg);
             },
             [&] {
               if constexpr (MODE != 2) {
-                B::template qk<2>(stage_of(n + 1), 0, qf, acc, lr, lg);
+                B::template qk0<2>(stage_of(n + 1), qf, acc, lr, lg);
+                __builtin_amdgcn_s_setprio(0);
                 sm(n + 1, std::bool_constant<MODE == 1>{});
               }
             });
