@@ -158,6 +158,23 @@ __device__ __forceinline__ void dma16(const void* g, uint16_t* lds) {
                : "memory", "m0");
 }
 
+// The same copy from a uniform 64-bit base plus a per-lane 32-bit byte offset
+// (the global_load saddr form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void dma16_base(const char* base, uint32_t off, uint16_t* lds) {
+  const uint32_t lb = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
+  // (readfirstlane yields an int: each half goes through uint32_t so that it
+  // is zero-extended)
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(bs), "s"(lb)
+               : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- shared parts
 template <int D, int FMT, bool PAGED>
 struct Src {
@@ -237,6 +254,64 @@ struct Src {
       const char *kp, *vp;
       const bool ok = row_src<CHECK>(p, it, kbase + r, kp, vp);
       dma16<ASYNC>(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, tile + (row0 + i * RPI) * D);
+    }
+  }
+
+  // ---- bf16: when keys [key0, key0 + n) are all before the item's end and
+  //      their rows are consecutive in one source (one page, the new tokens,
+  //      or the unpaged K/V), the row of key0 and the row stride; all values
+  //      uniform over the wave.
+  __device__ static __forceinline__ bool rows_contig(const AttnParams& p, const Item& it, int key0, int n,
+                                                     const char*& k0, const char*& v0, uint32_t& stride) {
+    key0 = __builtin_amdgcn_readfirstlane(key0);
+    if (key0 + n > it.kend) return false;
+    if constexpr (PAGED) {
+      if (FMT == kKvBf16 && it.new_direct && key0 + n > it.cache_len) {
+        if (key0 < it.cache_len) return false;
+        const uint64_t off =
+            static_cast<uint64_t>(static_cast<uint32_t>(it.kn_start + key0 - it.cache_len)) * it.new_row_bytes;
+        k0 = it.knb + off;
+        v0 = it.vnb + off;
+        stride = it.new_row_bytes;
+        return true;
+      }
+      uint32_t pi, pl, slot;
+      if (p.page_shift >= 0) {
+        pi = static_cast<uint32_t>(key0) >> p.page_shift;
+        pl = static_cast<uint32_t>(key0 + n - 1) >> p.page_shift;
+        slot = static_cast<uint32_t>(key0) & (p.page_size - 1);
+      } else {
+        pi = static_cast<uint32_t>(key0) / static_cast<uint32_t>(p.page_size);
+        pl = static_cast<uint32_t>(key0 + n - 1) / static_cast<uint32_t>(p.page_size);
+        slot = static_cast<uint32_t>(key0) - pi * p.page_size;
+      }
+      if (pi != pl) return false;
+      const int page = __builtin_amdgcn_readfirstlane(it.pids[pi - it.first_page]);
+      if (page < 0) return false;
+      const uint64_t off =
+          static_cast<uint64_t>(static_cast<uint32_t>(page) * static_cast<uint32_t>(p.page_size) + slot) *
+          it.row_bytes;
+      k0 = it.kb + off;
+      v0 = it.vb + off;
+    } else {
+      const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(it.kn_start + key0)) * it.row_bytes;
+      k0 = it.kb + off;
+      v0 = it.vb + off;
+    }
+    stride = it.row_bytes;
+    return true;
+  }
+
+  // tile rows [row0, row0 + nrows) from consecutive source rows at `src`
+  // (row r + row0 at src + r * stride); the calling wave issues nrows / RPI
+  // copies
+  __device__ static __forceinline__ void dma_rows(const char* src, uint32_t stride, uint16_t* tile, int row0,
+                                                  int nrows, int lane) {
+#pragma unroll
+    for (int i = 0; i < nrows / RPI; ++i) {
+      const int rr = i * RPI + lane / C::CHUNKS;
+      const int c = (lane % C::CHUNKS) ^ C::swz(row0 + rr);
+      dma16_base(src, static_cast<uint32_t>(rr) * stride + c * 16, tile + (row0 + i * RPI) * D);
     }
   }
 
@@ -349,7 +424,8 @@ struct Src {
   // staged in `pids` (LDS) by all `nt` threads.
   __device__ static __forceinline__ void setup_item(const AttnParams& p, const QEntry& e, int32_t* pids, int t,
                                                     int nt, Item& it) {
-    const int kvh = e.kvh;
+    // every field is the same for all lanes: keep them in scalar registers
+    const int kvh = __builtin_amdgcn_readfirstlane(e.kvh);
     it.row_bytes = static_cast<uint32_t>(p.hkv) * (D * ESIZE);
     it.new_row_bytes = static_cast<uint32_t>(p.hkv) * (D * 2);
     it.kb = static_cast<const char*>(p.k) + kvh * (D * ESIZE);
@@ -358,15 +434,15 @@ struct Src {
     it.vnb = static_cast<const char*>(p.v_new) + kvh * (D * 2);
     it.pids = pids;
     it.first_page = 0;
-    it.kn_start = e.item.s.kn_start;
-    it.cache_len = e.item.s.cache_len;
+    it.kn_start = __builtin_amdgcn_readfirstlane(e.item.s.kn_start);
+    it.cache_len = __builtin_amdgcn_readfirstlane(e.item.s.cache_len);
     it.kvh = kvh;
-    it.kend = e.item.key_end;
+    it.kend = __builtin_amdgcn_readfirstlane(e.item.key_end);
     it.new_direct = p.new_direct != 0;
     // page ids of the item's key range -> LDS
     if constexpr (PAGED) {
       if (e.item.key_end > e.item.key_begin) {
-        it.first_page = e.item.key_begin / p.page_size;
+        it.first_page = __builtin_amdgcn_readfirstlane(e.item.key_begin / p.page_size);
         const int last_page = (e.item.key_end - 1) / p.page_size;
         const int32_t* bt = p.block_table + static_cast<int64_t>(e.item.seq) * p.max_pages;
         for (int i = t; i <= last_page - it.first_page; i += nt) {
@@ -858,7 +934,12 @@ struct Prefill : Src<D, FMT, PAGED> {
     auto stage_dma = [&](int j) {
       const int kbase = kbeg + j * kBlockN;
       uint16_t* const kt = stage_of(j);
-      if (kbase + kBlockN <= it.kend) {
+      const char *k0, *v0;
+      uint32_t stride;
+      if (B::rows_contig(p, it, kbase + wave * WROWS, WROWS, k0, v0, stride)) {
+        B::dma_rows(k0, stride, kt, wave * WROWS, WROWS, lane);
+        B::dma_rows(v0, stride, kt + C::TILE, wave * WROWS, WROWS, lane);
+      } else if (kbase + kBlockN <= it.kend) {
         B::template dma_tile<false, false, true>(p, it, kt, kbase, wave * WROWS, WROWS, lane);
         B::template dma_tile<false, true, true>(p, it, kt + C::TILE, kbase, wave * WROWS, WROWS, lane);
       } else {
