@@ -95,16 +95,17 @@ void build_plan(const PlanInput& in, Plan& out) {
 
   // ---- split decision per tile -> units (tile, part).
   //      Prefill-mode grid (MFMA-bound, many items): longest-first dealing
-  //      ends the grid evenly when no tile is much above the average load of
-  //      a workgroup slot; a tile above 3/4 of that average (its partials cost
-  //      a merge over up to 256 rows) is split into parts near that size.
+  //      ends the grid evenly when no tile is above the average load of a
+  //      workgroup slot; only a tile above that average is split, into parts
+  //      near that size (the fp32 partials of up to 256 rows per part and
+  //      their merge pass cost more than a slightly uneven end of the grid).
   //      Decode-mode grid (HBM-bound, few long sequences): every item of a
   //      dispatch round takes about as long, so the grid lasts about
   //      ceil(items / slots) rounds of (work per item + fixed cost per item);
   //      tiles are cut into parts of a common size chosen so that the item
   //      count fills whole rounds of the slots.
   const int64_t cus = std::max(1, in.num_cus);
-  const double target_pre = 0.75 * total_pre / static_cast<double>(cus * std::max(1, in.pre_wg_per_cu));
+  const double target_pre = total_pre / static_cast<double>(cus * std::max(1, in.pre_wg_per_cu));
   const int32_t min_blocks = std::max(1, (in.split_min_keys + kBlockN - 1) / kBlockN);
   auto split_limit = [&](const Tile& t) {
     const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;

@@ -376,21 +376,20 @@ struct Src {
 
   // a7: 4 consecutive head-dim values (from d0) of tile row r, to out / lse or
   // to the split partials
-  __device__ static __forceinline__ void store4(const AttnParams& p, const WorkItem& item,
-                                                const SeqInfo& sq, int r, int token, int qh, int d0,
-                                                float x0, float x1, float x2, float x3, float lse_v,
-                                                bool write_lse) {
-    if (item.part < 0) {
-      uint16_t* orow = p.out + (static_cast<int64_t>(sq.q_start + token) * p.hq + qh) * D + d0;
+  __device__ static __forceinline__ void store4(const AttnParams& p, int part, int q_start, int r, int token,
+                                                int qh, int d0, float x0, float x1, float x2, float x3,
+                                                float lse_v, bool write_lse) {
+    if (part < 0) {
+      uint16_t* orow = p.out + (static_cast<int64_t>(q_start + token) * p.hq + qh) * D + d0;
       u32x2 w2;
       w2[0] = f32_to_bf16_rne(x0) | (static_cast<uint32_t>(f32_to_bf16_rne(x1)) << 16);
       w2[1] = f32_to_bf16_rne(x2) | (static_cast<uint32_t>(f32_to_bf16_rne(x3)) << 16);
       *reinterpret_cast<u32x2*>(orow) = w2;
-      if (write_lse && p.lse) p.lse[static_cast<int64_t>(qh) * p.total_q + sq.q_start + token] = lse_v;
+      if (write_lse && p.lse) p.lse[static_cast<int64_t>(qh) * p.total_q + q_start + token] = lse_v;
     } else {
-      *reinterpret_cast<float4*>(p.part_o + static_cast<int64_t>(item.part + r) * D + d0) =
+      *reinterpret_cast<float4*>(p.part_o + static_cast<int64_t>(part + r) * D + d0) =
           make_float4(x0, x1, x2, x3);
-      if (write_lse) p.part_lse[item.part + r] = lse_v;
+      if (write_lse) p.part_lse[part + r] = lse_v;
     }
   }
 
@@ -774,6 +773,9 @@ struct Decode : Src<D, FMT, PAGED> {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nb = it.kend > kbeg ? (it.kend - kbeg + DK - 1) / DK : 0;
+    const int part = __builtin_amdgcn_readfirstlane(item.part);
+    const int q_start = __builtin_amdgcn_readfirstlane(sq.q_start);
+    const int row0 = __builtin_amdgcn_readfirstlane(item.row0);
     uint16_t* const ktile = smem + (wave >> 1) * C::STAGE;
     uint16_t* const vtile = ktile + C::TILE;
     const int trow0 = (wave & 1) * DK;
@@ -875,10 +877,10 @@ struct Decode : Src<D, FMT, PAGED> {
       const bool live = lsum > 0.f;
       const float inv = live ? p.v_scale / lsum : 0.f;
       const float lse_v = live ? mmax * c * kLn2 + __logf(lsum) : -INFINITY;
-      const int pr = item.row0 + r;
+      const int pr = row0 + r;
       const int tok = pr / p.g;
       const int h = it.kvh * p.g + (pr - tok * p.g);
-      B::store4(p, item, sq, r, tok, h, d0, acc4.x * inv, acc4.y * inv, acc4.z * inv, acc4.w * inv,
+      B::store4(p, part, q_start, r, tok, h, d0, acc4.x * inv, acc4.y * inv, acc4.z * inv, acc4.w * inv,
                 lse_v, d0 == 0);
     }
   }
@@ -927,6 +929,8 @@ struct Prefill : Src<D, FMT, PAGED> {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
+    const int part = __builtin_amdgcn_readfirstlane(item.part);
+    const int q_start = __builtin_amdgcn_readfirstlane(sq.q_start);
 
     // ---- staging of block j into stage j mod NS: this wave's WROWS rows of K
     //      and V (bf16), or the block through registers (fp8)
@@ -1112,7 +1116,7 @@ struct Prefill : Src<D, FMT, PAGED> {
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4)
-            B::store4(p, item, sq, wrow, token, qh, d * 32 + i4 * 8 + lg * 4, o[d][i4 * 4 + 0] * inv,
+            B::store4(p, part, q_start, wrow, token, qh, d * 32 + i4 * 8 + lg * 4, o[d][i4 * 4 + 0] * inv,
                       o[d][i4 * 4 + 1] * inv, o[d][i4 * 4 + 2] * inv, o[d][i4 * 4 + 3] * inv, lse_v,
                       lg == 0 && d == 0 && i4 == 0);
       }
