@@ -136,7 +136,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="varlen_prefill",
                     choices=["varlen_prefill", "paged_decode", "chunked_prefill", "mixed_fp8", "tiny"])
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through (defeats the MALL)")

@@ -810,7 +810,15 @@ struct Decode : Src<D, FMT, PAGED> {
         B::template f8_store<F8PASS>(fv, vtile, trow0, DK, lane, 64);
         wait_lds();
       } else {
-        if (kbase + DK <= it.kend) {
+        const char *k0, *v0, *k1, *v1;
+        uint32_t st0, st1;
+        if (B::rows_contig(p, it, kbase, DK / 2, k0, v0, st0) &&
+            B::rows_contig(p, it, kbase + DK / 2, DK / 2, k1, v1, st1)) {
+          B::dma_rows(k0, st0, ktile, trow0, DK / 2, lane);
+          B::dma_rows(k1, st1, ktile, trow0 + DK / 2, DK / 2, lane);
+          B::dma_rows(v0, st0, vtile, trow0, DK / 2, lane);
+          B::dma_rows(v1, st1, vtile, trow0 + DK / 2, DK / 2, lane);
+        } else if (kbase + DK <= it.kend) {
           B::template dma_tile<false, false>(p, it, ktile, kbase - trow0, trow0, DK, lane);
           B::template dma_tile<false, true>(p, it, vtile, kbase - trow0, trow0, DK, lane);
         } else {

@@ -23,6 +23,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+constexpr int kRegParts = 4;
+
 __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   const MergeGroup gr = p.groups[blockIdx.x];
   const SeqInfo sq = gr.s;
@@ -32,13 +34,39 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
   for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
     const int r = idx / per_row;
     const int c = idx - r * per_row;
+    // the first kRegParts parts' lse and outputs are loaded together (one
+    // memory round trip); further parts are read in a second pass
+    float ls[kRegParts];
+    float4 os[kRegParts];
+#pragma unroll
+    for (int s = 0; s < kRegParts; ++s) {
+      if (s < gr.nsplit) {
+        const int pr = gr.part + s * gr.nrows + r;
+        ls[s] = p.part_lse[pr];
+        os[s] = *reinterpret_cast<const float4*>(p.part_o + static_cast<int64_t>(pr) * D + c * 4);
+      }
+    }
     float mx = -INFINITY;
-    for (int s = 0; s < gr.nsplit; ++s) mx = fmaxf(mx, p.part_lse[gr.part + s * gr.nrows + r]);
+#pragma unroll
+    for (int s = 0; s < kRegParts; ++s)
+      if (s < gr.nsplit) mx = fmaxf(mx, ls[s]);
+    for (int s = kRegParts; s < gr.nsplit; ++s) mx = fmaxf(mx, p.part_lse[gr.part + s * gr.nrows + r]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float lse_v = -INFINITY;
     if (mx != -INFINITY) {
       float wsum = 0.f;
-      for (int s = 0; s < gr.nsplit; ++s) {
+#pragma unroll
+      for (int s = 0; s < kRegParts; ++s) {
+        if (s < gr.nsplit) {
+          const float w = __expf(ls[s] - mx);
+          wsum += w;
+          acc.x += w * os[s].x;
+          acc.y += w * os[s].y;
+          acc.z += w * os[s].z;
+          acc.w += w * os[s].w;
+        }
+      }
+      for (int s = kRegParts; s < gr.nsplit; ++s) {
         const int pr = gr.part + s * gr.nrows + r;
         const float w = __expf(p.part_lse[pr] - mx);
         const float4 o = *reinterpret_cast<const float4*>(p.part_o + static_cast<int64_t>(pr) * D + c * 4);
