@@ -303,6 +303,7 @@ def test_full_size_workloads_sampled(name):
         pick |= set(int(x) for x in rng.choice(wl.B, SAMPLE[name] - 1, replace=False))
     kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
     Qf = oracle.bf16_bits_to_f64
+    worst = [0.0, 0.0, 0.0]
     for b in sorted(pick):
         s, e = int(wl.cu_seqlens_q[b]), int(wl.cu_seqlens_q[b + 1])
         K, V = oracle.sequence_kv(b, k_new=wl.k_new, v_new=wl.v_new,
@@ -311,5 +312,7 @@ def test_full_size_workloads_sampled(name):
                                   cache_seqlens=wl.cache_seqlens, page_size=wl.page_size,
                                   cache_dtype=wl.cache_dtype, kv_scale=wl.kv_scale)
         ro, rl = oracle.attend(Qf(wl.q[s:e]), K, V, wl.causal, wl.scale)
-        check_attention(o_all[s:e], l_all[:, s:e], ro, rl, kind, label=f"{name} seq {b}")
-    say(f"[ok] {name}: sequences {sorted(pick)}")
+        errs = check_attention(o_all[s:e], l_all[:, s:e], ro, rl, kind, label=f"{name} seq {b}")
+        worst = [max(w, float(x)) for w, x in zip(worst, errs)]
+    say(f"[ok] {name}: sequences {sorted(pick)}; worst max {worst[0]:.2e} mean {worst[1]:.2e} "
+        f"lse {worst[2]:.2e}")
