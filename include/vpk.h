@@ -170,6 +170,64 @@ int32_t kv_cache_append(const vpk_dims* dims,
                         int32_t page_size, const float* kv_scale,
                         const vpk_host_index* host, void* stream);
 
+/*
+ * Prepared calls (plan once, run many times).  The work list of a call depends
+ * only on the lengths (cu_seqlens_q, cu_seqlens_knew, cache_seqlens), the head
+ * counts and the flags, so a caller that runs the same lengths repeatedly (a
+ * layer stack of one decode step, a graph replayed every step) can plan once
+ * and launch without host work.  vpk_plan_run allocates nothing, synchronises
+ * nothing and records no event, so it can be captured into a HIP graph; the
+ * flash-attention-style APIs on the pages either lack graph support or list it
+ * per backend ("[Refactor] Uniform PoDAttention API with Horizontal Fusion SMs
+ * Schedule", Limitations and Future Work; "Add KV cache for paged/non-paged
+ * attention", the backend support list).
+ */
+typedef struct vpk_plan_s* vpk_plan;
+
+/*
+ * vpk_plan_create -- validate the lengths and build the work list of a call,
+ * in device memory of the current device (with its own split-partial space,
+ * error flag and zero rows).  Synchronous (one blocking upload); not for use
+ * inside stream capture.
+ *   dims        as for attn_varlen_paged_fwd (kv_cache_dtype fixes the cache
+ *               format of every run).
+ *   host        host copies of the index arrays; cu_seqlens_q always,
+ *               cu_seqlens_knew with has_new, cache_seqlens with has_cache
+ *               (block_table optional: when given, its page ids for the
+ *               slots that will be read or written are range-checked here).
+ *   has_new     1: runs pass k_new / v_new (appended first when has_cache).
+ *   has_cache   1: runs pass a paged cache.
+ *   page_size, causal  as for attn_varlen_paged_fwd.
+ *   plan        receives the handle; the caller owns it (vpk_plan_destroy).
+ * The host arrays are read before the call returns.  Errors as for
+ * attn_varlen_paged_fwd; nothing is allocated on failure.
+ */
+int32_t vpk_plan_create(const vpk_dims* dims, const vpk_host_index* host, int32_t has_new,
+                        int32_t has_cache, int32_t page_size, int32_t causal, vpk_plan* plan);
+
+/*
+ * vpk_plan_run -- enqueue the call a plan describes on `stream`: the same
+ * steps and results as attn_varlen_paged_fwd with those lengths (append, then
+ * attention, then the merge of split parts), with the device buffers given
+ * here (same layouts and alignment rules).  The device index arrays are not
+ * read: the lengths are the plan's, and block_table is read on the device
+ * only.  When a plan has both prefill-mode and decode-mode work, the two grids
+ * run one after the other on `stream`.  Runs of one plan share its partial
+ * space: overlapping runs of the same plan (two streams at once) race.
+ * kv_scale is read on the host at each call (a captured graph keeps the
+ * values of the captured call).
+ */
+int32_t vpk_plan_run(vpk_plan plan, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const int32_t* block_table, float scale,
+                     const float* kv_scale, void* out, float* lse, void* stream);
+
+/* Synchronise `stream` and return (and clear) the plan's device error flag
+ * (bit 0: a page id outside [0, num_pages) was met on the device). */
+int32_t vpk_plan_device_error(vpk_plan plan, void* stream, int32_t* flags);
+
+/* Free a plan (NULL is accepted).  No run of it may still be pending. */
+int32_t vpk_plan_destroy(vpk_plan plan);
+
 /* Message describing the calling thread's last non-success status ("" if none). */
 const char* vpk_last_error(void);
 

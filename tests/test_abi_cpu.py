@@ -138,3 +138,39 @@ def test_options():
     assert lib.vpk_set_option(b"nope", 1) == 1
     assert "unknown option" in lib.vpk_last_error().decode()
     assert lib.vpk_timing_read(7, None, None) == 1
+
+
+def _plan_create(dims, host, has_new=1, has_cache=1, page_size=16, causal=1):
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    st = lib.vpk_plan_create(ctypes.byref(dims), None if host is None else ctypes.byref(host),
+                             has_new, has_cache, page_size, causal, ctypes.byref(h))
+    return st, lib.vpk_last_error().decode(), h
+
+
+def test_plan_create_errors_before_the_device():
+    """vpk_plan_create checks everything on the host first: each bad argument
+    returns its status with no handle and no device call."""
+    d = _dims()
+    hi, keep = _host([0, 2, 4], [0, 2, 4], [3, 5])
+    st, msg, h = _plan_create(d, None)
+    assert st == 1 and "host index" in msg and h.value is None
+    hq, keep2 = _host([0, 2, 4])                                     # no cu_seqlens_knew / cache_seqlens
+    assert _plan_create(d, hq)[0] == 1
+    assert _plan_create(d, hi, has_new=0, has_cache=0)[0] == 1
+    assert _plan_create(d, hi, has_new=2)[0] == 1
+    assert _plan_create(d, hi, causal=2)[0] == 1
+    assert _plan_create(d, hi, page_size=0)[0] == 1
+    assert _plan_create(_dims(head_dim=96), hi)[0] == 2
+    bad, k3 = _host([0, 3, 2], [0, 2, 4], [3, 5])
+    assert "non-decreasing" in _plan_create(d, bad)[1]
+    full, k4 = _host([0, 2, 4], [0, 2, 4], [63, 5])                  # 63 + 2 keys > 4 pages of 16
+    assert _plan_create(d, full)[0] == 3
+    bt = np.array([[0, 1, 2, 3], [4, 99, 6, 7]], np.int32)           # page 99 >= num_pages
+    hb, k5 = _host([0, 2, 4], [0, 2, 4], [3, 20], bt)
+    st, msg, _ = _plan_create(d, hb)
+    assert st == 1 and "outside" in msg
+    assert _plan_create(_dims(total_knew=4), hi, has_new=0)[0] == 1   # new tokens counted without new tokens
+    lib = _lib.load()
+    assert lib.vpk_plan_run(None, None, None, None, None, None, None, 0.1, None, None, None, None) == 1
+    assert lib.vpk_plan_destroy(None) == 0

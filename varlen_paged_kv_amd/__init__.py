@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import VpkDims, VpkHostIndex
 
 __all__ = ["attn_varlen_paged_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
-           "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug",
+           "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE"]
 
 # kernel ids of the timing API: the prefill-mode attention grid, the standalone
@@ -153,6 +153,106 @@ def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     del keep
     _check(st)
     return out, lse
+
+
+class Plan:
+    """A prepared call (vpk_plan_create / vpk_plan_run): the work list of one set
+    of lengths, built once in device memory; run() launches without host work
+    and can be captured into a graph.
+
+    Plan(cu_seqlens_q, num_q_heads, num_kv_heads, head_dim, cu_seqlens_knew=None,
+         cache_seqlens=None, block_table=None, page_size=0, num_pages=0,
+         max_pages_per_seq=0, cache_dtype="bf16" | "fp8", causal=True)
+    The index arrays are host arrays (numpy or CPU tensors); block_table is
+    optional here (page-id range checks).  A plan is for one device: create it
+    with that device current.
+    """
+
+    def __init__(self, cu_seqlens_q, num_q_heads: int, num_kv_heads: int, head_dim: int, *,
+                 cu_seqlens_knew=None, cache_seqlens=None, block_table=None, page_size: int = 0,
+                 num_pages: int = 0, max_pages_per_seq: int = 0, cache_dtype: str = "bf16",
+                 causal: bool = True):
+        lib = _lib.load()
+        self._h = None
+        cu_q = _host_i32(cu_seqlens_q)
+        cu_kn = _host_i32(cu_seqlens_knew)
+        cl = _host_i32(cache_seqlens)
+        B = cu_q.size - 1
+        self.batch = B
+        self.has_new = cu_kn is not None
+        self.has_cache = cl is not None
+        self.fp8 = self.has_cache and cache_dtype == "fp8"
+        self.total_q = int(cu_q[-1])
+        self.total_knew = int(cu_kn[-1]) if self.has_new else 0
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.page_size = int(page_size) if self.has_cache else 0
+        self.num_pages = int(num_pages) if self.has_cache else 0
+        self.max_pages = int(max_pages_per_seq) if self.has_cache else 0
+        dims = VpkDims(B, self.total_q, self.total_knew, num_q_heads, num_kv_heads, head_dim,
+                       self.num_pages, self.max_pages,
+                       _lib.VPK_DTYPE_FP8_E4M3FN if self.fp8 else _lib.VPK_DTYPE_BF16)
+        hi, keep = _host_index(cu_q, cu_kn, cl, block_table)
+        h = ctypes.c_void_p()
+        st = lib.vpk_plan_create(ctypes.byref(dims), ctypes.byref(hi), int(self.has_new),
+                                 int(self.has_cache), self.page_size, int(bool(causal)), ctypes.byref(h))
+        del keep
+        _check(st)
+        self._h = h
+
+    def run(self, q, k_new=None, v_new=None, k_cache=None, v_cache=None, block_table=None, *,
+            scale: Optional[float] = None, kv_scale=None, out=None, lse=None, return_lse: bool = True,
+            stream=None):
+        """Enqueue the planned call with these buffers; returns (out, lse)."""
+        lib = _lib.load()
+        q = _dev(q, "q", _BF16)
+        k_new = _dev(k_new, "k_new", _BF16)
+        v_new = _dev(v_new, "v_new", _BF16)
+        k_cache = _dev(k_cache, "k_cache", _FP8 if self.fp8 else _BF16)
+        v_cache = _dev(v_cache, "v_cache", _FP8 if self.fp8 else _BF16)
+        block_table = _dev(block_table, "block_table", _I32)
+        Hq, Hkv, D = self.num_q_heads, self.num_kv_heads, self.head_dim
+        for name, t, shp in (("q", q, (self.total_q, Hq, D)),
+                             ("k_new", k_new, (self.total_knew, Hkv, D)),
+                             ("v_new", v_new, (self.total_knew, Hkv, D)),
+                             ("k_cache", k_cache, (self.num_pages, self.page_size, Hkv, D)),
+                             ("v_cache", v_cache, (self.num_pages, self.page_size, Hkv, D))):
+            if t is not None and tuple(t.shape) != shp:
+                raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+        if block_table is not None and tuple(block_table.shape) != (self.batch, self.max_pages):
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE,
+                           f"block_table has shape {tuple(block_table.shape)}, expected {(self.batch, self.max_pages)}")
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and return_lse:
+            lse = torch.empty((Hq, self.total_q), dtype=torch.float32, device=q.device)
+        ks = None
+        if self.fp8:
+            if kv_scale is None:
+                raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache")
+            ks = (ctypes.c_float * 2)(float(kv_scale[0]), float(kv_scale[1]))
+        st = lib.vpk_plan_run(self._h, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_table), float(scale), ks, _ptr(out), _ptr(lse),
+                              _stream_handle(stream))
+        _check(st)
+        return out, lse
+
+    def device_error(self, stream=None) -> int:
+        f = ctypes.c_int32(0)
+        _check(_lib.load().vpk_plan_device_error(self._h, _stream_handle(stream), ctypes.byref(f)))
+        return int(f.value)
+
+    def close(self):
+        if self._h is not None:
+            h, self._h = self._h, None
+            _check(_lib.load().vpk_plan_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def kv_cache_append(k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table, cache_seqlens,

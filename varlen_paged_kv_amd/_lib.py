@@ -26,7 +26,8 @@ STATUS_NAMES = {
 EXPORTS = (
     "attn_varlen_paged_fwd", "kv_cache_append", "vpk_last_error", "vpk_abi_version",
     "vpk_set_option", "vpk_timing_enable", "vpk_timing_reset", "vpk_timing_read",
-    "vpk_device_error", "vpk_plan_debug",
+    "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
+    "vpk_plan_destroy",
 )
 
 
@@ -91,5 +92,13 @@ def load() -> ctypes.CDLL:
     lib.vpk_plan_debug.restype = i32
     lib.vpk_plan_debug.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, i32,
                                    P(i32), i32, P(i32), P(i32)]
+    lib.vpk_plan_create.restype = i32
+    lib.vpk_plan_create.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, P(vp)]
+    lib.vpk_plan_run.restype = i32
+    lib.vpk_plan_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, P(f32), vp, vp, vp]
+    lib.vpk_plan_device_error.restype = i32
+    lib.vpk_plan_device_error.argtypes = [vp, vp, P(i32)]
+    lib.vpk_plan_destroy.restype = i32
+    lib.vpk_plan_destroy.argtypes = [vp]
     _lib = lib
     return lib

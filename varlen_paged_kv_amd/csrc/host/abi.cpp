@@ -395,12 +395,8 @@ Layout layout_for(const Plan& p, int32_t B, int32_t D) {
   return L;
 }
 
-// Serialise the plan into the next pinned plan buffer; *index receives it.
-int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B,
-                   int* index) {
-  int32_t st = take_plan_buffer(w, L.plan_end, index);
-  if (st) return st;
-  char* base = w->plan[*index].host;
+// Serialise the plan records into `base` (L.plan_end bytes).
+void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B, char* base) {
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
   if (cu_kn) std::memcpy(base + L.cu_kn, cu_kn, sizeof(int32_t) * (B + 1));
   if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
@@ -409,10 +405,18 @@ int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* 
     std::memcpy(base + L.queues, p.queue_start.data(), sizeof(int32_t) * p.queue_start.size());
   if (!p.queue_work.empty())
     std::memcpy(base + L.work, p.queue_work.data(), sizeof(int32_t) * p.queue_work.size());
+}
+
+// Serialise the plan into the next pinned plan buffer; *index receives it.
+int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B,
+                   int* index) {
+  int32_t st = take_plan_buffer(w, L.plan_end, index);
+  if (st) return st;
+  serialize_plan(p, L, cu_kn, B, w->plan[*index].host);
   return VPK_SUCCESS;
 }
 
-AppendParams append_params(const Call& c, Workspace* w, char* R, const Layout& L,
+AppendParams append_params(const Call& c, char* head, char* R, const Layout& L,
                            const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                            const int32_t* block_table) {
   const vpk_dims* d = c.d;
@@ -424,7 +428,7 @@ AppendParams append_params(const Call& c, Workspace* w, char* R, const Layout& L
   ap.block_table = block_table;
   ap.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
   ap.cu_knew = reinterpret_cast<const int32_t*>(R + L.cu_kn);
-  ap.err_flag = reinterpret_cast<int32_t*>(w->dev);
+  ap.err_flag = reinterpret_cast<int32_t*>(head);
   ap.batch = d->batch;
   ap.total_knew = d->total_knew;
   ap.max_pages = d->max_pages_per_seq;
@@ -447,6 +451,146 @@ int32_t enqueue_append(const AppendParams& ap, hipStream_t stream) {
 int32_t check_ptr(const void* p, size_t a, const char* name) {
   if (!p) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + " is NULL");
   if (!aligned(p, a)) return fail(VPK_ERROR_INVALID_VALUE, std::string(name) + " is not " + std::to_string(a) + "-byte aligned");
+  return VPK_SUCCESS;
+}
+
+// Where a call's device-side data lives: the plan records (pinned host
+// memory for a direct call, device memory for a prepared plan), the split
+// partials, and the head with the error flag and the zero rows.
+struct Bases {
+  char* R;
+  char* PA;
+  char* head;
+};
+
+// Launch a planned call: the append (fp8 cache, or standalone), the attention
+// grids, the merge.  With `side`, a call with both grids runs the decode-mode
+// grid on the workspace's side stream next to the prefill-mode grid; without
+// it the two grids run one after the other on `stream` (no events: nothing
+// here allocates, synchronises or records on another stream, so the whole
+// sequence can be captured into a graph).
+int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Bases& bs, const void* q,
+                    const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* block_table, int32_t causal, float scale, void* out, float* lse,
+                    hipStream_t stream, Workspace* side, bool timed) {
+  const vpk_dims* dims = c.d;
+  const float* kv_scale = c.kv_scale;
+  const int32_t page_size = c.page_size;
+  char* const R = bs.R;
+  char* const PA = bs.PA;
+  int32_t st;
+  const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
+  const AppendParams ap = append_params(c, bs.head, R, L, k_new, v_new, k_cache, v_cache, block_table);
+  // bf16 cache: attention reads the new tokens from k_new / v_new (the same
+  // bytes the append stores), so the append can run inside an attention grid.
+  // fp8 cache: attention must see the quantised bytes, so the append runs first.
+  const bool new_direct = do_append && !c.fp8;
+  const bool run_pre = plan.prefill.grid > 0;
+  const bool run_dec = plan.decode.grid > 0;
+  const bool fuse_append = new_direct && (run_pre || run_dec);
+  if (do_append && !fuse_append) {
+    if (timed) {
+      if ((st = enqueue_append(ap, stream))) return st;
+    } else {
+      const int rc = vpk::launch_append(ap, stream);
+      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "append launch");
+    }
+  }
+  if (run_pre || run_dec) {
+    AttnParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = c.has_cache ? k_cache : k_new;
+    p.v = c.has_cache ? v_cache : v_new;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.new_direct = new_direct ? 1 : 0;
+    p.block_table = block_table;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.part_o = reinterpret_cast<float*>(PA + L.part_o);
+    p.part_lse = reinterpret_cast<float*>(PA + L.part_lse);
+    p.err_flag = reinterpret_cast<int32_t*>(bs.head);
+    p.zeros = bs.head + kZerosOffset;
+    p.max_pages = dims->max_pages_per_seq;
+    p.num_pages = dims->num_pages;
+    p.page_size = c.has_cache ? page_size : 1;
+    p.page_shift = -1;
+    if (c.has_cache && (page_size & (page_size - 1)) == 0) {
+      int sh = 0;
+      while ((1 << sh) < page_size) ++sh;
+      p.page_shift = sh;
+    }
+    p.hq = dims->num_q_heads;
+    p.hkv = dims->num_kv_heads;
+    p.g = dims->num_q_heads / dims->num_kv_heads;
+    p.total_q = dims->total_q;
+    p.causal = causal;
+    const double log2e = 1.4426950408889634;
+    p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
+                                         (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
+    p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
+    p.app = ap;
+    const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
+    // `with_append`: this grid also runs one workgroup per new token
+    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s, bool with_append) -> int32_t {
+      AttnParams a = p;
+      a.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
+      a.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
+      a.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
+      a.persistent = Lc.persistent ? 1 : 0;
+      a.num_items = Lc.count;
+      a.attn_blocks = Lc.grid;
+      const int grid = Lc.grid + (with_append ? dims->total_knew : 0);
+      int rc;
+      if (timed) {
+        KernelTimer tm(dec ? 2 : 0, s);
+        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, dec, s);
+      } else {
+        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, dec, s);
+      }
+      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
+      return VPK_SUCCESS;
+    };
+    if (run_pre && run_dec && side) {
+      // both grids at once: the decode-mode grid (HBM-bound) on the side
+      // stream next to the prefill-mode grid (MFMA-bound), joined at the end
+      if ((st = ensure_aux(side))) return st;
+      hipError_t e;
+      if ((e = hipEventRecord(side->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
+      if ((e = hipStreamWaitEvent(side->aux, side->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
+      if ((st = launch(plan.decode, true, side->aux, fuse_append))) return st;
+      if ((e = hipEventRecord(side->ev_join, side->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
+      if ((st = launch(plan.prefill, false, stream, false))) return st;
+      if ((e = hipStreamWaitEvent(stream, side->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
+    } else {
+      // the new tokens ride with the first grid launched
+      if (run_dec && (st = launch(plan.decode, true, stream, fuse_append))) return st;
+      if (run_pre && (st = launch(plan.prefill, false, stream, fuse_append && !run_dec))) return st;
+    }
+  }
+  if (!plan.groups.empty()) {
+    // a8: LSE merge of split parts, after the grids (the kernel boundary makes
+    // the partials visible across the device without per-part fences)
+    MergeParams mp{};
+    mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
+    mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
+    mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
+    mp.out = static_cast<uint16_t*>(out);
+    mp.lse = lse;
+    mp.num_groups = static_cast<int32_t>(plan.groups.size());
+    mp.hq = dims->num_q_heads;
+    mp.g = dims->num_q_heads / dims->num_kv_heads;
+    mp.total_q = dims->total_q;
+    mp.head_dim = dims->head_dim;
+    int rc;
+    if (timed) {
+      KernelTimer tm(3, stream);
+      rc = vpk::launch_merge(mp, stream);
+    } else {
+      rc = vpk::launch_merge(mp, stream);
+    }
+    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
+  }
   return VPK_SUCCESS;
 }
 
@@ -510,106 +654,10 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   if ((st = get_workspace(stream, L.part_end, &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
-  char* const R = w->plan[region].host;
-  char* const PA = w->parts();
-
-  const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
-  const AppendParams ap = append_params(c, w, R, L, k_new, v_new, k_cache, v_cache, block_table);
-  // bf16 cache: attention reads the new tokens from k_new / v_new (the same
-  // bytes the append stores), so the append can run inside an attention grid.
-  // fp8 cache: attention must see the quantised bytes, so the append runs first.
-  const bool new_direct = do_append && !c.fp8;
-  const bool run_pre = plan.prefill.grid > 0;
-  const bool run_dec = plan.decode.grid > 0;
-  const bool fuse_append = new_direct && (run_pre || run_dec);
-  if (do_append && !fuse_append) {
-    if ((st = enqueue_append(ap, stream))) return st;
-  }
-  if (run_pre || run_dec) {
-    AttnParams p{};
-    p.q = static_cast<const uint16_t*>(q);
-    p.k = c.has_cache ? k_cache : k_new;
-    p.v = c.has_cache ? v_cache : v_new;
-    p.k_new = k_new;
-    p.v_new = v_new;
-    p.new_direct = new_direct ? 1 : 0;
-    p.block_table = block_table;
-    p.out = static_cast<uint16_t*>(out);
-    p.lse = lse;
-    p.part_o = reinterpret_cast<float*>(PA + L.part_o);
-    p.part_lse = reinterpret_cast<float*>(PA + L.part_lse);
-    p.err_flag = reinterpret_cast<int32_t*>(w->dev);
-    p.zeros = w->dev + kZerosOffset;
-    p.max_pages = dims->max_pages_per_seq;
-    p.num_pages = dims->num_pages;
-    p.page_size = c.has_cache ? page_size : 1;
-    p.page_shift = -1;
-    if (c.has_cache && (page_size & (page_size - 1)) == 0) {
-      int s = 0;
-      while ((1 << s) < page_size) ++s;
-      p.page_shift = s;
-    }
-    p.hq = dims->num_q_heads;
-    p.hkv = dims->num_kv_heads;
-    p.g = dims->num_q_heads / dims->num_kv_heads;
-    p.total_q = dims->total_q;
-    p.causal = causal;
-    const double log2e = 1.4426950408889634;
-    p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
-                                         (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
-    p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
-    p.app = ap;
-    const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
-    // `with_append`: this grid also runs one workgroup per new token
-    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s, bool with_append) -> int32_t {
-      AttnParams q = p;
-      q.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
-      q.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
-      q.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
-      q.persistent = Lc.persistent ? 1 : 0;
-      q.num_items = Lc.count;
-      q.attn_blocks = Lc.grid;
-      const int grid = Lc.grid + (with_append ? dims->total_knew : 0);
-      KernelTimer tm(dec ? 2 : 0, s);
-      const int rc = vpk::launch_attention(q, grid, dims->head_dim, fmt, c.has_cache, dec, s);
-      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
-      return VPK_SUCCESS;
-    };
-    if (run_pre && run_dec) {
-      // both grids at once: the decode-mode grid (HBM-bound) on the side
-      // stream next to the prefill-mode grid (MFMA-bound), joined at the end
-      if ((st = ensure_aux(w))) return st;
-      hipError_t e;
-      if ((e = hipEventRecord(w->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
-      if ((e = hipStreamWaitEvent(w->aux, w->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
-      if ((st = launch(plan.decode, true, w->aux, fuse_append))) return st;
-      if ((e = hipEventRecord(w->ev_join, w->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
-      if ((st = launch(plan.prefill, false, stream, false))) return st;
-      if ((e = hipStreamWaitEvent(stream, w->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
-    } else if (run_pre) {
-      if ((st = launch(plan.prefill, false, stream, fuse_append))) return st;
-    } else {
-      if ((st = launch(plan.decode, true, stream, fuse_append))) return st;
-    }
-  }
-  if (!plan.groups.empty()) {
-    // a8: LSE merge of split parts, after the grids (the kernel boundary makes
-    // the partials visible across the device without per-part fences)
-    MergeParams mp{};
-    mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
-    mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
-    mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
-    mp.out = static_cast<uint16_t*>(out);
-    mp.lse = lse;
-    mp.num_groups = static_cast<int32_t>(plan.groups.size());
-    mp.hq = dims->num_q_heads;
-    mp.g = dims->num_q_heads / dims->num_kv_heads;
-    mp.total_q = dims->total_q;
-    mp.head_dim = dims->head_dim;
-    KernelTimer tm(3, stream);
-    const int rc = vpk::launch_merge(mp, stream);
-    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
-  }
+  const Bases bases{w->plan[region].host, w->parts(), w->dev};
+  if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
+                        out, lse, stream, w, true)))
+    return st;
   return release_plan_buffer(w, stream, region);
 }
 
@@ -648,16 +696,193 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
-  if ((st = enqueue_append(append_params(c, w, w->plan[region].host, L, k_new, v_new, k_cache,
+  if ((st = enqueue_append(append_params(c, w->dev, w->plan[region].host, L, k_new, v_new, k_cache,
                                          v_cache, block_table),
                            stream)))
     return st;
   return release_plan_buffer(w, stream, region);
 }
 
+// Pointer checks shared by a direct call and a prepared plan's run.
+int32_t check_run_pointers(const Call& c, const void* q, const void* k_new, const void* v_new,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           float scale, const void* out, const float* lse) {
+  const vpk_dims* dims = c.d;
+  int32_t st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite and > 0");
+  if (c.has_new && (dims->total_knew > 0 || k_new || v_new)) {
+    if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
+  }
+  if (!c.has_new && (k_new || v_new)) return fail(VPK_ERROR_INVALID_VALUE, "the plan has no new tokens: k_new/v_new must be NULL");
+  if (c.has_cache) {
+    if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
+    if ((st = check_ptr(block_table, 4, "block_table"))) return st;
+  } else if (k_cache || v_cache) {
+    return fail(VPK_ERROR_INVALID_VALUE, "the plan has no cache: k_cache/v_cache must be NULL");
+  }
+  if (c.fp8) {
+    if (!c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache");
+    for (int i = 0; i < 2; ++i)
+      if (!std::isfinite(c.kv_scale[i]) || !(c.kv_scale[i] > 0.f))
+        return fail(VPK_ERROR_INVALID_VALUE, "kv_scale entries must be finite and > 0");
+  } else if (c.kv_scale && c.has_cache) {
+    return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
+  }
+  if (dims->total_q > 0) {
+    if ((st = check_ptr(q, 16, "q")) || (st = check_ptr(out, 16, "out"))) return st;
+    if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+  }
+  return VPK_SUCCESS;
+}
+
+}  // namespace
+
+// A prepared call: the plan of one set of lengths, in device memory with its
+// own error flag, zero rows and split partials.
+struct vpk_plan_s {
+  vpk_dims dims;
+  bool has_new = false, has_cache = false, fp8 = false;
+  int32_t page_size = 1, causal = 0;
+  int device = -1;
+  Plan plan;
+  Layout L{};
+  char* dev = nullptr;   // [head kFlagBytes][plan records L.plan_end][partials L.part_end]
+};
+
+namespace {
+
+int32_t plan_create_impl(const vpk_dims* dims, const vpk_host_index* host, int32_t has_new,
+                         int32_t has_cache, int32_t page_size, int32_t causal, vpk_plan* out) {
+  if (!out) return fail(VPK_ERROR_INVALID_VALUE, "plan output pointer is NULL");
+  *out = nullptr;
+  if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
+  if ((has_new != 0 && has_new != 1) || (has_cache != 0 && has_cache != 1))
+    return fail(VPK_ERROR_INVALID_VALUE, "has_new and has_cache must be 0 or 1");
+  if (!has_new && !has_cache) return fail(VPK_ERROR_INVALID_VALUE, "no keys: a plan needs new tokens, a cache, or both");
+  if (causal != 0 && causal != 1) return fail(VPK_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  const bool fp8 = has_cache && dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN;
+  static const float kAnyScale[2] = {1.f, 1.f};   // the scales come with each run
+  Call c{dims, has_new != 0, has_cache != 0, fp8, page_size, fp8 ? kAnyScale : nullptr};
+  int32_t st = check_dims(c);
+  if (st != VPK_SUCCESS) return st;
+  if (!has_new && dims->total_knew != 0) return fail(VPK_ERROR_INVALID_VALUE, "total_knew must be 0 without new tokens");
+  if (!has_cache && dims->num_pages != 0) return fail(VPK_ERROR_INVALID_VALUE, "num_pages must be 0 without a cache");
+  if (!host || !host->cu_seqlens_q || (has_new && !host->cu_seqlens_knew) || (has_cache && !host->cache_seqlens))
+    return fail(VPK_ERROR_INVALID_VALUE, "a plan needs the host index arrays (cu_seqlens_q, and cu_seqlens_knew / "
+                                         "cache_seqlens when there are new tokens / a cache)");
+  Mirrors m;
+  if ((st = get_mirrors(c, nullptr, nullptr, nullptr, host, nullptr, true, m))) return st;
+  if ((st = check_contents(c, m, true))) return st;
+
+  vpk_plan_s* pl = new (std::nothrow) vpk_plan_s();
+  if (!pl) return fail(VPK_ERROR_OUT_OF_MEMORY, "plan bookkeeping");
+  pl->dims = *dims;
+  pl->has_new = has_new != 0;
+  pl->has_cache = has_cache != 0;
+  pl->fp8 = fp8;
+  pl->page_size = has_cache ? page_size : 1;
+  pl->causal = causal;
+  const int32_t B = dims->batch;
+  PlanInput in;
+  fill_plan_input(c, m, causal, device_cus(), in);
+  try {
+    vpk::build_plan(in, pl->plan);
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
+  }
+  pl->L = layout_for(pl->plan, B, dims->head_dim);
+  hipError_t e = hipGetDevice(&pl->device);
+  if (e != hipSuccess) {
+    delete pl;
+    return hip_fail(e, "hipGetDevice");
+  }
+  const size_t bytes = kFlagBytes + pl->L.plan_end + pl->L.part_end;
+  void* d = nullptr;
+  if ((e = hipMalloc(&d, bytes)) != hipSuccess) {
+    delete pl;
+    return fail(VPK_ERROR_OUT_OF_MEMORY, std::string("hipMalloc plan: ") + hipGetErrorString(e));
+  }
+  pl->dev = static_cast<char*>(d);
+  std::vector<char> rec(pl->L.plan_end + kFlagBytes, 0);   // head (flag, zeros) then the records
+  serialize_plan(pl->plan, pl->L, m.cu_kn, B, rec.data() + kFlagBytes);
+  if ((e = hipMemcpy(pl->dev, rec.data(), rec.size(), hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(pl->dev);
+    delete pl;
+    return hip_fail(e, "hipMemcpy plan");
+  }
+  *out = pl;
+  return VPK_SUCCESS;
+}
+
+int32_t plan_run_impl(vpk_plan pl, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* block_table, float scale, const float* kv_scale,
+                      void* out, float* lse, void* stream_v) {
+  if (!pl) return fail(VPK_ERROR_INVALID_VALUE, "plan is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != pl->device) return fail(VPK_ERROR_INVALID_VALUE, "the plan was created on another device");
+  Call c{&pl->dims, pl->has_new, pl->has_cache, pl->fp8, pl->page_size, kv_scale};
+  int32_t st = check_run_pointers(c, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse);
+  if (st) return st;
+  if (pl->dims.batch == 0) return VPK_SUCCESS;
+  const Bases bases{pl->dev + kFlagBytes, pl->dev + kFlagBytes + pl->L.plan_end, pl->dev};
+  return enqueue_all(c, pl->plan, pl->L, bases, q, k_new, v_new, k_cache, v_cache, block_table, pl->causal,
+                     scale, out, lse, static_cast<hipStream_t>(stream_v), nullptr, false);
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t vpk_plan_create(const vpk_dims* dims, const vpk_host_index* host, int32_t has_new, int32_t has_cache,
+                        int32_t page_size, int32_t causal, vpk_plan* plan) {
+  try {
+    g_err.clear();
+    return plan_create_impl(dims, host, has_new, has_cache, page_size, causal, plan);
+  } catch (...) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host exception while planning");
+  }
+}
+
+int32_t vpk_plan_run(vpk_plan plan, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, const int32_t* block_table, float scale, const float* kv_scale, void* out,
+                     float* lse, void* stream) {
+  try {
+    g_err.clear();
+    return plan_run_impl(plan, q, k_new, v_new, k_cache, v_cache, block_table, scale, kv_scale, out, lse,
+                         stream);
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
+int32_t vpk_plan_device_error(vpk_plan plan, void* stream, int32_t* flags) {
+  g_err.clear();
+  if (!plan) return fail(VPK_ERROR_INVALID_VALUE, "plan is NULL");
+  hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t v = 0;
+  if ((e = hipMemcpy(&v, plan->dev, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy (flag)");
+  if (v != 0) {
+    const int32_t zero = 0;
+    if ((e = hipMemcpy(plan->dev, &zero, sizeof(zero), hipMemcpyHostToDevice)) != hipSuccess)
+      return hip_fail(e, "hipMemcpy (flag reset)");
+  }
+  if (flags) *flags = v;
+  return VPK_SUCCESS;
+}
+
+int32_t vpk_plan_destroy(vpk_plan plan) {
+  g_err.clear();
+  if (!plan) return VPK_SUCCESS;
+  hipError_t e = hipSuccess;
+  if (plan->dev) e = hipFree(plan->dev);
+  delete plan;
+  if (e != hipSuccess) return hip_fail(e, "hipFree plan");
+  return VPK_SUCCESS;
+}
 
 int32_t attn_varlen_paged_fwd(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
                               const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
