@@ -93,6 +93,9 @@ struct KernelTimer {
 
 // --------------------------------------------------------------- workspace
 
+// new tokens stored by one workgroup of the standalone append kernel
+constexpr int kAppendTokensStandalone = 8;
+
 // workspace head: [0, 256) error flag, [256, 512) zeros (never written)
 constexpr size_t kFlagBytes = 512;
 constexpr size_t kZerosOffset = 256;
@@ -374,17 +377,17 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
 }
 
 // Plan buffer layout (pinned host memory, offsets from its start):
-//   [seqs][cu_knew][units][merge groups][queue starts][queue work]
+//   [seqs][new tokens: sequence, position][units][merge groups][queue starts][queue work]
 // Partials area (device memory): [part_o fp32 rows x D][part_lse fp32 rows]
 struct Layout {
-  size_t seqs, cu_kn, items, groups, queues, work, plan_end, part_o, part_lse, part_end;
+  size_t seqs, tok, items, groups, queues, work, plan_end, part_o, part_lse, part_end;
 };
 
-Layout layout_for(const Plan& p, int32_t B, int32_t D) {
+Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D) {
   Layout L;
   L.seqs = 0;
-  L.cu_kn = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
-  L.items = align_up(L.cu_kn + sizeof(int32_t) * (B + 1), 64);
+  L.tok = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
+  L.items = align_up(L.tok + 2 * sizeof(int32_t) * static_cast<size_t>(Tn), 64);
   L.groups = align_up(L.items + sizeof(WorkItem) * p.items.size(), 64);
   L.queues = align_up(L.groups + sizeof(MergeGroup) * p.groups.size(), 64);
   L.work = align_up(L.queues + sizeof(int32_t) * p.queue_start.size(), 64);
@@ -395,10 +398,19 @@ Layout layout_for(const Plan& p, int32_t B, int32_t D) {
   return L;
 }
 
-// Serialise the plan records into `base` (L.plan_end bytes).
+// Serialise the plan records into `base` (L.plan_end bytes).  Each new token
+// gets its sequence and its logical position Lc + j, so an append workgroup
+// finds its tokens' slots with one read each.
 void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B, char* base) {
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
-  if (cu_kn) std::memcpy(base + L.cu_kn, cu_kn, sizeof(int32_t) * (B + 1));
+  if (cu_kn) {
+    int32_t* tok = reinterpret_cast<int32_t*>(base + L.tok);
+    for (int32_t b = 0; b < B; ++b)
+      for (int32_t t = cu_kn[b]; t < cu_kn[b + 1]; ++t) {
+        tok[2 * t] = b;
+        tok[2 * t + 1] = p.seqs[b].cache_len + (t - cu_kn[b]);
+      }
+  }
   if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
   if (!p.groups.empty()) std::memcpy(base + L.groups, p.groups.data(), sizeof(MergeGroup) * p.groups.size());
   if (!p.queue_start.empty())
@@ -426,8 +438,8 @@ AppendParams append_params(const Call& c, char* head, char* R, const Layout& L,
   ap.k_cache = k_cache;
   ap.v_cache = v_cache;
   ap.block_table = block_table;
-  ap.seqs = reinterpret_cast<const SeqInfo*>(R + L.seqs);
-  ap.cu_knew = reinterpret_cast<const int32_t*>(R + L.cu_kn);
+  ap.tok = reinterpret_cast<const int32_t*>(R + L.tok);
+  ap.tokens_per_wg = kAppendTokensStandalone;
   ap.err_flag = reinterpret_cast<int32_t*>(head);
   ap.batch = d->batch;
   ap.total_knew = d->total_knew;
@@ -540,7 +552,10 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       a.persistent = Lc.persistent ? 1 : 0;
       a.num_items = Lc.count;
       a.attn_blocks = Lc.grid;
-      const int grid = Lc.grid + (with_append ? dims->total_knew : 0);
+      // new tokens in groups: 32 per 512-thread prefill workgroup, 16 per
+      // 256-thread decode workgroup
+      a.app.tokens_per_wg = dec ? 16 : 32;
+      const int grid = Lc.grid + (with_append ? (dims->total_knew + a.app.tokens_per_wg - 1) / a.app.tokens_per_wg : 0);
       int rc;
       if (timed) {
         KernelTimer tm(dec ? 2 : 0, s);
@@ -649,7 +664,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
-  const Layout L = layout_for(plan, B, dims->head_dim);
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, L.part_end, &w))) return st;
   int region = 0;
@@ -691,7 +706,7 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
     s.kv_len = s.cache_len + s.new_len;
     plan.seqs[b] = s;
   }
-  const Layout L = layout_for(plan, B, dims->head_dim);
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
@@ -791,7 +806,7 @@ int32_t plan_create_impl(const vpk_dims* dims, const vpk_host_index* host, int32
     delete pl;
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
-  pl->L = layout_for(pl->plan, B, dims->head_dim);
+  pl->L = layout_for(pl->plan, B, dims->total_knew, dims->head_dim);
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) {
     delete pl;

@@ -52,44 +52,73 @@ __device__ __forceinline__ uint32_t enc2(uint32_t two_bf16, float inv) {
 
 }  // namespace append_detail
 
-// Store new token t (0 <= t < total_knew) with `nthreads` threads of index
-// `tid`.  A page id outside [0, num_pages) drops the token and raises bit 0 of
-// the device error flag instead of writing out of bounds.
-__device__ __forceinline__ void append_token(const AppendParams& p, int t, int tid, int nthreads) {
+// Store the new tokens of workgroup `wg` (tokens [wg * tokens_per_wg, ...) of
+// the call) with `nthreads` threads of index `tid`.  First each token's
+// destination row (page from block_table, slot from the logical position the
+// plan carries) goes to `dst` in LDS (tokens_per_wg entries), then the
+// threads copy 16-byte chunks, whose sources and destinations are then known
+// up front.  A page id outside [0, num_pages) drops the token and raises bit
+// 0 of the device error flag instead of writing out of bounds.
+__device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int tid, int nthreads,
+                                              int64_t* dst) {
   using namespace append_detail;
-  // sequence of token t: largest b with cu_knew[b] <= t
-  int lo = 0, hi = p.batch;   // invariant: cu_knew[lo] <= t < cu_knew[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.cu_knew[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int pos = p.seqs[b].cache_len + (t - p.cu_knew[b]);
-  const int pi = pos / p.page_size;
-  const int slot = pos - pi * p.page_size;
-  const int page = (pi < p.max_pages) ? p.block_table[static_cast<int64_t>(b) * p.max_pages + pi] : -1;
-  if (page < 0 || page >= p.num_pages) {
-    if (tid == 0) atomicOr(p.err_flag, 1);
-    return;
-  }
-  const int64_t dst_row = (static_cast<int64_t>(page) * p.page_size + slot) * p.row_elems;
-  const int64_t src_row = static_cast<int64_t>(t) * p.row_elems;
-  const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
-  for (int c = tid; c < 2 * chunks; c += nthreads) {
-    const bool is_v = c >= chunks;
-    const int cc = is_v ? c - chunks : c;
-    const uint16_t* src = (is_v ? p.v_new : p.k_new) + src_row + cc * 8;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(src);
-    if (p.fp8) {
-      const float inv = is_v ? p.v_inv_scale : p.k_inv_scale;
-      uint8_t* dst = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
-      u32x2 y;
-      y[0] = enc2(x[0], inv) | (enc2(x[1], inv) << 16);
-      y[1] = enc2(x[2], inv) | (enc2(x[3], inv) << 16);
-      *reinterpret_cast<u32x2*>(dst) = y;
+  const int t0 = wg * p.tokens_per_wg;
+  const int nt = min(p.tokens_per_wg, p.total_knew - t0);
+  for (int i = tid; i < nt; i += nthreads) {
+    const int b = p.tok[2 * (t0 + i)];
+    const int pos = p.tok[2 * (t0 + i) + 1];
+    const int pi = pos / p.page_size;
+    const int slot = pos - pi * p.page_size;
+    const int page = (pi < p.max_pages) ? p.block_table[static_cast<int64_t>(b) * p.max_pages + pi] : -1;
+    if (page < 0 || page >= p.num_pages) {
+      atomicOr(p.err_flag, 1);
+      dst[i] = -1;
     } else {
-      uint16_t* dst = static_cast<uint16_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
-      *reinterpret_cast<u32x4*>(dst) = x;
+      dst[i] = (static_cast<int64_t>(page) * p.page_size + slot) * p.row_elems;
+    }
+  }
+  __syncthreads();
+  const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
+  const int per_tok = 2 * chunks;       // K chunks then V chunks
+  const int total = nt * per_tok;
+  // four chunks per thread at a time: their loads are issued together, then
+  // they are encoded and stored
+  constexpr int kBatch = 4;
+  for (int f0 = tid; f0 < total; f0 += kBatch * nthreads) {
+    u32x4 x[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int f = f0 + k * nthreads;
+      if (f < total) {
+        const int i = f / per_tok;
+        const int c = f - i * per_tok;
+        const bool is_v = c >= chunks;
+        const int cc = is_v ? c - chunks : c;
+        x[k] = *reinterpret_cast<const u32x4*>((is_v ? p.v_new : p.k_new) +
+                                                 static_cast<int64_t>(t0 + i) * p.row_elems + cc * 8);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int f = f0 + k * nthreads;
+      if (f >= total) continue;
+      const int i = f / per_tok;
+      const int c = f - i * per_tok;
+      const int64_t dst_row = dst[i];
+      if (dst_row < 0) continue;
+      const bool is_v = c >= chunks;
+      const int cc = is_v ? c - chunks : c;
+      if (p.fp8) {
+        const float inv = is_v ? p.v_inv_scale : p.k_inv_scale;
+        uint8_t* d = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
+        u32x2 y;
+        y[0] = enc2(x[k][0], inv) | (enc2(x[k][1], inv) << 16);
+        y[1] = enc2(x[k][2], inv) | (enc2(x[k][3], inv) << 16);
+        *reinterpret_cast<u32x2*>(d) = y;
+      } else {
+        uint16_t* d = static_cast<uint16_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
+        *reinterpret_cast<u32x4*>(d) = x[k];
+      }
     }
   }
 }

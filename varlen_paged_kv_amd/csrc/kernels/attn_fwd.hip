@@ -905,7 +905,7 @@ struct Decode : Src<D, FMT, PAGED> {
     const int lg = lane >> 5;   // lane half
     // workgroups past the attention part of the grid store new tokens
     if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
-      append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
+      append_tokens(p.app, blockIdx.x - p.attn_blocks, t, NT, reinterpret_cast<int64_t*>(smem));
       return;
     }
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
@@ -1141,7 +1141,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     const int lg = lane >> 5;
     // workgroups past the attention part of the grid store new tokens
     if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
-      append_token(p.app, blockIdx.x - p.attn_blocks, t, NT);
+      append_tokens(p.app, blockIdx.x - p.attn_blocks, t, NT, reinterpret_cast<int64_t*>(smem));
       return;
     }
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];

@@ -64,17 +64,20 @@ struct MergeGroup {
 
 enum KvFormat : int32_t { kKvBf16 = 0, kKvFp8 = 1 };
 
+// largest number of new tokens one append workgroup stores
+constexpr int kAppendTokensMax = 32;
+
 struct AppendParams {
   const uint16_t* k_new;      // bf16 [Tn, Hkv, D]
   const uint16_t* v_new;
   void* k_cache;
   void* v_cache;
   const int32_t* block_table;
-  const SeqInfo* seqs;
-  const int32_t* cu_knew;     // [B + 1]
+  const int32_t* tok;         // [Tn][2]: sequence and logical position of each new token
   int32_t* err_flag;
   int32_t batch;
   int32_t total_knew;
+  int32_t tokens_per_wg;      // new tokens stored by one workgroup
   int32_t max_pages;
   int32_t num_pages;
   int32_t page_size;
