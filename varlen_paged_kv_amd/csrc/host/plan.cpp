@@ -44,9 +44,13 @@ double block_cost(int32_t nrows, int32_t kv_bytes, bool decode_mode) {
 }
 
 // Fixed cost of one work item (its metadata, page ids, Q rows, the final
-// combine and stores), in the units of block_cost: about 1.6 blocks of a
-// decode-mode item, measured on MI355X.
+// combine and stores), in the units of block_cost, measured on MI355X: about
+// 1.6 units for a decode-mode item; a prefill-mode item (Q load of 256 rows,
+// the first blocks' staging round trip, the output stores) costs about
+// 13,000 cycles against about 3,900 per 9-unit block of 256 rows, i.e. 30
+// units.
 constexpr double kItemCost = 1.6;
+constexpr double kPrefillItemCost = 30.0;
 
 }  // namespace
 
@@ -87,7 +91,8 @@ void build_plan(const PlanInput& in, Plan& out) {
       if (in.causal) kend = std::min<int64_t>(kend, static_cast<int64_t>(t_last) + s.kv_len - s.q_len + 1);
       kend = std::max<int64_t>(kend, 0);
       const int32_t nblk = static_cast<int32_t>((kend + kBlockN - 1) / kBlockN);
-      const double c = kItemCost + nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
+      const double c = (rows <= kWaveRows ? kItemCost : kPrefillItemCost) +
+                       nblk * block_cost(nr, in.kv_bytes, rows <= kWaveRows);
       tiles.push_back(Tile{b, static_cast<int32_t>(r0), nr, 0, static_cast<int32_t>(kend), c, rows <= kWaveRows});
       (rows <= kWaveRows ? total_dec : total_pre) += c * in.hkv;
     }
@@ -179,7 +184,8 @@ void build_plan(const PlanInput& in, Plan& out) {
     for (int32_t s = 0; s < n; ++s) {
       const int32_t b0 = static_cast<int32_t>(static_cast<int64_t>(nblk) * s / n);
       const int32_t b1 = static_cast<int32_t>(static_cast<int64_t>(nblk) * (s + 1) / n);
-      units.push_back(Unit{kItemCost + (b1 - b0) * block_cost(t.nrows, in.kv_bytes, t.dec), ti, s, b0, b1, n, ngroups});
+      units.push_back(Unit{(t.dec ? kItemCost : kPrefillItemCost) + (b1 - b0) * block_cost(t.nrows, in.kv_bytes, t.dec),
+                           ti, s, b0, b1, n, ngroups});
     }
     ++ngroups;
   }
@@ -261,6 +267,7 @@ void build_plan(const PlanInput& in, Plan& out) {
   static thread_local std::vector<int32_t> owner;
   static thread_local std::vector<int32_t> count;
   static thread_local std::vector<int32_t> fill;
+  static thread_local std::vector<int64_t> by_cost;
   out.persistent = false;
   for (Launch* L : {&out.prefill, &out.decode}) {
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
@@ -284,13 +291,18 @@ void build_plan(const PlanInput& in, Plan& out) {
     for (int32_t q = 0; q < nq; ++q) heap.push(Load{0.0, q});
     count.assign(nq, 0);
     owner.resize(nwork);
-    for (int64_t w = 0; w < nwork; ++w) {
-      const double cost = units[order[L->first + w / in.hkv]].cost;
+    // longest first onto the least-loaded queue (LPT); each queue then runs
+    // its work in the launch order above
+    by_cost.resize(nwork);
+    std::iota(by_cost.begin(), by_cost.end(), 0);
+    auto cost_of = [&](int64_t w) { return units[order[L->first + w / in.hkv]].cost; };
+    std::stable_sort(by_cost.begin(), by_cost.end(), [&](int64_t a, int64_t b) { return cost_of(a) > cost_of(b); });
+    for (int64_t w : by_cost) {
       Load l = heap.top();
       heap.pop();
       owner[w] = l.second;
       ++count[l.second];
-      l.first += cost;
+      l.first += cost_of(w);
       heap.push(l);
     }
     for (int32_t q = 0; q < nq; ++q) out.queue_start[q0 + q + 1] = out.queue_start[q0 + q] + count[q];
