@@ -267,7 +267,9 @@ void build_plan(const PlanInput& in, Plan& out) {
   static thread_local std::vector<int32_t> owner;
   static thread_local std::vector<int32_t> count;
   static thread_local std::vector<int32_t> fill;
-  static thread_local std::vector<int64_t> by_cost;
+  static thread_local std::vector<int32_t> by_unit;
+  static thread_local std::vector<double> heap_key;
+  static thread_local std::vector<int32_t> heap_queue;
   out.persistent = false;
   for (Launch* L : {&out.prefill, &out.decode}) {
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
@@ -286,24 +288,45 @@ void build_plan(const PlanInput& in, Plan& out) {
     if (nq == 0) continue;
     const size_t q0 = out.queue_start.size();
     out.queue_start.resize(q0 + nq + 1, 0);
-    using Load = std::pair<double, int32_t>;
-    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-    for (int32_t q = 0; q < nq; ++q) heap.push(Load{0.0, q});
-    count.assign(nq, 0);
-    owner.resize(nwork);
     // longest first onto the least-loaded queue (LPT); each queue then runs
-    // its work in the launch order above
-    by_cost.resize(nwork);
-    std::iota(by_cost.begin(), by_cost.end(), 0);
-    auto cost_of = [&](int64_t w) { return units[order[L->first + w / in.hkv]].cost; };
-    std::stable_sort(by_cost.begin(), by_cost.end(), [&](int64_t a, int64_t b) { return cost_of(a) > cost_of(b); });
-    for (int64_t w : by_cost) {
-      Load l = heap.top();
-      heap.pop();
-      owner[w] = l.second;
-      ++count[l.second];
-      l.first += cost_of(w);
-      heap.push(l);
+    // its work in the launch order above.  Works of one unit (its kv heads)
+    // cost the same, so units are sorted and their works dealt in turn.
+    std::vector<int32_t>& own = owner;
+    std::vector<int32_t>& cnt = count;
+    std::vector<int32_t>& ub = by_unit;
+    std::vector<double>& hk = heap_key;
+    std::vector<int32_t>& hq = heap_queue;
+    cnt.assign(nq, 0);
+    own.resize(nwork);
+    ub.resize(L->count);
+    std::iota(ub.begin(), ub.end(), 0);
+    const int32_t* const ord = order.data() + L->first;
+    const Unit* const un = units.data();
+    std::stable_sort(ub.begin(), ub.end(), [&](int32_t a, int32_t b) { return un[ord[a]].cost > un[ord[b]].cost; });
+    // binary min-heap of (load, queue), ties to the lower queue index
+    hk.assign(nq, 0.0);
+    hq.resize(nq);
+    std::iota(hq.begin(), hq.end(), 0);
+    auto less = [&](int32_t i, int32_t j) { return hk[i] < hk[j] || (hk[i] == hk[j] && hq[i] < hq[j]); };
+    for (const int32_t u : ub) {
+      const double c = un[ord[u]].cost;
+      for (int32_t h = 0; h < in.hkv; ++h) {
+        const int64_t w = static_cast<int64_t>(u) * in.hkv + h;
+        const int32_t q = hq[0];
+        own[w] = q;
+        ++cnt[q];
+        hk[0] += c;
+        for (int32_t i = 0;;) {   // sift the root down
+          const int32_t l = 2 * i + 1, r = l + 1;
+          int32_t m = i;
+          if (l < nq && less(l, m)) m = l;
+          if (r < nq && less(r, m)) m = r;
+          if (m == i) break;
+          std::swap(hk[i], hk[m]);
+          std::swap(hq[i], hq[m]);
+          i = m;
+        }
+      }
     }
     for (int32_t q = 0; q < nq; ++q) out.queue_start[q0 + q + 1] = out.queue_start[q0 + q] + count[q];
     fill.assign(out.queue_start.begin() + q0, out.queue_start.begin() + q0 + nq);
