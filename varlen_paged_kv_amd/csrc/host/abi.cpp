@@ -243,6 +243,10 @@ struct Mirrors {
   const int32_t* cu_kn = nullptr;
   const int32_t* cache_lens = nullptr;
   const int32_t* block_table = nullptr;   // may stay null (no host check)
+  // page-list form: each sequence's own query rows and page-id range
+  const int32_t* q_start = nullptr;       // with q_len instead of cu_q
+  const int32_t* q_len = nullptr;
+  const int32_t* bt_row = nullptr;        // kv_indptr: first page-id index per sequence (B + 1 entries)
   std::vector<int32_t> b1, b2, b3;
 };
 
@@ -370,6 +374,10 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
   in.cu_q = m.cu_q;
   in.cu_kn = m.cu_kn;
   in.cache_lens = m.cache_lens;
+  in.q_start = m.q_start;
+  in.q_len = m.q_len;
+  in.bt_row = m.bt_row;
+  in.max_pages = c.d->max_pages_per_seq;
   in.num_cus = num_cus;
   in.force_splits = static_cast<int32_t>(g_opt.force_splits.load());
   in.persistent = static_cast<int32_t>(g_opt.persistent.load());
@@ -398,17 +406,22 @@ Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D) {
   return L;
 }
 
-// Serialise the plan records into `base` (L.plan_end bytes).  Each new token
-// gets its sequence and its logical position Lc + j, so an append workgroup
-// finds its tokens' slots with one read each.
-void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B, char* base) {
+// Serialise the plan records into `base` (L.plan_end bytes).  New token j of
+// sequence b sits at logical position Lc + j: its record is the block_table
+// index of that position's page id (the sequence's first index + pos / S)
+// and the slot pos % S, so an append workgroup finds its tokens' slots with
+// one read each.
+void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B, int32_t page_size,
+                    char* base) {
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
   if (cu_kn) {
     int32_t* tok = reinterpret_cast<int32_t*>(base + L.tok);
+    const int32_t S = std::max(1, page_size);
     for (int32_t b = 0; b < B; ++b)
       for (int32_t t = cu_kn[b]; t < cu_kn[b + 1]; ++t) {
-        tok[2 * t] = b;
-        tok[2 * t + 1] = p.seqs[b].cache_len + (t - cu_kn[b]);
+        const int32_t pos = p.seqs[b].cache_len + (t - cu_kn[b]);
+        tok[2 * t] = p.seqs[b].bt_row + pos / S;
+        tok[2 * t + 1] = pos % S;
       }
   }
   if (!p.items.empty()) std::memcpy(base + L.items, p.items.data(), sizeof(WorkItem) * p.items.size());
@@ -421,10 +434,10 @@ void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_
 
 // Serialise the plan into the next pinned plan buffer; *index receives it.
 int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B,
-                   int* index) {
+                   int32_t page_size, int* index) {
   int32_t st = take_plan_buffer(w, L.plan_end, index);
   if (st) return st;
-  serialize_plan(p, L, cu_kn, B, w->plan[*index].host);
+  serialize_plan(p, L, cu_kn, B, page_size, w->plan[*index].host);
   return VPK_SUCCESS;
 }
 
@@ -668,7 +681,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, L.part_end, &w))) return st;
   int region = 0;
-  if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
   const Bases bases{w->plan[region].host, w->parts(), w->dev};
   if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
                         out, lse, stream, w, true)))
@@ -704,13 +717,14 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
     s.kn_start = m.cu_kn[b];
     s.cache_len = m.cache_lens[b];
     s.kv_len = s.cache_len + s.new_len;
+    s.bt_row = static_cast<int32_t>(static_cast<int64_t>(b) * dims->max_pages_per_seq);
     plan.seqs[b] = s;
   }
   const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
-  if ((st = write_plan(w, plan, L, m.cu_kn, B, &region))) return st;
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
   if ((st = enqueue_append(append_params(c, w->dev, w->plan[region].host, L, k_new, v_new, k_cache,
                                          v_cache, block_table),
                            stream)))
@@ -820,7 +834,7 @@ int32_t plan_create_impl(const vpk_dims* dims, const vpk_host_index* host, int32
   }
   pl->dev = static_cast<char*>(d);
   std::vector<char> rec(pl->L.plan_end + kFlagBytes, 0);   // head (flag, zeros) then the records
-  serialize_plan(pl->plan, pl->L, m.cu_kn, B, rec.data() + kFlagBytes);
+  serialize_plan(pl->plan, pl->L, m.cu_kn, B, pl->page_size, rec.data() + kFlagBytes);
   if ((e = hipMemcpy(pl->dev, rec.data(), rec.size(), hipMemcpyHostToDevice)) != hipSuccess) {
     (void)hipFree(pl->dev);
     delete pl;

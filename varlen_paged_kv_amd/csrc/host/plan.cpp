@@ -68,8 +68,14 @@ void build_plan(const PlanInput& in, Plan& out) {
   for (int32_t b = 0; b < B; ++b) {
     SeqInfo& s = out.seqs[b];
     s = SeqInfo{};
-    s.q_start = in.cu_q[b];
-    s.q_len = in.cu_q[b + 1] - in.cu_q[b];
+    if (in.q_start) {
+      s.q_start = in.q_start[b];
+      s.q_len = in.q_len[b];
+    } else {
+      s.q_start = in.cu_q[b];
+      s.q_len = in.cu_q[b + 1] - in.cu_q[b];
+    }
+    s.bt_row = in.bt_row ? in.bt_row[b] : static_cast<int32_t>(static_cast<int64_t>(b) * in.max_pages);
     s.new_len = in.has_new ? in.cu_kn[b + 1] - in.cu_kn[b] : 0;
     s.kn_start = in.has_new ? in.cu_kn[b] : 0;
     s.cache_len = (in.has_cache && in.cache_lens) ? in.cache_lens[b] : 0;

@@ -19,9 +19,13 @@ struct PlanInput {
   bool causal = false;
   int32_t page_size = 1;
   int32_t kv_bytes = 2;                 // bytes per cached element (2 bf16, 1 fp8)
-  const int32_t* cu_q = nullptr;        // [B + 1] host
+  const int32_t* cu_q = nullptr;        // [B + 1] host (or null with q_start / q_len)
+  const int32_t* q_start = nullptr;     // [B] host: first query row of each sequence (with q_len)
+  const int32_t* q_len = nullptr;       // [B] host
   const int32_t* cu_kn = nullptr;       // [B + 1] host, or null
   const int32_t* cache_lens = nullptr;  // [B] host, or null
+  const int32_t* bt_row = nullptr;      // [B] host: first page-id index per sequence, or null (b * max_pages)
+  int32_t max_pages = 0;                // row length of a dense block_table
   int32_t num_cus = 256;
   int32_t wg_per_cu = 2;                // resident decode-mode workgroups per CU
   int32_t pre_wg_per_cu = 1;            // resident prefill-mode workgroups per CU

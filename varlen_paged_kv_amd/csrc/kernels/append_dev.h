@@ -54,8 +54,8 @@ __device__ __forceinline__ uint32_t enc2(uint32_t two_bf16, float inv) {
 
 // Store the new tokens of workgroup `wg` (tokens [wg * tokens_per_wg, ...) of
 // the call) with `nthreads` threads of index `tid`.  First each token's
-// destination row (page from block_table, slot from the logical position the
-// plan carries) goes to `dst` in LDS (tokens_per_wg entries), then the
+// destination row (page read from block_table at the index the plan carries,
+// slot from the plan) goes to `dst` in LDS (tokens_per_wg entries), then the
 // threads copy 16-byte chunks, whose sources and destinations are then known
 // up front.  A page id outside [0, num_pages) drops the token and raises bit
 // 0 of the device error flag instead of writing out of bounds.
@@ -65,11 +65,11 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
   const int t0 = wg * p.tokens_per_wg;
   const int nt = min(p.tokens_per_wg, p.total_knew - t0);
   for (int i = tid; i < nt; i += nthreads) {
-    const int b = p.tok[2 * (t0 + i)];
-    const int pos = p.tok[2 * (t0 + i) + 1];
-    const int pi = pos / p.page_size;
-    const int slot = pos - pi * p.page_size;
-    const int page = (pi < p.max_pages) ? p.block_table[static_cast<int64_t>(b) * p.max_pages + pi] : -1;
+    // block_table index of the token's page id (inside its sequence's row:
+    // the host checked the capacity) and the slot in that page
+    const int entry = p.tok[2 * (t0 + i)];
+    const int slot = p.tok[2 * (t0 + i) + 1];
+    const int page = p.block_table[entry];
     if (page < 0 || page >= p.num_pages) {
       atomicOr(p.err_flag, 1);
       dst[i] = -1;

@@ -443,7 +443,7 @@ struct Src {
       if (e.item.key_end > e.item.key_begin) {
         it.first_page = __builtin_amdgcn_readfirstlane(e.item.key_begin / p.page_size);
         const int last_page = (e.item.key_end - 1) / p.page_size;
-        const int32_t* bt = p.block_table + static_cast<int64_t>(e.item.seq) * p.max_pages;
+        const int32_t* bt = p.block_table + e.item.s.bt_row;
         for (int i = t; i <= last_page - it.first_page; i += nt) {
           int pg = bt[it.first_page + i];
           if (pg < 0 || pg >= p.num_pages) {

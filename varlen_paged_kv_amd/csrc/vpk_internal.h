@@ -23,13 +23,14 @@ constexpr int kMaxItemPages = 1024;
 
 // Per-sequence facts taken from the host mirrors (32 bytes).
 struct SeqInfo {
-  int32_t q_start;    // cu_seqlens_q[b]
+  int32_t q_start;    // first query row of the sequence (cu_seqlens_q[b], or its own start)
   int32_t q_len;      // Lq
   int32_t kv_len;     // Lk = Lc + Ln (or Ln without a cache)
   int32_t kn_start;   // cu_seqlens_knew[b] (0 without new K/V)
   int32_t cache_len;  // Lc
   int32_t new_len;    // Ln
-  int32_t pad0, pad1;
+  int32_t bt_row;     // index of the sequence's first page id in block_table (b * max_pages, or its CSR offset)
+  int32_t pad1;
 };
 
 // One unit of attention work (64 bytes): packed rows [row0, row0 + nrows) of
@@ -73,7 +74,7 @@ struct AppendParams {
   void* k_cache;
   void* v_cache;
   const int32_t* block_table;
-  const int32_t* tok;         // [Tn][2]: sequence and logical position of each new token
+  const int32_t* tok;         // [Tn][2]: block_table index of each new token's page id, and its slot
   int32_t* err_flag;
   int32_t batch;
   int32_t total_knew;
