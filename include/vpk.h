@@ -158,6 +158,40 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims,
                               const vpk_host_index* host, void* stream);
 
 /*
+ * The page-list form of the same call.  The POD page's batch API describes
+ * sequences by a page list in CSR form (an offsets array into one array of
+ * page ids) and lets the query rows of a sequence sit anywhere in q/out (its
+ * own start and length instead of cumulative offsets) ("[Refactor] Uniform
+ * PoDAttention API with Horizontal Fusion SMs Schedule", Key Changes 1).
+ */
+typedef struct {
+  const int32_t* q_start;          /* [B]: first row of sequence b in q / out and in lse's row axis */
+  const int32_t* q_len;            /* [B]: Lq; rows of different sequences may not overlap */
+  const int32_t* cu_seqlens_knew;  /* [B + 1], as for attn_varlen_paged_fwd; NULL without new K/V */
+  const int32_t* cache_seqlens;    /* [B] length before the append; NULL without a cache */
+  const int32_t* kv_indptr;        /* [B + 1] non-decreasing: sequence b's page ids are
+                                      kv_indices[kv_indptr[b] .. kv_indptr[b + 1]); NULL without a cache */
+  const int32_t* kv_indices;       /* host copy of kv_indices, or NULL (then page ids are not range-checked
+                                      on the host; see vpk_host_index.block_table) */
+} vpk_host_pages;
+
+/*
+ * attn_varlen_paged_list_fwd -- attn_varlen_paged_fwd with the page lists and
+ * query rows of vpk_host_pages: every length and offset comes from `host`
+ * (required), only kv_indices (device int32 [kv_indptr[B]]) is read on the
+ * device.  dims->total_q is the row count of q / out / lse (rows no sequence
+ * names are left untouched); dims->max_pages_per_seq is not used.  Results
+ * are those of attn_varlen_paged_fwd for a block_table whose row b holds
+ * sequence b's page list.  Errors as for attn_varlen_paged_fwd (overlapping
+ * query rows: VPK_ERROR_INVALID_VALUE; a page list too short for Lc + Ln:
+ * VPK_ERROR_CAPACITY).
+ */
+int32_t attn_varlen_paged_list_fwd(const vpk_dims* dims, const void* q, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, const int32_t* kv_indices, int32_t page_size,
+                                   int32_t causal, float scale, const float* kv_scale, void* out, float* lse,
+                                   const vpk_host_pages* host, void* stream);
+
+/*
  * kv_cache_append -- step 1 alone: store k_new/v_new into the paged cache at
  * positions [Lc, Lc + Ln) of each sequence (same rules and arguments as above).
  * Idempotent: repeating it with the same arguments writes the same bytes.

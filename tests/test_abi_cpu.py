@@ -174,3 +174,42 @@ def test_plan_create_errors_before_the_device():
     lib = _lib.load()
     assert lib.vpk_plan_run(None, None, None, None, None, None, None, 0.1, None, None, None, None) == 1
     assert lib.vpk_plan_destroy(None) == 0
+
+
+def _list_call(dims, hp, *, q=FAKE, k_new=FAKE, v_new=FAKE, kc=FAKE, vc=FAKE, kvi=FAKE, page_size=16,
+               causal=1, scale=0.1, out=FAKE, lse=FAKE):
+    lib = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.attn_varlen_paged_list_fwd(ctypes.byref(dims), vp(q), vp(k_new), vp(v_new), vp(kc), vp(vc), vp(kvi),
+                                        page_size, causal, scale, None, vp(out), vp(lse),
+                                        None if hp is None else ctypes.byref(hp), None)
+    return st, lib.vpk_last_error().decode()
+
+
+def _pages(q_start, q_len, cu_kn=None, cl=None, indptr=None, indices=None):
+    arrs = [None if a is None else np.ascontiguousarray(a, np.int32)
+            for a in (q_start, q_len, cu_kn, cl, indptr, indices)]
+    return _lib.VpkHostPages(*[None if a is None else a.ctypes.data for a in arrs]), arrs
+
+
+def test_page_list_form_errors_before_the_device():
+    """attn_varlen_paged_list_fwd checks its host arrays before any device work."""
+    d = _dims(total_q=10)
+    ok, k0 = _pages([0, 6], [2, 2], [0, 2, 4], [3, 5], [0, 2, 4], [0, 1, 2, 3])
+    assert _list_call(d, None)[0] == 1
+    hp, k1 = _pages([0, 1], [2, 2], [0, 2, 4], [3, 5], [0, 2, 4])          # rows 0-1 and 1-2 overlap
+    st, msg = _list_call(d, hp)
+    assert st == 1 and "share" in msg
+    hp, k2 = _pages([0, 9], [2, 2], [0, 2, 4], [3, 5], [0, 2, 4])          # row 10 is past total_q
+    assert "outside" in _list_call(d, hp)[1]
+    hp, k3 = _pages([0, 6], [2, 2], [0, 2, 4], [3, 5], [0, 2, 1])          # kv_indptr decreases
+    assert "non-decreasing" in _list_call(d, hp)[1]
+    hp, k4 = _pages([0, 6], [2, 2], [0, 2, 4], [31, 5], [0, 2, 4])         # 31 + 2 keys > 2 pages of 16
+    assert _list_call(d, hp)[0] == 3
+    hp, k5 = _pages([0, 6], [2, 2], [0, 2, 4], [3, 5], [0, 2, 4], [0, 1, 99, 3])
+    st, msg = _list_call(d, hp)
+    assert st == 1 and "kv_indices" in msg
+    hp, k6 = _pages([0, 6], [2, 2], [0, 2, 4], None, [0, 2, 4])            # cache without cache_seqlens
+    assert _list_call(d, hp)[0] == 1
+    hp, k7 = _pages([0, 6], [2, 2])                                        # new tokens without cu_seqlens_knew
+    assert _list_call(d, hp, kc=None, vc=None, kvi=None)[0] == 1

@@ -20,9 +20,9 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import VpkDims, VpkHostIndex
+from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 
-__all__ = ["attn_varlen_paged_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
+__all__ = ["attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE"]
 
@@ -150,6 +150,66 @@ def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
                                    _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens),
                                    int(page_size), int(bool(causal)), float(scale), ks,
                                    _ptr(out), _ptr(lse), ctypes.byref(hi), _stream_handle(stream))
+    del keep
+    _check(st)
+    return out, lse
+
+
+def attn_varlen_paged_list_fwd(q: torch.Tensor, q_start, q_len, k_new=None, v_new=None, cu_seqlens_knew=None,
+                               k_cache=None, v_cache=None, kv_indptr=None, kv_indices=None, cache_seqlens=None,
+                               page_size: int = 0, causal: bool = True, scale: Optional[float] = None,
+                               kv_scale=None, *, out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                               kv_indices_host=None, stream=None):
+    """The page-list form: sequence b's query rows are q[q_start[b] : q_start[b] + q_len[b]]
+    (anywhere in q, not overlapping), its page ids kv_indices[kv_indptr[b] : kv_indptr[b + 1]].
+
+    q_start, q_len, cu_seqlens_knew, cache_seqlens and kv_indptr are host arrays
+    (numpy or CPU tensors); kv_indices is a device int32 tensor (kv_indices_host
+    an optional host copy for page-id range checks).  ``out`` rows that no
+    sequence names are left as they are (a new ``out`` starts as zeros).
+    Returns (out [Tq, Hq, D] bf16, lse [Hq, Tq] fp32 or None).
+    """
+    lib = _lib.load()
+    q = _dev(q, "q", _BF16)
+    k_new = _dev(k_new, "k_new", _BF16)
+    v_new = _dev(v_new, "v_new", _BF16)
+    fp8 = k_cache is not None and k_cache.dtype in _FP8
+    k_cache = _dev(k_cache, "k_cache", _FP8 if fp8 else _BF16)
+    v_cache = _dev(v_cache, "v_cache", _FP8 if fp8 else _BF16)
+    kv_indices = _dev(kv_indices, "kv_indices", _I32)
+    if q.dim() != 3:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "q must be [total_q, num_q_heads, head_dim]")
+    Tq, Hq, D = q.shape
+    qs, ql = _host_i32(q_start), _host_i32(q_len)
+    B = qs.size
+    Hkv = (k_new if k_new is not None else k_cache).shape[-2]
+    Tn = 0 if k_new is None else k_new.shape[0]
+    P = 0 if k_cache is None else k_cache.shape[0]
+    for name, t, shp in (("k_new", k_new, (Tn, Hkv, D)), ("v_new", v_new, (Tn, Hkv, D)),
+                         ("k_cache", k_cache, (P, page_size, Hkv, D)),
+                         ("v_cache", v_cache, (P, page_size, Hkv, D))):
+        if t is not None and tuple(t.shape) != shp:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.zeros_like(q)
+    if lse is None and return_lse:
+        lse = torch.full((Hq, Tq), float("nan"), dtype=torch.float32, device=q.device)
+    dims = VpkDims(B, Tq, Tn, Hq, Hkv, D, P, 0, _lib.VPK_DTYPE_FP8_E4M3FN if fp8 else _lib.VPK_DTYPE_BF16)
+    ks = None
+    if fp8:
+        if kv_scale is None:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache")
+        ks = (ctypes.c_float * 2)(float(kv_scale[0]), float(kv_scale[1]))
+    keep = [qs, ql, _host_i32(cu_seqlens_knew), _host_i32(cache_seqlens), _host_i32(kv_indptr),
+            _host_i32(kv_indices_host)]
+    hp = VpkHostPages(*[None if a is None else a.ctypes.data for a in keep])
+    st = lib.attn_varlen_paged_list_fwd(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(kv_indices), int(page_size), int(bool(causal)),
+                                        float(scale), ks, _ptr(out), _ptr(lse), ctypes.byref(hp),
+                                        _stream_handle(stream))
     del keep
     _check(st)
     return out, lse

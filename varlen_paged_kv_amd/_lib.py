@@ -27,8 +27,13 @@ EXPORTS = (
     "attn_varlen_paged_fwd", "kv_cache_append", "vpk_last_error", "vpk_abi_version",
     "vpk_set_option", "vpk_timing_enable", "vpk_timing_reset", "vpk_timing_read",
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
-    "vpk_plan_destroy",
+    "vpk_plan_destroy", "attn_varlen_paged_list_fwd",
 )
+
+
+class VpkHostPages(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q_start", "q_len", "cu_seqlens_knew", "cache_seqlens",
+                                                "kv_indptr", "kv_indices")]
 
 
 class VpkDims(ctypes.Structure):
@@ -92,6 +97,9 @@ def load() -> ctypes.CDLL:
     lib.vpk_plan_debug.restype = i32
     lib.vpk_plan_debug.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, i32,
                                    P(i32), i32, P(i32), P(i32)]
+    lib.attn_varlen_paged_list_fwd.restype = i32
+    lib.attn_varlen_paged_list_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, i32, i32, f32, P(f32), vp, vp,
+                                               P(VpkHostPages), vp]
     lib.vpk_plan_create.restype = i32
     lib.vpk_plan_create.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, P(vp)]
     lib.vpk_plan_run.restype = i32

@@ -3,6 +3,7 @@
 // vpk_status plus a thread-local message.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -479,6 +480,38 @@ int32_t check_ptr(const void* p, size_t a, const char* name) {
   return VPK_SUCCESS;
 }
 
+// Pointer checks shared by a direct call and a prepared plan's run.
+int32_t check_run_pointers(const Call& c, const void* q, const void* k_new, const void* v_new,
+                           const void* k_cache, const void* v_cache, const int32_t* block_table,
+                           float scale, const void* out, const float* lse) {
+  const vpk_dims* dims = c.d;
+  int32_t st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite and > 0");
+  if (c.has_new && (dims->total_knew > 0 || k_new || v_new)) {
+    if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
+  }
+  if (!c.has_new && (k_new || v_new)) return fail(VPK_ERROR_INVALID_VALUE, "without new tokens k_new/v_new must be NULL");
+  if (c.has_cache) {
+    if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
+    if ((st = check_ptr(block_table, 4, "block_table"))) return st;
+  } else if (k_cache || v_cache) {
+    return fail(VPK_ERROR_INVALID_VALUE, "without a cache k_cache/v_cache must be NULL");
+  }
+  if (c.fp8) {
+    if (!c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache");
+    for (int i = 0; i < 2; ++i)
+      if (!std::isfinite(c.kv_scale[i]) || !(c.kv_scale[i] > 0.f))
+        return fail(VPK_ERROR_INVALID_VALUE, "kv_scale entries must be finite and > 0");
+  } else if (c.kv_scale && c.has_cache) {
+    return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
+  }
+  if (dims->total_q > 0) {
+    if ((st = check_ptr(q, 16, "q")) || (st = check_ptr(out, 16, "out"))) return st;
+    if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
+  }
+  return VPK_SUCCESS;
+}
+
 // Where a call's device-side data lives: the plan records (pinned host
 // memory for a direct call, device memory for a prepared plan), the split
 // partials, and the head with the error flag and the zero rows.
@@ -622,6 +655,33 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
   return VPK_SUCCESS;
 }
 
+// Plan a validated call and enqueue it on `stream` (direct calls).
+int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const void* q, const void* k_new,
+                         const void* v_new, void* k_cache, void* v_cache, const int32_t* block_table, float scale,
+                         void* out, float* lse, hipStream_t stream) {
+  const vpk_dims* dims = c.d;
+  const int32_t B = dims->batch;
+  int32_t st;
+  PlanInput in;
+  fill_plan_input(c, m, causal, device_cus(), in);
+  Plan plan;
+  try {
+    vpk::build_plan(in, plan);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
+  }
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
+  Workspace* w = nullptr;
+  if ((st = get_workspace(stream, L.part_end, &w))) return st;
+  int region = 0;
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
+  const Bases bases{w->plan[region].host, w->parts(), w->dev};
+  if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
+                        out, lse, stream, w, true)))
+    return st;
+  return release_plan_buffer(w, stream, region);
+}
+
 int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
                   const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
                   void* k_cache, void* v_cache, const int32_t* block_table,
@@ -668,25 +728,97 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   Mirrors m;
   if ((st = get_mirrors(c, cu_seqlens_q, cu_seqlens_knew, cache_seqlens, host, stream, true, m))) return st;
   if ((st = check_contents(c, m, true))) return st;
+  return plan_and_enqueue(c, m, causal, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse, stream);
+}
 
-  PlanInput in;
-  fill_plan_input(c, m, causal, device_cus(), in);
-  Plan plan;
-  try {
-    vpk::build_plan(in, plan);
-  } catch (const std::bad_alloc&) {
-    return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
+// The page-list form: each sequence's query rows [q_start, q_start + q_len)
+// and page ids kv_indices[kv_indptr[b], kv_indptr[b + 1]); every index array
+// is read from the host copies, kv_indices also on the device.
+int32_t attn_list_impl(const vpk_dims* dims, const void* q, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const int32_t* kv_indices, int32_t page_size,
+                       int32_t causal, float scale, const float* kv_scale, void* out, float* lse,
+                       const vpk_host_pages* host, void* stream_v) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
+  if (!host) return fail(VPK_ERROR_INVALID_VALUE, "host is NULL: the page-list form needs the host index arrays");
+  const bool has_new = k_new != nullptr || v_new != nullptr || host->cu_seqlens_knew != nullptr;
+  const bool has_cache = k_cache != nullptr || v_cache != nullptr;
+  if (has_cache && (!host->cache_seqlens || !host->kv_indptr))
+    return fail(VPK_ERROR_INVALID_VALUE, "cache_seqlens and kv_indptr are required with a cache");
+  // the dense row length is not used here; the longest page list stands in for
+  // it in the slot-index range check
+  vpk_dims d = *dims;
+  d.max_pages_per_seq = 0;
+  if (has_cache) {
+    if (dims->batch < 0) return fail(VPK_ERROR_INVALID_VALUE, "negative batch or length");
+    for (int32_t b = 0; b < dims->batch; ++b) {
+      const int64_t n = static_cast<int64_t>(host->kv_indptr[b + 1]) - host->kv_indptr[b];
+      if (n < 0) return fail(VPK_ERROR_INVALID_VALUE, "kv_indptr must be non-decreasing");
+      d.max_pages_per_seq = static_cast<int32_t>(std::max<int64_t>(d.max_pages_per_seq, n));
+    }
+    d.max_pages_per_seq = std::max(d.max_pages_per_seq, 1);
   }
-  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
-  Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.part_end, &w))) return st;
-  int region = 0;
-  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
-  const Bases bases{w->plan[region].host, w->parts(), w->dev};
-  if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
-                        out, lse, stream, w, true)))
-    return st;
-  return release_plan_buffer(w, stream, region);
+  dims = &d;
+  Call c{dims, has_new, has_cache, dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN && has_cache, page_size, kv_scale};
+  int32_t st = check_dims(c);
+  if (st != VPK_SUCCESS) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_new and v_new must both be given or both be NULL");
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_cache and v_cache must both be given or both be NULL");
+  if (!has_new && !has_cache) return fail(VPK_ERROR_INVALID_VALUE, "no keys: give k_new/v_new, a cache, or both");
+  if (causal != 0 && causal != 1) return fail(VPK_ERROR_INVALID_VALUE, "causal must be 0 or 1");
+  if (!has_new && dims->total_knew != 0) return fail(VPK_ERROR_INVALID_VALUE, "total_knew must be 0 without k_new");
+  if (!has_cache && dims->num_pages != 0) return fail(VPK_ERROR_INVALID_VALUE, "num_pages must be 0 without a cache");
+  if ((st = check_run_pointers(c, q, k_new, v_new, k_cache, v_cache, kv_indices, scale, out, lse))) return st;
+  const int32_t B = dims->batch;
+  if (!host->q_start || !host->q_len) return fail(VPK_ERROR_INVALID_VALUE, "q_start and q_len are required");
+  if (has_new && !host->cu_seqlens_knew) return fail(VPK_ERROR_INVALID_VALUE, "cu_seqlens_knew is NULL while k_new is given");
+  if (B == 0) return VPK_SUCCESS;
+  // query rows: inside [0, total_q), no two sequences sharing a row
+  std::vector<std::pair<int32_t, int32_t>> spans;
+  spans.reserve(B);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t a = host->q_start[b], n = host->q_len[b];
+    if (a < 0 || n < 0 || a + n > dims->total_q)
+      return fail(VPK_ERROR_INVALID_VALUE, "sequence " + std::to_string(b) + ": query rows outside [0, total_q)");
+    if (n > 0) spans.emplace_back(static_cast<int32_t>(a), static_cast<int32_t>(a + n));
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].second) return fail(VPK_ERROR_INVALID_VALUE, "two sequences share query rows");
+  Mirrors m;
+  m.q_start = host->q_start;
+  m.q_len = host->q_len;
+  m.cu_kn = has_new ? host->cu_seqlens_knew : nullptr;
+  if (has_new && (st = check_cu(m.cu_kn, B, dims->total_knew, "cu_seqlens_knew")) != VPK_SUCCESS) return st;
+  std::vector<int32_t> zero_rows;
+  if (has_cache) {
+    const int32_t* ip = host->kv_indptr;
+    if (ip[0] < 0) return fail(VPK_ERROR_INVALID_VALUE, "kv_indptr[0] must be >= 0");
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t lc = host->cache_seqlens[b];
+      if (lc < 0) return fail(VPK_ERROR_INVALID_VALUE, "cache_seqlens must be >= 0");
+      const int64_t lk = lc + (has_new ? m.cu_kn[b + 1] - m.cu_kn[b] : 0);
+      const int64_t cap = static_cast<int64_t>(ip[b + 1] - ip[b]) * page_size;
+      if (lk > cap)
+        return fail(VPK_ERROR_CAPACITY, "sequence " + std::to_string(b) + " needs " + std::to_string(lk) +
+                                            " slots, its page list holds " + std::to_string(cap));
+      if (host->kv_indices) {
+        const int64_t np = (lk + page_size - 1) / page_size;
+        for (int64_t i = 0; i < np; ++i) {
+          const int32_t pg = host->kv_indices[ip[b] + i];
+          if (pg < 0 || pg >= dims->num_pages)
+            return fail(VPK_ERROR_INVALID_VALUE, "kv_indices[" + std::to_string(ip[b] + i) + "] = " +
+                                                     std::to_string(pg) + " is outside [0, num_pages)");
+        }
+      }
+    }
+    m.cache_lens = host->cache_seqlens;
+    m.bt_row = ip;
+  } else {
+    zero_rows.assign(B + 1, 0);
+    m.bt_row = zero_rows.data();
+  }
+  return plan_and_enqueue(c, m, causal, q, k_new, v_new, k_cache, v_cache, kv_indices, scale, out, lse, stream);
 }
 
 int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
@@ -730,38 +862,6 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
                            stream)))
     return st;
   return release_plan_buffer(w, stream, region);
-}
-
-// Pointer checks shared by a direct call and a prepared plan's run.
-int32_t check_run_pointers(const Call& c, const void* q, const void* k_new, const void* v_new,
-                           const void* k_cache, const void* v_cache, const int32_t* block_table,
-                           float scale, const void* out, const float* lse) {
-  const vpk_dims* dims = c.d;
-  int32_t st;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(VPK_ERROR_INVALID_VALUE, "scale must be finite and > 0");
-  if (c.has_new && (dims->total_knew > 0 || k_new || v_new)) {
-    if ((st = check_ptr(k_new, 16, "k_new")) || (st = check_ptr(v_new, 16, "v_new"))) return st;
-  }
-  if (!c.has_new && (k_new || v_new)) return fail(VPK_ERROR_INVALID_VALUE, "the plan has no new tokens: k_new/v_new must be NULL");
-  if (c.has_cache) {
-    if ((st = check_ptr(k_cache, 16, "k_cache")) || (st = check_ptr(v_cache, 16, "v_cache"))) return st;
-    if ((st = check_ptr(block_table, 4, "block_table"))) return st;
-  } else if (k_cache || v_cache) {
-    return fail(VPK_ERROR_INVALID_VALUE, "the plan has no cache: k_cache/v_cache must be NULL");
-  }
-  if (c.fp8) {
-    if (!c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache");
-    for (int i = 0; i < 2; ++i)
-      if (!std::isfinite(c.kv_scale[i]) || !(c.kv_scale[i] > 0.f))
-        return fail(VPK_ERROR_INVALID_VALUE, "kv_scale entries must be finite and > 0");
-  } else if (c.kv_scale && c.has_cache) {
-    return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
-  }
-  if (dims->total_q > 0) {
-    if ((st = check_ptr(q, 16, "q")) || (st = check_ptr(out, 16, "out"))) return st;
-    if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
-  }
-  return VPK_SUCCESS;
 }
 
 }  // namespace
@@ -924,6 +1024,21 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims, const void* q, const int32_t
     return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache,
                      block_table, cache_seqlens, page_size, causal, scale, kv_scale, out, lse,
                      host, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
+int32_t attn_varlen_paged_list_fwd(const vpk_dims* dims, const void* q, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, const int32_t* kv_indices, int32_t page_size,
+                                   int32_t causal, float scale, const float* kv_scale, void* out, float* lse,
+                                   const vpk_host_pages* host, void* stream) {
+  try {
+    g_err.clear();
+    return attn_list_impl(dims, q, k_new, v_new, k_cache, v_cache, kv_indices, page_size, causal, scale,
+                          kv_scale, out, lse, host, stream);
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
   } catch (...) {
