@@ -14,7 +14,10 @@ It computes, plainly and slowly, in float64 (numpy):
     query head, with grouped-query heads and bottom-right causal masking --
     ``attend`` / ``attend_rows``;
   * the associative LSE merge of partial results over a split of the key
-    range -- ``merge_partials``.
+    range -- ``merge_partials``;
+  * rotary position embedding of the query rows and the new key rows before
+    the append (optional) -- ``rope.positions`` / ``rope.rotate_bf16`` and
+    ``run_call(rope=...)``.
 
 Pages this follows (cited by title and section):
   * "Add flash_attn_varlen_func_with_kvcache" (flash-attention PR), sections
@@ -37,6 +40,7 @@ mathematics or by library routines (see each function's docstring).
 from .formats import (  # noqa: F401
     bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode, e4m3fn_value_table,
 )
+from . import rope  # noqa: F401
 from .attention import (  # noqa: F401
     append, attend, attend_rows, depage, merge_partials, run_call, run_workload, sequence_kv,
 )

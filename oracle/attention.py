@@ -40,6 +40,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
+from . import rope as _rope
 from .formats import bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode
 
 
@@ -204,13 +205,24 @@ def merge_partials(parts):
 def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k_cache=None,
              v_cache=None, block_table=None, cache_seqlens=None, page_size=0, causal=True,
              scale=None, kv_scale=None, cache_dtype=None, Hkv=None, q_dtype="bf16",
-             new_dtype="bf16", seqs: Optional[Sequence[int]] = None):
+             new_dtype="bf16", seqs: Optional[Sequence[int]] = None, rope=None):
     """One whole call: append, then attention for every sequence.
 
     Returns dict(out [Tq, Hq, D], lse [Hq, Tq], k_cache, v_cache) with float64
     outputs and the caches as stored after the append.  ``seqs`` restricts the
-    attention to some sequences (rows of the others stay 0 / -inf).
+    attention to some sequences (rows of the others stay 0 / -inf).  ``rope``
+    (dict with cos, sin, rotary_dim, interleaved) first turns the query rows
+    and the new key rows by their positions (``oracle.rope``); values and the
+    cached rows are not turned.
     """
+    if rope is not None:
+        if q_dtype != "bf16" or new_dtype != "bf16":
+            raise ValueError("rotary embedding is defined here for bf16 rows")
+        qpos, kpos = _rope.positions(cu_seqlens_q, cu_seqlens_knew, cache_seqlens)
+        args = (rope["cos"], rope["sin"], int(rope["rotary_dim"]), bool(rope["interleaved"]))
+        q = _rope.rotate_bf16(q, qpos, *args)
+        if k_new is not None:
+            k_new = _rope.rotate_bf16(k_new, kpos, *args)
     Q = _decode(q, q_dtype)
     Tq, Hq, D = Q.shape
     if scale is None:

@@ -123,6 +123,19 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
+def rope_tables(max_positions: int, rotary_dim: int, base: float = 10000.0):
+    """Angle tables for rotary embedding: (cos, sin), float32 [max_positions, rotary_dim / 2].
+
+    Entry [m, i] is cos / sin of m * base ** (-2 i / rotary_dim), computed in
+    float64 and rounded once to float32.  This is a caller-side input (like a
+    weight): neither the oracle nor the kernels compute the angles.
+    """
+    half = rotary_dim // 2
+    theta = np.float64(base) ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_positions, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def _draw_lengths(name: str, rng: np.random.Generator):
     """Return (q_lens, new_lens, cache_lens) as int64 arrays."""
     if name == "tiny":
