@@ -158,6 +158,55 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims,
                               const vpk_host_index* host, void* stream);
 
 /*
+ * Rotary position embedding applied by attn_varlen_paged_rope_fwd.  The
+ * TransformerEngine KV-cache page ("Add KV cache for paged/non-paged
+ * attention", Description) names RoPE for inference as the step that comes
+ * with the cache path without defining it; the rotation here is the published
+ * one (Su et al., "RoFormer", section 3.4): coordinates in pairs (a, b), pair
+ * i of a row at position m turned by the angle m * theta_i:
+ *   a' = a cos - b sin,  b' = a sin + b cos.
+ *   cos, sin        device float32 [max_positions, rotary_dim / 2], 16-byte
+ *                   aligned: entry [m, i] for position m, pair i (the caller's
+ *                   angles; any base or scaling).  Borrowed, read only.
+ *   max_positions   rows of the tables.
+ *   rotary_dim      turned coordinates [0, rotary_dim): a multiple of 16 in
+ *                   [16, head_dim]; later coordinates are copied.
+ *   interleaved     0: pair i is (i, i + rotary_dim / 2); 1: pair i is (2i, 2i + 1).
+ */
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int32_t max_positions;
+  int32_t rotary_dim;
+  int32_t interleaved;
+} vpk_rope;
+
+/*
+ * attn_varlen_paged_rope_fwd -- attn_varlen_paged_fwd with the query rows and
+ * the new key rows turned by vpk_rope first (values are not turned).  New
+ * token j of a sequence sits at position Lc + j (the slot it is appended to),
+ * query row i at Lk - Lq + i (the key its end-aligned causal bound stops at),
+ * so a decode row over a cache of Lk keys sits at Lk - 1.  The turned rows
+ * are bf16: each product and the difference / sum rounded to float32, then
+ * round to nearest even; the cache stores the turned keys.  q and k_new are
+ * not modified (the turned copies live in library workspace).
+ * Extra errors: VPK_ERROR_INVALID_VALUE when rope is NULL or its fields break
+ * the rules above, when a sequence has more query rows than keys, or when a
+ * position reaches max_positions.  Other arguments and errors as for
+ * attn_varlen_paged_fwd.
+ */
+int32_t attn_varlen_paged_rope_fwd(const vpk_dims* dims,
+                                   const void* q, const int32_t* cu_seqlens_q,
+                                   const void* k_new, const void* v_new,
+                                   const int32_t* cu_seqlens_knew,
+                                   void* k_cache, void* v_cache,
+                                   const int32_t* block_table, const int32_t* cache_seqlens,
+                                   int32_t page_size, int32_t causal, float scale,
+                                   const float* kv_scale, const vpk_rope* rope,
+                                   void* out, float* lse,
+                                   const vpk_host_index* host, void* stream);
+
+/*
  * The page-list form of the same call.  The POD page's batch API describes
  * sequences by a page list in CSR form (an offsets array into one array of
  * page ids) and lets the query rows of a sequence sit anywhere in q/out (its
@@ -291,7 +340,8 @@ int32_t vpk_set_option(const char* name, int64_t value);
  *           1 = append launched on its own (fp8 cache, persistent schedule,
  *               or kv_cache_append),
  *           2 = attention grid of decode-mode items (likewise),
- *           3 = LSE merge of split parts.
+ *           3 = LSE merge of split parts,
+ *           4 = rotary embedding of q / k_new (attn_varlen_paged_rope_fwd).
  */
 int32_t vpk_timing_enable(int32_t enable);
 int32_t vpk_timing_reset(void);

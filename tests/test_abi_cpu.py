@@ -213,3 +213,38 @@ def test_page_list_form_errors_before_the_device():
     assert _list_call(d, hp)[0] == 1
     hp, k7 = _pages([0, 6], [2, 2])                                        # new tokens without cu_seqlens_knew
     assert _list_call(d, hp, kc=None, vc=None, kvi=None)[0] == 1
+
+
+def test_rope_errors_before_the_device():
+    lib = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(dims, rope, host):
+        st = lib.attn_varlen_paged_rope_fwd(ctypes.byref(dims), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                            vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 16, 1, 0.1, None,
+                                            None if rope is None else ctypes.byref(rope), vp(FAKE), vp(FAKE),
+                                            ctypes.byref(host), None)
+        return st, lib.vpk_last_error().decode()
+
+    def rope(**kw):
+        r = dict(cos=FAKE, sin=FAKE, max_positions=64, rotary_dim=128, interleaved=0)
+        r.update(kw)
+        return _lib.VpkRope(**r)
+
+    d = _dims()
+    hi, k = _host([0, 2, 4], [0, 2, 4], [3, 5])
+    assert call(d, None, hi) == (1, "rope is NULL")
+    for kw, frag in ((dict(rotary_dim=120), "rotary_dim"), (dict(rotary_dim=144), "rotary_dim"),
+                     (dict(rotary_dim=0), "rotary_dim"), (dict(interleaved=2), "interleaved"),
+                     (dict(max_positions=0), "max_positions"), (dict(cos=None), "rope->cos"),
+                     (dict(sin=FAKE + 4), "rope->sin")):
+        st, msg = call(d, rope(**kw), hi)
+        assert st == 1 and frag in msg, (kw, msg)
+    # positions: sequence 1 reaches Lc + Ln - 1 = 6; with 6 table rows that is past the end
+    st, msg = call(d, rope(max_positions=6), hi)
+    assert st == 1 and "sequence 1 reaches position 6" in msg
+    # a sequence with more query rows than keys has no position for its first rows
+    d2 = _dims(total_knew=2)
+    hi, k = _host([0, 3, 4], [0, 1, 2], [1, 5])
+    st, msg = call(d2, rope(), hi)
+    assert st == 1 and "sequence 0" in msg and "query rows than keys" in msg

@@ -105,6 +105,47 @@ def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     read back from the device by the library (a blocking copy).
     Returns (out [Tq, Hq, D] bf16, lse [Hq, Tq] fp32 or None).
     """
+    return _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                       cache_seqlens, page_size, causal, scale, kv_scale, out, lse, return_lse, host_index,
+                       stream, None)
+
+
+def attn_varlen_paged_rope_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                               k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                               cu_seqlens_knew: Optional[torch.Tensor] = None,
+                               k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
+                               block_table: Optional[torch.Tensor] = None,
+                               cache_seqlens: Optional[torch.Tensor] = None,
+                               page_size: int = 0, causal: bool = True, scale: Optional[float] = None,
+                               kv_scale: Optional[Sequence[float]] = None, *,
+                               rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                               rotary_dim: Optional[int] = None, interleaved: bool = False,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               return_lse: bool = True, host_index: Optional[dict] = None,
+                               stream=None):
+    """attn_varlen_paged_fwd with the query rows and new key rows turned by
+    rotary embedding first (new token j at Lc + j, query row i at Lk - Lq + i).
+
+    rope_cos / rope_sin: device float32 [max_positions, rotary_dim / 2];
+    rotary_dim defaults to twice their width.  q and k_new are not modified;
+    the cache stores the turned keys.
+    """
+    rope_cos = _dev(rope_cos, "rope_cos", (torch.float32,))
+    rope_sin = _dev(rope_sin, "rope_sin", (torch.float32,))
+    if rope_cos.dim() != 2 or tuple(rope_sin.shape) != tuple(rope_cos.shape):
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "rope_cos / rope_sin must both be [max_positions, rotary_dim / 2]")
+    if rotary_dim is None:
+        rotary_dim = 2 * rope_cos.shape[1]
+    if 2 * rope_cos.shape[1] != rotary_dim:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "rope tables must have rotary_dim / 2 columns")
+    rope = _lib.VpkRope(_ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], int(rotary_dim), int(bool(interleaved)))
+    return _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                       cache_seqlens, page_size, causal, scale, kv_scale, out, lse, return_lse, host_index,
+                       stream, (rope, rope_cos, rope_sin))
+
+
+def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table, cache_seqlens,
+                page_size, causal, scale, kv_scale, out, lse, return_lse, host_index, stream, rope):
     lib = _lib.load()
     q = _dev(q, "q", _BF16)
     cu_seqlens_q = _dev(cu_seqlens_q, "cu_seqlens_q", _I32)
@@ -145,11 +186,14 @@ def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     h = host_index or {}
     hi, keep = _host_index(h.get("cu_seqlens_q"), h.get("cu_seqlens_knew"),
                            h.get("cache_seqlens"), h.get("block_table"))
-    st = lib.attn_varlen_paged_fwd(ctypes.byref(dims), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_new),
-                                   _ptr(v_new), _ptr(cu_seqlens_knew), _ptr(k_cache),
-                                   _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens),
-                                   int(page_size), int(bool(causal)), float(scale), ks,
-                                   _ptr(out), _ptr(lse), ctypes.byref(hi), _stream_handle(stream))
+    args = (ctypes.byref(dims), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_knew),
+            _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens), int(page_size),
+            int(bool(causal)), float(scale), ks)
+    tail = (_ptr(out), _ptr(lse), ctypes.byref(hi), _stream_handle(stream))
+    if rope is None:
+        st = lib.attn_varlen_paged_fwd(*args, *tail)
+    else:
+        st = lib.attn_varlen_paged_rope_fwd(*args, ctypes.byref(rope[0]), *tail)
     del keep
     _check(st)
     return out, lse

@@ -27,7 +27,7 @@ EXPORTS = (
     "attn_varlen_paged_fwd", "kv_cache_append", "vpk_last_error", "vpk_abi_version",
     "vpk_set_option", "vpk_timing_enable", "vpk_timing_reset", "vpk_timing_read",
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
-    "vpk_plan_destroy", "attn_varlen_paged_list_fwd",
+    "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
 )
 
 
@@ -48,6 +48,11 @@ class VpkDims(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("kv_cache_dtype", ctypes.c_int32),
     ]
+
+
+class VpkRope(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("max_positions", ctypes.c_int32),
+                ("rotary_dim", ctypes.c_int32), ("interleaved", ctypes.c_int32)]
 
 
 class VpkHostIndex(ctypes.Structure):
@@ -97,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.vpk_plan_debug.restype = i32
     lib.vpk_plan_debug.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, i32,
                                    P(i32), i32, P(i32), P(i32)]
+    lib.attn_varlen_paged_rope_fwd.restype = i32
+    lib.attn_varlen_paged_rope_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32,
+                                               P(f32), P(VpkRope), vp, vp, P(VpkHostIndex), vp]
     lib.attn_varlen_paged_list_fwd.restype = i32
     lib.attn_varlen_paged_list_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, i32, i32, f32, P(f32), vp, vp,
                                                P(VpkHostPages), vp]

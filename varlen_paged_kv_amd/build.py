@@ -25,6 +25,7 @@ SOURCES = [
     "kernels/attn_fwd.hip",
     "kernels/append.hip",
     "kernels/merge.hip",
+    "kernels/rope.hip",
     "host/plan.cpp",
     "host/abi.cpp",
 ]

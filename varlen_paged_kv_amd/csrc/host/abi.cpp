@@ -58,9 +58,9 @@ std::mutex g_tmu;
 std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_tpending;
 std::vector<hipEvent_t> g_tfree;
-constexpr int kTimedKernels = 4;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge
-double g_tms[kTimedKernels] = {0, 0, 0, 0};
-int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0};
+constexpr int kTimedKernels = 5;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge, 4 rotary embedding
+double g_tms[kTimedKernels] = {0, 0, 0, 0, 0};
+int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0, 0};
 
 hipEvent_t take_event() {
   if (!g_tfree.empty()) {
@@ -389,10 +389,12 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
 //   [seqs][new tokens: sequence, position][units][merge groups][queue starts][queue work]
 // Partials area (device memory): [part_o fp32 rows x D][part_lse fp32 rows]
 struct Layout {
-  size_t seqs, tok, items, groups, queues, work, plan_end, part_o, part_lse, part_end;
+  size_t seqs, tok, items, groups, queues, work, qpos, kpos, plan_end, part_o, part_lse, rot_q, rot_k, part_end;
 };
 
-Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D) {
+// `rope`: the call turns q and k_new first; their positions go into the plan
+// and the turned copies into device memory after the split partials.
+Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dims* rope = nullptr) {
   Layout L;
   L.seqs = 0;
   L.tok = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
@@ -400,10 +402,16 @@ Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D) {
   L.groups = align_up(L.items + sizeof(WorkItem) * p.items.size(), 64);
   L.queues = align_up(L.groups + sizeof(MergeGroup) * p.groups.size(), 64);
   L.work = align_up(L.queues + sizeof(int32_t) * p.queue_start.size(), 64);
-  L.plan_end = align_up(L.work + sizeof(int32_t) * p.queue_work.size(), 256);
+  L.qpos = align_up(L.work + sizeof(int32_t) * p.queue_work.size(), 64);
+  const size_t tq = rope ? static_cast<size_t>(rope->total_q) : 0, tn = rope ? static_cast<size_t>(Tn) : 0;
+  L.kpos = align_up(L.qpos + sizeof(int32_t) * tq, 64);
+  L.plan_end = align_up(L.kpos + sizeof(int32_t) * tn, 256);
   L.part_o = 0;
   L.part_lse = align_up(sizeof(float) * D * static_cast<size_t>(p.part_rows), 256);
-  L.part_end = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
+  L.rot_q = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
+  const size_t hq = rope ? static_cast<size_t>(rope->num_q_heads) : 0, hkv = rope ? static_cast<size_t>(rope->num_kv_heads) : 0;
+  L.rot_k = align_up(L.rot_q + 2 * tq * hq * D, 256);
+  L.part_end = align_up(L.rot_k + 2 * tn * hkv * D, 256);
   return L;
 }
 
@@ -440,6 +448,20 @@ int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* 
   if (st) return st;
   serialize_plan(p, L, cu_kn, B, page_size, w->plan[*index].host);
   return VPK_SUCCESS;
+}
+
+// Positions of the rows the rotary embedding turns: query row i of a sequence
+// at Lk - Lq + i (the key its end-aligned causal bound stops at), new token j
+// at Lc + j (the slot the append writes); rows no sequence names get -1.
+void write_rope_positions(const Plan& p, const Layout& L, int32_t B, int32_t Tq, char* base) {
+  int32_t* qpos = reinterpret_cast<int32_t*>(base + L.qpos);
+  int32_t* kpos = reinterpret_cast<int32_t*>(base + L.kpos);
+  std::fill(qpos, qpos + Tq, -1);
+  for (int32_t b = 0; b < B; ++b) {
+    const SeqInfo& q = p.seqs[b];
+    for (int32_t i = 0; i < q.q_len; ++i) qpos[q.q_start + i] = q.kv_len - q.q_len + i;
+    for (int32_t j = 0; j < q.new_len; ++j) kpos[q.kn_start + j] = q.cache_len + j;
+  }
 }
 
 AppendParams append_params(const Call& c, char* head, char* R, const Layout& L,
@@ -656,9 +678,34 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
 }
 
 // Plan a validated call and enqueue it on `stream` (direct calls).
+int32_t check_rope_args(const Call& c, const vpk_rope* rope) {
+  int32_t st;
+  const int32_t D = c.d->head_dim;
+  if ((st = check_ptr(rope->cos, 16, "rope->cos")) || (st = check_ptr(rope->sin, 16, "rope->sin"))) return st;
+  if (rope->rotary_dim < 16 || rope->rotary_dim > D || rope->rotary_dim % 16 != 0)
+    return fail(VPK_ERROR_INVALID_VALUE, "rope->rotary_dim must be a multiple of 16 in [16, head_dim]");
+  if (rope->interleaved != 0 && rope->interleaved != 1) return fail(VPK_ERROR_INVALID_VALUE, "rope->interleaved must be 0 or 1");
+  if (rope->max_positions < 1) return fail(VPK_ERROR_INVALID_VALUE, "rope->max_positions must be >= 1");
+  return VPK_SUCCESS;
+}
+
+// Every turned row needs a position in [0, max_positions): Lq <= Lk and Lk <= max_positions.
+int32_t check_rope_positions(const Plan& plan, int32_t B, const vpk_rope* rope) {
+  for (int32_t b = 0; b < B; ++b) {
+    const SeqInfo& q = plan.seqs[b];
+    if (q.q_len > q.kv_len)
+      return fail(VPK_ERROR_INVALID_VALUE, "sequence " + std::to_string(b) + ": with rotary embedding a sequence needs "
+                                           "no more query rows than keys (query row i sits at Lk - Lq + i)");
+    if ((q.q_len > 0 || q.new_len > 0) && q.kv_len > rope->max_positions)
+      return fail(VPK_ERROR_INVALID_VALUE, "sequence " + std::to_string(b) + " reaches position " +
+                                               std::to_string(q.kv_len - 1) + ", past rope->max_positions");
+  }
+  return VPK_SUCCESS;
+}
+
 int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const void* q, const void* k_new,
                          const void* v_new, void* k_cache, void* v_cache, const int32_t* block_table, float scale,
-                         void* out, float* lse, hipStream_t stream) {
+                         void* out, float* lse, hipStream_t stream, const vpk_rope* rope = nullptr) {
   const vpk_dims* dims = c.d;
   const int32_t B = dims->batch;
   int32_t st;
@@ -670,12 +717,39 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
-  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
+  if (rope && (st = check_rope_positions(plan, B, rope))) return st;
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr);
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, L.part_end, &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
   const Bases bases{w->plan[region].host, w->parts(), w->dev};
+  if (rope) {
+    // turn q and k_new into copies; everything after reads the copies
+    write_rope_positions(plan, L, B, dims->total_q, bases.R);
+    vpk::RopeParams rp{};
+    rp.q = static_cast<const uint16_t*>(q);
+    rp.q_out = reinterpret_cast<uint16_t*>(bases.PA + L.rot_q);
+    rp.qpos = reinterpret_cast<const int32_t*>(bases.R + L.qpos);
+    rp.k = static_cast<const uint16_t*>(k_new);
+    rp.k_out = reinterpret_cast<uint16_t*>(bases.PA + L.rot_k);
+    rp.kpos = reinterpret_cast<const int32_t*>(bases.R + L.kpos);
+    rp.cos = rope->cos;
+    rp.sin = rope->sin;
+    rp.q_rows = dims->total_q;
+    rp.k_rows = k_new ? dims->total_knew : 0;
+    rp.hq = dims->num_q_heads;
+    rp.hkv = dims->num_kv_heads;
+    rp.rot_dim = rope->rotary_dim;
+    rp.interleaved = rope->interleaved;
+    {
+      KernelTimer tm(4, stream);
+      const int rc = vpk::launch_rope(rp, dims->head_dim, stream);
+      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "rotary embedding launch");
+    }
+    q = rp.q_out;
+    if (k_new) k_new = rp.k_out;
+  }
   if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
                         out, lse, stream, w, true)))
     return st;
@@ -687,7 +761,7 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
                   void* k_cache, void* v_cache, const int32_t* block_table,
                   const int32_t* cache_seqlens, int32_t page_size, int32_t causal, float scale,
                   const float* kv_scale, void* out, float* lse, const vpk_host_index* host,
-                  void* stream_v) {
+                  void* stream_v, const vpk_rope* rope = nullptr) {
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
   // new tokens are present when any of their arrays is given; with total_knew == 0
@@ -723,12 +797,14 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     if ((st = check_ptr(q, 16, "q")) || (st = check_ptr(out, 16, "out"))) return st;
     if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
   }
+  if (rope && (st = check_rope_args(c, rope))) return st;
   if (B == 0) return VPK_SUCCESS;
 
   Mirrors m;
   if ((st = get_mirrors(c, cu_seqlens_q, cu_seqlens_knew, cache_seqlens, host, stream, true, m))) return st;
   if ((st = check_contents(c, m, true))) return st;
-  return plan_and_enqueue(c, m, causal, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse, stream);
+  return plan_and_enqueue(c, m, causal, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse, stream,
+                          rope);
 }
 
 // The page-list form: each sequence's query rows [q_start, q_start + q_len)
@@ -1031,6 +1107,25 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims, const void* q, const int32_t
   }
 }
 
+int32_t attn_varlen_paged_rope_fwd(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
+                                   const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
+                                   void* k_cache, void* v_cache, const int32_t* block_table,
+                                   const int32_t* cache_seqlens, int32_t page_size, int32_t causal,
+                                   float scale, const float* kv_scale, const vpk_rope* rope, void* out,
+                                   float* lse, const vpk_host_index* host, void* stream) {
+  try {
+    g_err.clear();
+    if (!rope) return fail(VPK_ERROR_INVALID_VALUE, "rope is NULL");
+    return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache,
+                     block_table, cache_seqlens, page_size, causal, scale, kv_scale, out, lse,
+                     host, stream, rope);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
 int32_t attn_varlen_paged_list_fwd(const vpk_dims* dims, const void* q, const void* k_new, const void* v_new,
                                    void* k_cache, void* v_cache, const int32_t* kv_indices, int32_t page_size,
                                    int32_t causal, float scale, const float* kv_scale, void* out, float* lse,
@@ -1108,7 +1203,7 @@ int32_t vpk_timing_reset(void) {
 }
 
 int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..3");
+  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..4");
   std::lock_guard<std::mutex> lk(g_tmu);
   for (const TimingRec& r : g_tpending) {
     hipError_t e = hipEventSynchronize(r.b);

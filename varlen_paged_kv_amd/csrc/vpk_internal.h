@@ -139,10 +139,29 @@ struct MergeParams {
   int32_t head_dim;
 };
 
+// Rotary embedding of the query rows and the new key rows into copies.
+struct RopeParams {
+  const uint16_t* q;          // bf16 [q_rows, hq, D]
+  uint16_t* q_out;            // turned copy, same layout
+  const int32_t* qpos;        // [q_rows] position of each row, -1 = row not read
+  const uint16_t* k;          // bf16 [k_rows, hkv, D]
+  uint16_t* k_out;
+  const int32_t* kpos;        // [k_rows]
+  const float* cos;           // [max_positions, rot_dim / 2]
+  const float* sin;
+  int32_t q_rows;
+  int32_t k_rows;
+  int32_t hq;
+  int32_t hkv;
+  int32_t rot_dim;            // multiple of 16, <= D
+  int32_t interleaved;
+};
+
 // Kernel launchers (defined in the .hip files); they return hipError_t as int.
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
                      bool decode, void* stream);
 int launch_append(const AppendParams& p, void* stream);
 int launch_merge(const MergeParams& p, void* stream);
+int launch_rope(const RopeParams& p, int head_dim, void* stream);
 
 }  // namespace vpk
