@@ -1,7 +1,7 @@
 """Benchmark: one step = one attn_varlen_paged_fwd call (append + plan upload +
 attention + split merge) over a seeded synthetic batch on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rope]
 
 Default workload: varlen prefill without a cache (16 sequences, lengths
 U[256, 2048], 32 query / 8 kv heads, head_dim 128, bf16, causal).  Other names:
@@ -12,6 +12,9 @@ Prints ONE JSON line.  `value` is the algorithmic throughput of the whole step
 pair per query head) or, for pure decode, KV-cache GB/s (Lk * Hkv * D * 2 *
 bytes per element per sequence).  `roofline` is the attention kernel alone,
 timed with HIP events recorded by the library on the launch stream.
+With --rope each step is attn_varlen_paged_rope_fwd (rotary embedding of q
+and k_new first, rotary_dim = head_dim, half-split pairing) and the line also
+carries the rotation kernel's own time and bandwidth.
 """
 from __future__ import annotations
 
@@ -144,6 +147,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for HBM counters)")
     ap.add_argument("--persistent", type=int, default=-1)
+    ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -187,6 +191,12 @@ def main():
     host = dict(cu_seqlens_q=wl.cu_seqlens_q, cu_seqlens_knew=wl.cu_seqlens_knew,
                 cache_seqlens=wl.cache_seqlens, block_table=wl.block_table)
     vpk.set_option("persistent", args.persistent)
+    rope_kw = None
+    if args.rope:
+        from synth import rope_tables
+        cos, sin = rope_tables(int(wl.kv_lens().max()), wl.D)
+        rope_kw = dict(rope_cos=torch.from_numpy(cos).to(dev), rope_sin=torch.from_numpy(sin).to(dev),
+                       rotary_dim=wl.D, interleaved=False)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -198,10 +208,12 @@ def main():
 
     def step(i):
         c = copies[i % len(copies)]
-        vpk.attn_varlen_paged_fwd(c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"],
-                                  c["vc"], c["bt"], c["cl"], wl.page_size, wl.causal, wl.scale,
-                                  wl.kv_scale if fp8 else None, out=c["out"], lse=c["lse"],
-                                  host_index=host)
+        args_ = (c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"], c["vc"], c["bt"], c["cl"],
+                 wl.page_size, wl.causal, wl.scale, wl.kv_scale if fp8 else None)
+        if rope_kw is None:
+            vpk.attn_varlen_paged_fwd(*args_, out=c["out"], lse=c["lse"], host_index=host)
+        else:
+            vpk.attn_varlen_paged_rope_fwd(*args_, **rope_kw, out=c["out"], lse=c["lse"], host_index=host)
 
     print(f"[bench] {args.workload}: Tq={wl.Tq} Tn={wl.Tn} pages={wl.num_pages} "
           f"flops/step={step_flops:.3e} kv bytes/step={step_bytes:.3e}", file=sys.stderr, flush=True)
@@ -235,6 +247,7 @@ def main():
     dec_ms, dec_n = vpk.timing_read(vpk.KERNEL_ATTENTION_DECODE)
     app_ms, app_n = vpk.timing_read(vpk.KERNEL_APPEND)
     mrg_ms, mrg_n = vpk.timing_read(vpk.KERNEL_MERGE)
+    rot_ms, rot_n = vpk.timing_read(vpk.KERNEL_ROPE)
     elapsed = max(gpu_ms / 1e3, 1e-9)
     ms_per_step = gpu_ms / args.steps
     avg = lambda ms, n: ms / max(n, 1)
@@ -242,7 +255,8 @@ def main():
           f"instrumented pass {inst_ms * 1e3 / args.steps:.1f} us/step); "
           f"attention prefill-mode {avg(pre_ms, pre_n) * 1e3:.1f} us x{pre_n}, decode-mode "
           f"{avg(dec_ms, dec_n) * 1e3:.1f} us x{dec_n}, standalone append {avg(app_ms, app_n) * 1e3:.1f} us x{app_n}, "
-          f"merge {avg(mrg_ms, mrg_n) * 1e3:.1f} us x{mrg_n}", file=sys.stderr, flush=True)
+          f"merge {avg(mrg_ms, mrg_n) * 1e3:.1f} us x{mrg_n}, rotary {avg(rot_ms, rot_n) * 1e3:.1f} us x{rot_n}",
+          file=sys.stderr, flush=True)
 
     # work of the sequences each grid serves (decode-mode: q_len * g <= 32 rows)
     dec_seq = wl.q_lens() * (wl.Hq // wl.Hkv) <= 32
@@ -270,8 +284,19 @@ def main():
                              f"over a second pass of the same {args.steps} steps "
                              f"({inst_ms * 1e3 / args.steps:.1f} us/step with the events)")
 
+    rope_line = None
+    if args.rope:
+        # algorithmic bytes: q and k_new read once and written once (bf16); the
+        # angle tables (max_pos x D/2 x 8 bytes) are re-read through the caches
+        rbytes = 2.0 * 2.0 * wl.D * (wl.Tq * wl.Hq + wl.Tn * wl.Hkv)
+        rus = avg(rot_ms, rot_n) * 1e3
+        rope_line = {"kernel": "rotary embedding of q and k_new", "rotary_dim": wl.D, "interleaved": False,
+                     "kernel_avg_us": rus, "bytes": rbytes, "bound": "hbm",
+                     "achieved": rbytes / max(rus, 1e-9) * 1e-3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": rbytes / max(rus, 1e-9) * 1e-3 / PEAK_HBM_GBS}
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.rope:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl)
 
@@ -285,11 +310,14 @@ def main():
                    "page_size": wl.page_size, "causal": wl.causal,
                    "kv_cache": wl.cache_dtype or "none", "pages": wl.num_pages,
                    "flops_per_step": step_flops, "kv_bytes_per_step": step_bytes,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **({"rope": "rotary_dim=head_dim, half-split"}
+                                                   if args.rope else {})},
         "pct_of_peak": 100.0 * value / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if rope_line is not None:
+        line["rope_kernel"] = rope_line
     print(json.dumps(line), flush=True)
 
 

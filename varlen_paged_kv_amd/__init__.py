@@ -24,11 +24,12 @@ from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 
 __all__ = ["attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
-           "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE"]
+           "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE", "KERNEL_ROPE",
+           "attn_varlen_paged_rope_fwd"]
 
 # kernel ids of the timing API: the prefill-mode attention grid, the standalone
 # append, the decode-mode attention grid, the split merge
-KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE = 0, 1, 2, 3
+KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE, KERNEL_ROPE = 0, 1, 2, 3, 4
 
 
 class VpkError(RuntimeError):

@@ -14,13 +14,16 @@
 // rounded to float32, their difference or sum rounded to float32 (no fused
 // multiply-add), then round to nearest even to bf16.
 //
-// The pass is HBM-bound and elementwise: one thread per 16-byte chunk of
-// output (8 coordinates of one head of one row); in the half-split form a
-// thread also reads its partner chunk (same row, same wave, so the same cache
-// lines) and 8 angles; in the interleaved form its own chunk holds its 4
-// pairs.  Rows with a negative position are skipped (no sequence names them).
+// The pass is HBM-bound and elementwise: a thread turns 16-byte chunks of
+// output (8 coordinates of one head of one row); in the half-split form it
+// also reads the partner chunk (same row, read by the same wave, so the same
+// cache lines) and 8 angles; in the interleaved form its own chunk holds its
+// 4 pairs.  Rows with a negative position are skipped (no sequence names
+// them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "../vpk_internal.h"
 
@@ -62,76 +65,98 @@ __device__ __forceinline__ uint4 pack8(const uint16_t* r) {
   return v;
 }
 
+// Rows per workgroup: at most kRopeRowsMax, chosen so that each tensor gets
+// about kRopeTargetWgs workgroups.
+constexpr int kRopeRowsMax = 256;
+constexpr int kRopeTargetWgs = 1024;
+
+// Workgroup: `rows` consecutive rows of q (the first q_blocks workgroups) or of
+// k_new.  Their positions are staged in LDS with one read (the position arrays
+// may sit in host memory).  A head row splits into units: in the half-split
+// form a unit is a chunk of the first half with its partner chunk (8 pairs,
+// two chunks out), in the interleaved form one chunk (4 pairs); the chunks
+// past rotary_dim are copy units.  The 256 threads walk the units of the
+// block; a thread keeps the angles it read while its position and unit stay
+// the same (the heads of a row share them).
 template <int D>
-__global__ __launch_bounds__(256) void rope_kernel(const RopeParams p) {
+__global__ __launch_bounds__(256) void rope_kernel(const RopeParams p, int q_rpw, int k_rpw, int q_blocks) {
   constexpr int CH = D / 8;                      // 16-byte chunks per head row
-  const uint64_t chunk = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
-  // (row, head) of q, then of k_new; each count is below 2^31 (checked by the host)
-  const uint32_t job = static_cast<uint32_t>(chunk / CH);
-  const int c = static_cast<int>(chunk % CH);
-  const uint32_t q_jobs = static_cast<uint32_t>(p.q_rows) * static_cast<uint32_t>(p.hq);
-  const uint16_t* src;
-  uint16_t* dst;
-  int32_t pos;
-  if (job < q_jobs) {
-    src = p.q + static_cast<size_t>(job) * D;
-    dst = p.q_out + static_cast<size_t>(job) * D;
-    pos = p.qpos[job / static_cast<uint32_t>(p.hq)];
-  } else {
-    const uint32_t kj = job - q_jobs;
-    if (kj >= static_cast<uint32_t>(p.k_rows) * static_cast<uint32_t>(p.hkv)) return;
-    src = p.k + static_cast<size_t>(kj) * D;
-    dst = p.k_out + static_cast<size_t>(kj) * D;
-    pos = p.kpos[kj / static_cast<uint32_t>(p.hkv)];
-  }
-  if (pos < 0) return;
-  const uint4* s4 = reinterpret_cast<const uint4*>(src);
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
-  const int R = p.rot_dim;
-  const int half = R >> 1;
-  const int e = c * 8;                           // first coordinate of this chunk
-  if (e >= R) {
-    d4[c] = s4[c];
-    return;
-  }
-  const float* cr = p.cos + static_cast<int64_t>(pos) * half;
-  const float* sr = p.sin + static_cast<int64_t>(pos) * half;
-  float x[8];
-  uint16_t r[8];
-  if (p.interleaved) {
-    unpack8(s4[c], x);
-    const float4 cv = *reinterpret_cast<const float4*>(cr + e / 2);
-    const float4 sv = *reinterpret_cast<const float4*>(sr + e / 2);
-    const float cs[4] = {cv.x, cv.y, cv.z, cv.w}, sn[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) turn(x[2 * i], x[2 * i + 1], cs[i], sn[i], r[2 * i], r[2 * i + 1]);
-  } else {
-    // chunk in the first half: a = own, b = partner; in the second: a = partner, b = own
-    const bool first = e < half;
-    const int pair0 = first ? e : e - half;
-    const int pc = first ? c + half / 8 : c - half / 8;
-    float y[8];
-    unpack8(s4[c], x);
-    unpack8(s4[pc], y);
-    const float4 c0 = *reinterpret_cast<const float4*>(cr + pair0);
-    const float4 c1 = *reinterpret_cast<const float4*>(cr + pair0 + 4);
-    const float4 s0 = *reinterpret_cast<const float4*>(sr + pair0);
-    const float4 s1 = *reinterpret_cast<const float4*>(sr + pair0 + 4);
-    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t ra, rb;
-      if (first) {
-        turn(x[i], y[i], cs[i], sn[i], ra, rb);
-        r[i] = ra;
-      } else {
-        turn(y[i], x[i], cs[i], sn[i], ra, rb);
-        r[i] = rb;
+  __shared__ int32_t spos[kRopeRowsMax];
+  const bool is_q = static_cast<int>(blockIdx.x) < q_blocks;
+  const int blk = is_q ? blockIdx.x : blockIdx.x - q_blocks;
+  const int rpw = is_q ? q_rpw : k_rpw;
+  const int H = is_q ? p.hq : p.hkv;
+  const int r0 = blk * rpw;
+  const int nr = min(rpw, (is_q ? p.q_rows : p.k_rows) - r0);
+  const int32_t* pos = is_q ? p.qpos : p.kpos;
+  for (int i = threadIdx.x; i < nr; i += 256) spos[i] = pos[r0 + i];
+  __syncthreads();
+  const size_t base = static_cast<size_t>(r0) * H * D;
+  const uint16_t* src = (is_q ? p.q : p.k) + base;
+  uint16_t* dst = (is_q ? p.q_out : p.k_out) + base;
+  const int rc = p.rot_dim / 8;                  // turned chunks per head row
+  const int half = p.rot_dim / 2;
+  const bool inter = p.interleaved != 0;
+  const uint32_t U = inter ? CH : CH - rc / 2;   // units per head row
+  const uint32_t row_units = static_cast<uint32_t>(H) * U;
+  const uint32_t units = static_cast<uint32_t>(nr) * row_units;
+  int64_t have = -1;                             // (position, unit) of the angles in cs / sn
+  float cs[8], sn[8];
+  for (uint32_t k = threadIdx.x; k < units; k += 256) {
+    const uint32_t row = k / row_units;
+    const uint32_t rem = k - row * row_units;
+    const uint32_t hrow = row * H + rem / U;     // head row within the block
+    const int u = static_cast<int>(rem % U);
+    const int m = spos[row];
+    if (m < 0) continue;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src + static_cast<size_t>(hrow) * D);
+    uint4* d4 = reinterpret_cast<uint4*>(dst + static_cast<size_t>(hrow) * D);
+    const int rot_units = inter ? rc : rc / 2;
+    if (u >= rot_units) {
+      const int c = inter ? u : u + rc / 2;
+      d4[c] = s4[c];
+      continue;
+    }
+    const int64_t want = static_cast<int64_t>(m) * CH + u;
+    const float* cr = p.cos + static_cast<int64_t>(m) * half;
+    const float* sr = p.sin + static_cast<int64_t>(m) * half;
+    float x[8];
+    uint16_t r[8];
+    if (inter) {
+      const uint4 v = s4[u];
+      if (want != have) {
+        const float4 cv = *reinterpret_cast<const float4*>(cr + 4 * u);
+        const float4 sv = *reinterpret_cast<const float4*>(sr + 4 * u);
+        cs[0] = cv.x, cs[1] = cv.y, cs[2] = cv.z, cs[3] = cv.w;
+        sn[0] = sv.x, sn[1] = sv.y, sn[2] = sv.z, sn[3] = sv.w;
+        have = want;
       }
+      unpack8(v, x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) turn(x[2 * i], x[2 * i + 1], cs[i], sn[i], r[2 * i], r[2 * i + 1]);
+      d4[u] = pack8(r);
+    } else {
+      // a = chunk u of the first half, b = its partner u + rotary_dim / 16
+      const uint4 va = s4[u], vb = s4[u + rc / 2];
+      if (want != have) {
+        const float4 c0 = *reinterpret_cast<const float4*>(cr + 8 * u);
+        const float4 c1 = *reinterpret_cast<const float4*>(cr + 8 * u + 4);
+        const float4 s0 = *reinterpret_cast<const float4*>(sr + 8 * u);
+        const float4 s1 = *reinterpret_cast<const float4*>(sr + 8 * u + 4);
+        cs[0] = c0.x, cs[1] = c0.y, cs[2] = c0.z, cs[3] = c0.w, cs[4] = c1.x, cs[5] = c1.y, cs[6] = c1.z, cs[7] = c1.w;
+        sn[0] = s0.x, sn[1] = s0.y, sn[2] = s0.z, sn[3] = s0.w, sn[4] = s1.x, sn[5] = s1.y, sn[6] = s1.z, sn[7] = s1.w;
+        have = want;
+      }
+      float y[8];
+      uint16_t rb[8];
+      unpack8(va, x);
+      unpack8(vb, y);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) turn(x[i], y[i], cs[i], sn[i], r[i], rb[i]);
+      d4[u] = pack8(r);
+      d4[u + rc / 2] = pack8(rb);
     }
   }
-  d4[c] = pack8(r);
 }
 
 }  // namespace
@@ -139,16 +164,18 @@ __global__ __launch_bounds__(256) void rope_kernel(const RopeParams p) {
 int launch_rope(const RopeParams& p, int head_dim, void* stream) {
   if (head_dim != 64 && head_dim != 128) return static_cast<int>(hipErrorInvalidValue);
   if (p.rot_dim < 16 || p.rot_dim > head_dim || p.rot_dim % 16 != 0) return static_cast<int>(hipErrorInvalidValue);
-  const int64_t jobs = static_cast<int64_t>(p.q_rows) * p.hq + static_cast<int64_t>(p.k_rows) * p.hkv;
-  const int64_t chunks = jobs * (head_dim / 8);
-  if (chunks <= 0) return 0;
-  const int64_t grid = (chunks + 255) / 256;
-  if (grid > 0x7fffffff) return static_cast<int>(hipErrorInvalidValue);
+  if (p.q_rows < 0 || p.k_rows < 0) return static_cast<int>(hipErrorInvalidValue);
+  auto rows_per_wg = [](int rows) { return std::min(kRopeRowsMax, std::max(1, (rows + kRopeTargetWgs - 1) / kRopeTargetWgs)); };
+  const int q_rpw = rows_per_wg(p.q_rows), k_rpw = rows_per_wg(p.k_rows);
+  const int q_blocks = (p.q_rows + q_rpw - 1) / q_rpw;
+  const int k_blocks = (p.k_rows + k_rpw - 1) / k_rpw;
+  if (q_blocks + k_blocks == 0) return 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(q_blocks + k_blocks));
   if (head_dim == 128)
-    hipLaunchKernelGGL(rope_kernel<128>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_kernel<128>, grid, dim3(256), 0, s, p, q_rpw, k_rpw, q_blocks);
   else
-    hipLaunchKernelGGL(rope_kernel<64>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_kernel<64>, grid, dim3(256), 0, s, p, q_rpw, k_rpw, q_blocks);
   return static_cast<int>(hipGetLastError());
 }
 
