@@ -298,11 +298,27 @@ int32_t vpk_plan_create(const vpk_dims* dims, const vpk_host_index* host, int32_
  * run one after the other on `stream`.  Runs of one plan share its partial
  * space: overlapping runs of the same plan (two streams at once) race.
  * kv_scale is read on the host at each call (a captured graph keeps the
- * values of the captured call).
+ * values of the captured call; vpk_plan_run_device_scale reads them on the
+ * device instead).
  */
 int32_t vpk_plan_run(vpk_plan plan, const void* q, const void* k_new, const void* v_new,
                      void* k_cache, void* v_cache, const int32_t* block_table, float scale,
                      const float* kv_scale, void* out, float* lse, void* stream);
+
+/*
+ * vpk_plan_run_device_scale -- vpk_plan_run with the fp8 scales in device
+ * memory: kv_scale_dev is a device float[2] = {k_scale, v_scale} (4-byte
+ * aligned, borrowed) that the kernels read when they run, so a graph captured
+ * around this call follows scales the caller updates between replays.  The
+ * kernels derive the score factor and the reciprocals the way the host does
+ * for vpk_plan_run (same bits for the same scales).  The values must be
+ * finite and > 0 (they are not checked: a bad value gives bad results, never
+ * an out-of-bounds access).  For a bf16 plan kv_scale_dev must be NULL.
+ * Errors as for vpk_plan_run.
+ */
+int32_t vpk_plan_run_device_scale(vpk_plan plan, const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const int32_t* block_table, float scale,
+                                  const float* kv_scale_dev, void* out, float* lse, void* stream);
 
 /* Synchronise `stream` and return (and clear) the plan's device error flag
  * (bit 0: a page id outside [0, num_pages) was met on the device). */

@@ -248,3 +248,11 @@ def test_rope_errors_before_the_device():
     hi, k = _host([0, 3, 4], [0, 1, 2], [1, 5])
     st, msg = call(d2, rope(), hi)
     assert st == 1 and "sequence 0" in msg and "query rows than keys" in msg
+
+
+def test_device_scale_run_errors_before_the_device():
+    lib = _lib.load()
+    vp = ctypes.c_void_p
+    st = lib.vpk_plan_run_device_scale(None, vp(FAKE), None, None, None, None, None, 0.1, vp(FAKE), vp(FAKE),
+                                       vp(FAKE), None)
+    assert st == 1 and b"plan is NULL" in lib.vpk_last_error()

@@ -117,3 +117,56 @@ def test_plan_run_in_graph_replays(case):
     del g
     plan.close()
     say(f"[ok] graph replays of {case}: bitwise equal to eager calls")
+
+
+def test_device_scales_follow_changes_between_graph_replays():
+    """fp8 plan run with the scales in device memory: bitwise equal to the direct
+    call with the same scales on the host, also in a captured graph whose scale
+    buffer the program rewrites between replays."""
+    vpk.set_option("force_splits", 2)
+    wl = CASES["mixed_fp8"]()
+    dc = DeviceCall(wl)
+    plan = _plan_for(dc)
+    ks_host = np.asarray(wl.kv_scale, np.float32)
+    ks_dev = torch.from_numpy(ks_host.copy()).cuda()
+
+    def direct(ks):
+        return vpk.attn_varlen_paged_fwd(dc.q, dc.cu_q, dc.k_new, dc.v_new, dc.cu_kn, dc.k_cache, dc.v_cache,
+                                         dc.bt, dc.cl, wl.page_size, wl.causal, wl.scale,
+                                         (float(ks[0]), float(ks[1])), host_index=dc.host)
+
+    out = torch.empty_like(dc.q)
+    lse = torch.empty((wl.Hq, wl.Tq), dtype=torch.float32, device=dc.q.device)
+    plan.run(dc.q, dc.k_new, dc.v_new, dc.k_cache, dc.v_cache, dc.bt, scale=wl.scale, kv_scale=ks_dev,
+             out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = direct(ks_host)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out), _bits(ref_out)) and np.array_equal(_bits(lse), _bits(ref_lse))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.run(dc.q, dc.k_new, dc.v_new, dc.k_cache, dc.v_cache, dc.bt, scale=wl.scale, kv_scale=ks_dev,
+                 out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(dc.q, dc.k_new, dc.v_new, dc.k_cache, dc.v_cache, dc.bt, scale=wl.scale, kv_scale=ks_dev,
+                 out=out, lse=lse)
+    torch.cuda.synchronize()
+    for rep, f in enumerate((1.25, 0.5, 1.0)):
+        ks = (ks_host * np.float32(f)).astype(np.float32)
+        ks_dev.copy_(torch.from_numpy(ks))           # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = _bits(out), _bits(lse)
+        kc_g = dc.k_cache.cpu().numpy().copy()
+        ref_out, ref_lse = direct(ks)
+        torch.cuda.synchronize()
+        assert np.array_equal(got_o, _bits(ref_out)), f"replay {rep} (scales x{f}): out differs"
+        assert np.array_equal(got_l, _bits(ref_lse)), f"replay {rep} (scales x{f}): lse differs"
+        assert np.array_equal(kc_g, dc.k_cache.cpu().numpy()), f"replay {rep}: appended codes differ"
+    del g
+    plan.close()
+    say("[ok] device scales: plan runs and graph replays follow the scale buffer bit for bit")

@@ -307,7 +307,11 @@ class Plan:
     def run(self, q, k_new=None, v_new=None, k_cache=None, v_cache=None, block_table=None, *,
             scale: Optional[float] = None, kv_scale=None, out=None, lse=None, return_lse: bool = True,
             stream=None):
-        """Enqueue the planned call with these buffers; returns (out, lse)."""
+        """Enqueue the planned call with these buffers; returns (out, lse).
+
+        kv_scale (fp8 plans): a host pair (k_scale, v_scale), read now, or a
+        device float32 tensor of 2 elements, read by the kernels when they run
+        (vpk_plan_run_device_scale: a captured graph follows later values)."""
         lib = _lib.load()
         q = _dev(q, "q", _BF16)
         k_new = _dev(k_new, "k_new", _BF16)
@@ -332,6 +336,15 @@ class Plan:
             out = torch.empty_like(q)
         if lse is None and return_lse:
             lse = torch.empty((Hq, self.total_q), dtype=torch.float32, device=q.device)
+        if isinstance(kv_scale, torch.Tensor) and kv_scale.is_cuda:
+            ksd = _dev(kv_scale, "kv_scale", (torch.float32,))
+            if ksd.numel() != 2:
+                raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "a device kv_scale holds 2 floats")
+            st = lib.vpk_plan_run_device_scale(self._h, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                               _ptr(v_cache), _ptr(block_table), float(scale), _ptr(ksd),
+                                               _ptr(out), _ptr(lse), _stream_handle(stream))
+            _check(st)
+            return out, lse
         ks = None
         if self.fp8:
             if kv_scale is None:

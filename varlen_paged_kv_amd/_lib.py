@@ -28,6 +28,7 @@ EXPORTS = (
     "vpk_set_option", "vpk_timing_enable", "vpk_timing_reset", "vpk_timing_read",
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
     "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
+    "vpk_plan_run_device_scale",
 )
 
 
@@ -112,6 +113,8 @@ def load() -> ctypes.CDLL:
     lib.vpk_plan_create.argtypes = [P(VpkDims), P(VpkHostIndex), i32, i32, i32, i32, P(vp)]
     lib.vpk_plan_run.restype = i32
     lib.vpk_plan_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, P(f32), vp, vp, vp]
+    lib.vpk_plan_run_device_scale.restype = i32
+    lib.vpk_plan_run_device_scale.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp]
     lib.vpk_plan_device_error.restype = i32
     lib.vpk_plan_device_error.argtypes = [vp, vp, P(i32)]
     lib.vpk_plan_destroy.restype = i32

@@ -255,7 +255,8 @@ struct Call {
   const vpk_dims* d;
   bool has_new, has_cache, fp8;
   int32_t page_size;
-  const float* kv_scale;
+  const float* kv_scale;                  // host {k_scale, v_scale} (fp8)
+  const float* kv_scale_dev = nullptr;    // or the same in device memory, read by the kernels
 };
 
 int32_t check_cu(const int32_t* cu, int32_t B, int32_t total, const char* name) {
@@ -484,8 +485,9 @@ AppendParams append_params(const Call& c, char* head, char* R, const Layout& L,
   ap.page_size = c.page_size;
   ap.row_elems = d->num_kv_heads * d->head_dim;
   ap.fp8 = c.fp8 ? 1 : 0;
-  ap.k_inv_scale = c.fp8 ? 1.0f / c.kv_scale[0] : 1.0f;
-  ap.v_inv_scale = c.fp8 ? 1.0f / c.kv_scale[1] : 1.0f;
+  ap.k_inv_scale = c.fp8 && c.kv_scale ? 1.0f / c.kv_scale[0] : 1.0f;
+  ap.v_inv_scale = c.fp8 && c.kv_scale ? 1.0f / c.kv_scale[1] : 1.0f;
+  ap.kv_scale_dev = c.fp8 ? c.kv_scale_dev : nullptr;
   return ap;
 }
 
@@ -519,12 +521,15 @@ int32_t check_run_pointers(const Call& c, const void* q, const void* k_new, cons
   } else if (k_cache || v_cache) {
     return fail(VPK_ERROR_INVALID_VALUE, "without a cache k_cache/v_cache must be NULL");
   }
-  if (c.fp8) {
+  if (c.fp8 && c.kv_scale_dev) {
+    if (c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "give the fp8 scales on the host or on the device, not both");
+    if ((st = check_ptr(c.kv_scale_dev, 4, "kv_scale_dev"))) return st;
+  } else if (c.fp8) {
     if (!c.kv_scale) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache");
     for (int i = 0; i < 2; ++i)
       if (!std::isfinite(c.kv_scale[i]) || !(c.kv_scale[i] > 0.f))
         return fail(VPK_ERROR_INVALID_VALUE, "kv_scale entries must be finite and > 0");
-  } else if (c.kv_scale && c.has_cache) {
+  } else if ((c.kv_scale || c.kv_scale_dev) && c.has_cache) {
     return fail(VPK_ERROR_INVALID_VALUE, "kv_scale must be NULL for a bf16 cache");
   }
   if (dims->total_q > 0) {
@@ -606,9 +611,11 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
     p.total_q = dims->total_q;
     p.causal = causal;
     const double log2e = 1.4426950408889634;
-    p.qk_scale_log2 = static_cast<float>(static_cast<double>(scale) * log2e *
-                                         (c.fp8 ? static_cast<double>(kv_scale[0]) : 1.0));
-    p.v_scale = c.fp8 ? kv_scale[1] : 1.0f;
+    const bool host_scales = c.fp8 && kv_scale;
+    p.scale_log2e = static_cast<double>(scale) * log2e;
+    p.qk_scale_log2 = static_cast<float>(p.scale_log2e * (host_scales ? static_cast<double>(kv_scale[0]) : 1.0));
+    p.v_scale = host_scales ? kv_scale[1] : 1.0f;
+    p.kv_scale_dev = c.fp8 ? c.kv_scale_dev : nullptr;
     p.app = ap;
     const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
     // `with_append`: this grid also runs one workgroup per new token
@@ -1022,13 +1029,13 @@ int32_t plan_create_impl(const vpk_dims* dims, const vpk_host_index* host, int32
 
 int32_t plan_run_impl(vpk_plan pl, const void* q, const void* k_new, const void* v_new, void* k_cache,
                       void* v_cache, const int32_t* block_table, float scale, const float* kv_scale,
-                      void* out, float* lse, void* stream_v) {
+                      void* out, float* lse, void* stream_v, const float* kv_scale_dev = nullptr) {
   if (!pl) return fail(VPK_ERROR_INVALID_VALUE, "plan is NULL");
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != pl->device) return fail(VPK_ERROR_INVALID_VALUE, "the plan was created on another device");
-  Call c{&pl->dims, pl->has_new, pl->has_cache, pl->fp8, pl->page_size, kv_scale};
+  Call c{&pl->dims, pl->has_new, pl->has_cache, pl->fp8, pl->page_size, kv_scale, kv_scale_dev};
   int32_t st = check_run_pointers(c, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse);
   if (st) return st;
   if (pl->dims.batch == 0) return VPK_SUCCESS;
@@ -1048,6 +1055,19 @@ int32_t vpk_plan_create(const vpk_dims* dims, const vpk_host_index* host, int32_
     return plan_create_impl(dims, host, has_new, has_cache, page_size, causal, plan);
   } catch (...) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host exception while planning");
+  }
+}
+
+int32_t vpk_plan_run_device_scale(vpk_plan plan, const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const int32_t* block_table, float scale,
+                                  const float* kv_scale_dev, void* out, float* lse, void* stream) {
+  try {
+    g_err.clear();
+    if (plan && plan->fp8 && !kv_scale_dev) return fail(VPK_ERROR_INVALID_VALUE, "kv_scale_dev is NULL for an fp8 plan");
+    return plan_run_impl(plan, q, k_new, v_new, k_cache, v_cache, block_table, scale, nullptr, out, lse, stream,
+                         kv_scale_dev);
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
   }
 }
 

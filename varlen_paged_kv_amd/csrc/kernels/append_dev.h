@@ -78,6 +78,13 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
     }
   }
   __syncthreads();
+  // fp8: the reciprocals of the scales (fp32 division, rounded once, as the
+  // host computes them when the scales are passed by value)
+  float k_inv = p.k_inv_scale, v_inv = p.v_inv_scale;
+  if (p.fp8 && p.kv_scale_dev) {
+    k_inv = 1.0f / p.kv_scale_dev[0];
+    v_inv = 1.0f / p.kv_scale_dev[1];
+  }
   const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
   const int per_tok = 2 * chunks;       // K chunks then V chunks
   const int total = nt * per_tok;
@@ -109,7 +116,7 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
       const bool is_v = c >= chunks;
       const int cc = is_v ? c - chunks : c;
       if (p.fp8) {
-        const float inv = is_v ? p.v_inv_scale : p.k_inv_scale;
+        const float inv = is_v ? v_inv : k_inv;
         uint8_t* d = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;
         u32x2 y;
         y[0] = enc2(x[k][0], inv) | (enc2(x[k][1], inv) << 16);

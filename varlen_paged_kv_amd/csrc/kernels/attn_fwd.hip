@@ -749,6 +749,19 @@ struct Src {
 };
 
 // ------------------------------------------------------------------ decode mode
+// The score factor (scale * log2 e, times k_scale for fp8) and the output
+// factor (v_scale for fp8): by value, or, when the call passes the fp8 scales
+// in device memory, derived from them here the way the host derives them (a
+// double product rounded once to float), so both give the same bits.
+__device__ __forceinline__ void scales(const AttnParams& p, float& qk, float& vs) {
+  qk = p.qk_scale_log2;
+  vs = p.v_scale;
+  if (p.kv_scale_dev) {
+    qk = static_cast<float>(p.scale_log2e * static_cast<double>(p.kv_scale_dev[0]));
+    vs = p.kv_scale_dev[1];
+  }
+}
+
 template <int D, int FMT, bool PAGED>
 struct Decode : Src<D, FMT, PAGED> {
   using B = Src<D, FMT, PAGED>;
@@ -769,7 +782,7 @@ struct Decode : Src<D, FMT, PAGED> {
   // keeps its own running max / sum / output; the four partial states are
   // merged through LDS at the end.
   __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
-                              uint16_t* smem, float c, int wave, int lr, int lg, int t) {
+                              uint16_t* smem, float c, float v_scale, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nb = it.kend > kbeg ? (it.kend - kbeg + DK - 1) / DK : 0;
@@ -883,7 +896,7 @@ struct Decode : Src<D, FMT, PAGED> {
         }
       }
       const bool live = lsum > 0.f;
-      const float inv = live ? p.v_scale / lsum : 0.f;
+      const float inv = live ? v_scale / lsum : 0.f;
       const float lse_v = live ? mmax * c * kLn2 + __logf(lsum) : -INFINITY;
       const int pr = row0 + r;
       const int tok = pr / p.g;
@@ -908,9 +921,11 @@ struct Decode : Src<D, FMT, PAGED> {
       append_tokens(p.app, blockIdx.x - p.attn_blocks, t, NT, reinterpret_cast<int64_t*>(smem));
       return;
     }
+    float qk, vs;
+    scales(p, qk, vs);
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
-      item(p, e.item, e.item.s, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+      item(p, e.item, e.item.s, it, smem, qk, vs, wave, lr, lg, t);
     });
   }
 };
@@ -933,7 +948,7 @@ struct Prefill : Src<D, FMT, PAGED> {
   static constexpr int F8PASS = (kBlockN * B::F8CH + NT - 1) / NT;
 
   __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
-                              uint16_t* smem, float c, int wave, int lr, int lg, int t) {
+                              uint16_t* smem, float c, float v_scale, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
@@ -1117,7 +1132,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     if (wr1 >= wr0) {
       const float l_tot = wave_pair_sum(l_run);
       const bool live = l_tot > 0.f;
-      const float inv = live ? p.v_scale / l_tot : 0.f;
+      const float inv = live ? v_scale / l_tot : 0.f;
       const float lse_v = live ? m_run * c * kLn2 + __logf(l_tot) : -INFINITY;
       if (row_ok) {
 #pragma unroll
@@ -1144,9 +1159,11 @@ struct Prefill : Src<D, FMT, PAGED> {
       append_tokens(p.app, blockIdx.x - p.attn_blocks, t, NT, reinterpret_cast<int64_t*>(smem));
       return;
     }
+    float qk, vs;
+    scales(p, qk, vs);
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
-      item(p, e.item, e.item.s, it, smem, p.qk_scale_log2, wave, lr, lg, t);
+      item(p, e.item, e.item.s, it, smem, qk, vs, wave, lr, lg, t);
     });
   }
 };

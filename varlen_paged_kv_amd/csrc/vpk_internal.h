@@ -86,6 +86,7 @@ struct AppendParams {
   int32_t fp8;
   float k_inv_scale;          // fp32(1 / k_scale)
   float v_inv_scale;
+  const float* kv_scale_dev;  // fp8: {k_scale, v_scale} in device memory, read at run time (overrides the two above)
 };
 
 struct AttnParams {
@@ -119,6 +120,8 @@ struct AttnParams {
   int32_t causal;
   float qk_scale_log2;        // scale * log2(e) (* k_scale for fp8)
   float v_scale;              // 1 (bf16) or v_scale (fp8)
+  const float* kv_scale_dev;  // fp8: {k_scale, v_scale} in device memory (overrides the two above)
+  double scale_log2e;         // scale * log2(e) in double, for the device-scale product
   AppendParams app;           // the append, when it runs inside this grid
 };
 
