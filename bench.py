@@ -58,15 +58,18 @@ def work_of(wl):
     return flops, kv_bytes
 
 
-def kernel_sha():
+ROPE_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/rope.hip", "varlen_paged_kv_amd/csrc/vpk_internal.h"]
+
+
+def kernel_sha(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def load_traffic(workload):
+def load_traffic(workload, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
@@ -76,7 +79,7 @@ def load_traffic(workload):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256") != kernel_sha():
+    if t.get("kernel_sha256") != kernel_sha(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -293,7 +296,8 @@ def main():
         rope_line = {"kernel": "rotary embedding of q and k_new", "rotary_dim": wl.D, "interleaved": False,
                      "kernel_avg_us": rus, "bytes": rbytes, "bound": "hbm",
                      "achieved": rbytes / max(rus, 1e-9) * 1e-3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": rbytes / max(rus, 1e-9) * 1e-3 / PEAK_HBM_GBS}
+                     "frac": rbytes / max(rus, 1e-9) * 1e-3 / PEAK_HBM_GBS,
+                     "traffic": load_traffic("rope_" + args.workload, ROPE_SOURCES)}
 
     cpu = None
     if not args.no_cpu_baseline and not args.rope:
