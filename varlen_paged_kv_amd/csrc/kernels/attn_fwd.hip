@@ -948,7 +948,7 @@ struct Prefill : Src<D, FMT, PAGED> {
   static constexpr int F8PASS = (kBlockN * B::F8CH + NT - 1) / NT;
 
   __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
-                              uint16_t* smem, float c, float v_scale, int wave, int lr, int lg, int t) {
+                              uint16_t* smem, int* lims, float c, float v_scale, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
     const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
@@ -995,8 +995,14 @@ struct Prefill : Src<D, FMT, PAGED> {
 
     // per-row and per-wave key bounds
     const int shift = sq.kv_len - sq.q_len;
-    int lim = it.kend - 1;
-    if (p.causal) lim = min(lim, token + shift);
+    {
+      // the row's last visible key, kept in LDS: only blocks that cross a
+      // row bound read it, and a register held across the loop for it
+      // would be spilled
+      int lim = it.kend - 1;
+      if (p.causal) lim = min(lim, token + shift);
+      lims[t] = lim - lg * 4;   // the softmax adds the lane half's offset back
+    }
     const int wr0 = wave * kWaveRows;
     const int wr1 = min(item.nrows, wr0 + kWaveRows) - 1;          // last valid row of the wave
     int wlo = it.kend - 1, whi = it.kend - 1;
@@ -1014,6 +1020,10 @@ struct Prefill : Src<D, FMT, PAGED> {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
     float m_run = -INFINITY;
+    // opaque start value: otherwise the compiler folds the first block's
+    // threshold m c + 8 into a constant that it keeps live (and spills)
+    // across the whole loop
+    asm volatile("" : "+v"(m_run));
     float l_run = 0.f;
     f32x16 acc[2];
     bf16x8 pf[2][2];
@@ -1048,7 +1058,8 @@ struct Prefill : Src<D, FMT, PAGED> {
     // complete at barrier n + 2.
     const bool group_b = wave >= NW / 2;
     auto sm = [&](int n, auto mask_tag) {
-      B::template softmax<2, decltype(mask_tag)::value>(acc, pf, o, m_run, l_run, kbeg + n * kBlockN, lim, c,
+      B::template softmax<2, decltype(mask_tag)::value>(acc, pf, o, m_run, l_run, kbeg + n * kBlockN,
+                                                         decltype(mask_tag)::value ? lims[t] + lg * 4 : 0, c,
                                                          lg);
     };
     // interval after barrier n: the caller's first MFMA phase, then start
@@ -1076,22 +1087,25 @@ struct Prefill : Src<D, FMT, PAGED> {
 
     // (an item without keys skips both: its rows get out = 0, lse = -inf)
     if (nblk > 0 && !group_b) {
+      // Group A runs the softmax of block n first and then one MFMA phase
+      // (P V of block n, scores of block n + 1), group B the reverse: each
+      // SIMD then always pairs one wave in its MFMA phase with one in its
+      // softmax, and no part of the interval has both waves issuing MFMAs
+      // while the vector ALU idles.  A's copies are issued at the start of
+      // the interval, B's after its first MFMA phase.
+      if (nb_w > 0) B::template qk0<2>(stage_of(0), qf, acc, lr, lg);   // scores of block 0
       auto body = [&](int n, auto mode_tag) {
-        constexpr int MODE = decltype(mode_tag)::value;   // 0 unmasked, 1 masked, 2 none
+        constexpr int MODE = decltype(mode_tag)::value;   // of block n: 0 unmasked, 1 masked, 2 none
         __syncthreads();                                    // barrier n
-        uint16_t* const kt = stage_of(n);
         interval(
-            n,
-            [&] {
-              __builtin_amdgcn_s_setprio(1);
-              if constexpr (MODE != 2) B::template qk0<2>(kt, qf, acc, lr, lg);
-            },
+            n, [] {},
             [&] {
               if constexpr (MODE != 2) {
                 __builtin_amdgcn_s_setprio(0);
                 sm(n, std::bool_constant<MODE == 1>{});
                 __builtin_amdgcn_s_setprio(1);
-                B::template pv0<2>(kt + C::TILE, pf, o, lr, lg);
+                B::template pv0<2>(stage_of(n) + C::TILE, pf, o, lr, lg);
+                if (n + 1 < nb_w) B::template qk0<2>(stage_of(n + 1), qf, acc, lr, lg);
               }
             });
       };
@@ -1149,6 +1163,7 @@ struct Prefill : Src<D, FMT, PAGED> {
   __device__ static void run(const AttnParams& p) {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * C::STAGE];
     __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
+    __shared__ int lims[NT];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
@@ -1163,7 +1178,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     scales(p, qk, vs);
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
-      item(p, e.item, e.item.s, it, smem, qk, vs, wave, lr, lg, t);
+      item(p, e.item, e.item.s, it, smem, lims, qk, vs, wave, lr, lg, t);
     });
   }
 };
