@@ -393,6 +393,39 @@ struct Src {
     }
   }
 
+  // a7 for a whole row pair of lanes: output block d (32 head-dim values) of
+  // this lane's row, from the O^T accumulator layout, where lane half lg
+  // holds values 8 i + 4 lg + (0..3), i = 0..3.  Two permlane32 swaps per 16
+  // values give lane half 0 the values 16 k + (0..7) and lane half 1 the
+  // values 16 k + 8 + (0..7), so each row is written as contiguous 16-byte
+  // pieces (half as many store instructions as 8-byte stores).
+  __device__ static __forceinline__ void store_out_block(const AttnParams& p, int q_start, int token, int qh,
+                                                         int d, const f32x16& od, float inv, int lg,
+                                                         bool row_ok) {
+    uint16_t* orow = p.out + (static_cast<int64_t>(q_start + token) * p.hq + qh) * D + d * 32 + lg * 8;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t x[2], y[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        x[e] = f32_to_bf16_rne(od[8 * k + 2 * e] * inv) |
+               (static_cast<uint32_t>(f32_to_bf16_rne(od[8 * k + 2 * e + 1] * inv)) << 16);
+        y[e] = f32_to_bf16_rne(od[8 * k + 4 + 2 * e] * inv) |
+               (static_cast<uint32_t>(f32_to_bf16_rne(od[8 * k + 4 + 2 * e + 1] * inv)) << 16);
+      }
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // vdst x: upper lanes receive y of the lower lanes; src y: lower
+        // lanes receive x of the upper lanes
+        const auto s = __builtin_amdgcn_permlane32_swap(x[e], y[e], false, false);
+        w[e] = s[0];
+        w[2 + e] = s[1];
+      }
+      if (row_ok) *reinterpret_cast<u32x4*>(orow + 16 * k) = w;
+    }
+  }
+
   // Work-queue entries of a workgroup, read from the plan once per chunk of
   // the queue into LDS (the plan lives in pinned host memory, so each read
   // crosses PCIe: one round trip per chunk instead of one per item).
@@ -1148,7 +1181,13 @@ struct Prefill : Src<D, FMT, PAGED> {
       const bool live = l_tot > 0.f;
       const float inv = live ? v_scale / l_tot : 0.f;
       const float lse_v = live ? m_run * c * kLn2 + __logf(l_tot) : -INFINITY;
-      if (row_ok) {
+      if (part < 0) {
+        // the two lanes of a row exchange values, so every lane of the wave
+        // runs the swaps; rows past the item's end store nothing
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) B::store_out_block(p, q_start, token, qh, d, o[d], inv, lg, row_ok);
+        if (row_ok && lg == 0 && p.lse) p.lse[static_cast<int64_t>(qh) * p.total_q + q_start + token] = lse_v;
+      } else if (row_ok) {
 #pragma unroll
         for (int d = 0; d < DBLK; ++d)
 #pragma unroll
