@@ -201,8 +201,12 @@ def test_fp8_encoder_every_bf16_pattern(scale):
     assert np.array_equal(vc_d.cpu().numpy(), rv)
 
 
-def _one_hot_case(S, cache, seed):
-    """Keys orthogonal (40 * e_code), each query aimed at one visible key: out must be that V row."""
+def _one_hot_case(S, cache, seed, all_codes_v=False):
+    """Keys orthogonal (40 * e_code), each query aimed at one visible key: out must be that V row.
+
+    all_codes_v (fp8): the V rows of each sequence and kv head run through every finite
+    non-zero e4m3fn code (subnormals, negatives and the largest magnitudes included), so
+    the widening of every such code reaches an output bit for bit."""
     rng = np.random.default_rng(seed)
     D, Hq, Hkv = 128, 8, 2
     g = Hq // Hkv
@@ -222,7 +226,13 @@ def _one_hot_case(S, cache, seed):
         for h in range(Hkv):
             for j in range(lk[b]):
                 K[cu_k[b] + j, h, codes[j]] = 40.0
-                if fp8:   # distinct e4m3 values per key: code pattern
+                if fp8 and all_codes_v:
+                    # codes 1..126 and 129..254 (0x7F / 0xFF are NaN, 0x80 is -0, whose
+                    # sum with +0 products is +0), in turn over keys and elements
+                    finite = np.concatenate([np.arange(1, 127), np.arange(129, 255)])
+                    V[cu_k[b] + j, h] = oracle.e4m3fn_decode(
+                        finite[(np.arange(D) + (j * 2 + h) * D) % len(finite)].astype(np.uint8))
+                elif fp8:   # distinct e4m3 values per key: code pattern
                     V[cu_k[b] + j, h] = oracle.e4m3fn_decode(((np.arange(D) * 3 + j * 5 + h) % 100 + 8).astype(np.uint8))
                 else:
                     V[cu_k[b] + j, h] = rng.standard_normal(D).astype(np.float32)
@@ -266,6 +276,22 @@ def _one_hot_case(S, cache, seed):
 def test_one_hot_gather_probe_bit_exact(S, cache):
     wl, expect = _one_hot_case(S, cache, seed=S * 10 + (cache == "fp8"))
     say(f"[case] one-hot probe S={S} cache={cache}")
+    out, _ = DeviceCall(wl).run()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"first mismatches at {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("S", [16, 64])
+def test_one_hot_probe_every_e4m3_code(S):
+    """The fp8 widening in the attention kernels (decode-mode and prefill-mode rows) is exact
+    on every finite non-zero e4m3fn code: each output row is its V row's decoded codes."""
+    wl, expect = _one_hot_case(S, "fp8", seed=77 + S, all_codes_v=True)
+    # the targeted rows reach every finite non-zero code (checked on the host)
+    vals = (expect.astype(np.uint32) << 16).view(np.float32)
+    reached = set(np.unique(oracle.e4m3fn_encode(vals.reshape(-1))).tolist())
+    assert set(range(1, 127)) | set(range(129, 255)) <= reached
+    say(f"[case] one-hot probe over every e4m3 code S={S}")
     out, _ = DeviceCall(wl).run()
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
     bad = np.argwhere(got != expect)

@@ -87,13 +87,12 @@ struct Cfg {
 };
 
 // Four e4m3fn codes (one dword) -> four bf16 values (two dwords), exactly:
-// v_cvt_pk_f32_fp8 widens OCP e4m3fn to fp32 on gfx950, and every e4m3fn value
-// is a bf16 value, so keeping the upper half of each fp32 loses nothing.
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 widens two OCP e4m3fn codes straight to
+// two bf16 values times a scale; with the scale 1 nothing is rounded, since
+// every e4m3fn value is a bf16 value (one instruction per two codes).
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, uint32_t& hi) {
-  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);   // bytes 0, 1
-  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);    // bytes 2, 3
-  lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));   // bytes 0, 1
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));    // bytes 2, 3
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
