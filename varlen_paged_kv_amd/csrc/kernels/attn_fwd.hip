@@ -1094,10 +1094,11 @@ struct Prefill : Src<D, FMT, PAGED> {
                                                          decltype(mask_tag)::value ? lims[t] + lg * 4 : 0, c,
                                                          lg);
     };
-    // interval after barrier n: the caller's first MFMA phase, then start
-    // staging block n + 3 (the copies of all eight waves are then not issued
-    // at the same moment), the rest of the work, then wait for block n + 2
-    // (bf16) or store block n + 3 (fp8)
+    // interval after barrier n: the caller's first part (nothing for group
+    // A, the MFMA phase for group B), then start staging block n + 3 (the
+    // copies of all eight waves are then not issued at the same moment), the
+    // rest of the work, then wait for block n + 2 (bf16) or store block n + 3
+    // (fp8)
     auto interval = [&](int n, auto&& first, auto&& rest) {
       first();
       int issued = 0;
@@ -1124,7 +1125,8 @@ struct Prefill : Src<D, FMT, PAGED> {
       // SIMD then always pairs one wave in its MFMA phase with one in its
       // softmax, and no part of the interval has both waves issuing MFMAs
       // while the vector ALU idles.  A's copies are issued at the start of
-      // the interval, B's after its first MFMA phase.
+      // the interval, B's after its MFMA phase (not between its P V and its
+      // scores, which split that phase and stretched A's).
       if (nb_w > 0) B::template qk0<2>(stage_of(0), qf, acc, lr, lg);   // scores of block 0
       auto body = [&](int n, auto mode_tag) {
         constexpr int MODE = decltype(mode_tag)::value;   // of block n: 0 unmasked, 1 masked, 2 none
@@ -1158,12 +1160,13 @@ struct Prefill : Src<D, FMT, PAGED> {
         interval(
             n,
             [&] {
+              // one MFMA phase, then the copies, then the softmax
               __builtin_amdgcn_s_setprio(1);
               if (n < nb_w) B::template pv0<2>(stage_of(n) + C::TILE, pf, o, lr, lg);
+              if constexpr (MODE != 2) B::template qk0<2>(stage_of(n + 1), qf, acc, lr, lg);
             },
             [&] {
               if constexpr (MODE != 2) {
-                B::template qk0<2>(stage_of(n + 1), qf, acc, lr, lg);
                 __builtin_amdgcn_s_setprio(0);
                 sm(n + 1, std::bool_constant<MODE == 1>{});
               }
