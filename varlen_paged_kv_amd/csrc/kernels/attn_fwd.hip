@@ -58,6 +58,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -716,6 +718,106 @@ struct Src {
         }
   }
 
+  // ---- fp8 cache, decode mode: raw e4m3fn code rows in LDS, widened when
+  //      the MFMA fragments are read.  A wave's 16 KB region (32 bf16 rows of
+  //      K and of V) holds 64 code rows of 128 bytes (head_dim 128) of K and
+  //      of V, so a wave keeps 64 keys in flight instead of the 32 it could
+  //      hold widened.  Chunk c (16 bytes) of code row r sits at c ^ f8swz(r):
+  //      the transposed V reads of a 16-lane group take chunks c and c ^ 1 of
+  //      rows {0..3, 8..11} (+ 4 or + 16 j), which then fall into distinct
+  //      bank groups.
+  static constexpr int F8ROW = D;   // bytes of a code row
+  __device__ static __forceinline__ int f8swz(int r) {
+    return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
+  }
+  // rows [0, 64) of a region <- keys [kbase, kbase + 64) of K (V_ROWS false)
+  // or V; rows past the item's end or on an unusable page read zeros; the
+  // calling wave issues 8 copies of 8 rows
+  template <bool V_ROWS>
+  __device__ static __forceinline__ void dma_raw8(const AttnParams& p, const Item& it, uint8_t* region, int kbase,
+                                                  int lane) {
+    const char* zeros = static_cast<const char*>(p.zeros);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ f8swz(r);
+      const char *kp, *vp;
+      const bool ok = row_src<true>(p, it, kbase + r, kp, vp);
+      dma16<true>(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, reinterpret_cast<uint16_t*>(region + i * 8 * F8ROW));
+    }
+  }
+  __device__ static __forceinline__ bf16x8 widen8(uint32_t c0, uint32_t c1) {
+    u32x4 w;
+    uint32_t a, b, x, y;
+    e4m3x4_to_bf16x4(c0, a, b);
+    e4m3x4_to_bf16x4(c1, x, y);
+    w[0] = a;
+    w[1] = b;
+    w[2] = x;
+    w[3] = y;
+    return __builtin_bit_cast(bf16x8, w);
+  }
+  // K operand of k-step s for code row r: head-dim values 16 s + 8 lg + (0..7)
+  __device__ static __forceinline__ bf16x8 kread8(const uint8_t* rk, int r, int s, int lg) {
+    const u32x2 v =
+        *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+            static_cast<uintptr_t>(lds_addr(reinterpret_cast<const uint16_t*>(rk + r * F8ROW + ((s ^ f8swz(r)) << 4) + lg * 8))));
+    return widen8(v[0], v[1]);
+  }
+  // V^T operand of key step j and output block d: keys 16 j + 4 lg + e and
+  // 16 j + 8 + 4 lg + e (e = 0..3) of head-dim value 32 d + lr, the key order
+  // of the P^T operand.  A 16-lane group addresses 8 code rows (lanes 2q and
+  // 2q + 1 the two halves of row q's 16-byte chunk); ds_read_b64_tr_b8 then
+  // gives lane i byte i of each of the 8 rows, in row order.
+  __device__ static __forceinline__ bf16x8 vread8(const uint8_t* rv, int j, int d, int lr, int lg) {
+    const int i = lr & 15;
+    const int q = i >> 1;
+    const int row = 16 * j + 4 * lg + (q & 3) + 8 * (q >> 2);
+    const int chunk = 2 * d + (lr >> 4);
+    const uint8_t* a = rv + row * F8ROW + ((chunk ^ f8swz(row)) << 4) + 8 * (i & 1);
+    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        reinterpret_cast<lds_i32x2*>(static_cast<uintptr_t>(lds_addr(reinterpret_cast<const uint16_t*>(a)))));
+    return widen8(static_cast<uint32_t>(x[0]), static_cast<uint32_t>(x[1]));
+  }
+  // a3..a6 over the 32 keys held in code rows [hrow0, hrow0 + 32) of the
+  // regions rk / rv (keys kbase ..), as compute<1, MASK> does for bf16 tiles
+  template <bool MASK>
+  __device__ static __forceinline__ void compute8(const uint8_t* rk, const uint8_t* rv, int hrow0,
+                                                  const bf16x8 (&qf)[C::KSTEPS], f32x16 (&o)[C::DBLK],
+                                                  float& m_run, float& l_run, int kbase, int lim, float c, int lr,
+                                                  int lg) {
+    constexpr int KH = C::KSTEPS / 2;
+    f32x16 acc[1];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[0][i] = 0.f;
+    bf16x8 kf[2][KH];
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s) kf[rnd][s] = kread8(rk, hrow0 + lr, rnd * KH + s, lg);
+#pragma unroll
+    for (int rnd = 0; rnd < 2; ++rnd)
+#pragma unroll
+      for (int s = 0; s < KH; ++s)
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[rnd][s], qf[rnd * KH + s], acc[0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* const rvh = rv + hrow0 * F8ROW;
+    bf16x8 vf[2][C::DBLK];
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d) vf[0][d] = vread8(rvh, 0, d, lr, lg);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 pf[1][2];
+    softmax<1, MASK>(acc, pf, o, m_run, l_run, kbase, lim, c, lg);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < C::DBLK; ++d) vf[1][d] = vread8(rvh, 1, d, lr, lg);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int d = 0; d < C::DBLK; ++d)
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[jj][d], pf[0][jj], o[d], 0, 0, 0);
+  }
+
   // ---- a3..a6 for this wave's 32 query rows over keys [kbase, kbase + 32 NH)
   //      held in tile rows [trow0, trow0 + 32 NH).  MASK: some key of the block
   //      lies beyond `lim` (the item's end, or the causal bound of the row).
@@ -877,9 +979,32 @@ struct Decode : Src<D, FMT, PAGED> {
     // this wave's blocks j = wave, wave + 4, ...: unmasked while at or below
     // the item's smallest key bound
     const int nb_full = min(nb, max(0, (tile_lim - kbeg + 1) / DK));
-    int j = wave;
-    for (; j < nb_full; j += kWaves) step(j, std::false_type{});
-    for (; j < nb; j += kWaves) step(j, std::true_type{});
+    if constexpr (FMT == kKvFp8 && D == 128) {
+      // fp8 codes staged raw: wave w takes the 64-key blocks w, w + 4, ...
+      // (two 32-key halves each) in its own region
+      uint8_t* const rk = reinterpret_cast<uint8_t*>(ktile + trow0 * D);
+      uint8_t* const rv = reinterpret_cast<uint8_t*>(vtile + trow0 * D);
+      const int nb64 = (nb + 1) / 2;
+      for (int jb = wave; jb < nb64; jb += kWaves) {
+        const int kbase = kbeg + jb * 2 * DK;
+        wait_lds();   // this wave's reads of its previous block are complete
+        B::template dma_raw8<false>(p, it, rk, kbase, lane);
+        B::template dma_raw8<true>(p, it, rv, kbase, lane);
+        wait_vmem();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int j32 = 2 * jb + hh;
+          if (j32 < nb_full)
+            B::template compute8<false>(rk, rv, hh * DK, qf, o, m_run, l_run, kbase + hh * DK, lim, c, lr, lg);
+          else if (j32 < nb)
+            B::template compute8<true>(rk, rv, hh * DK, qf, o, m_run, l_run, kbase + hh * DK, lim, c, lr, lg);
+        }
+      }
+    } else {
+      int j = wave;
+      for (; j < nb_full; j += kWaves) step(j, std::false_type{});
+      for (; j < nb; j += kWaves) step(j, std::true_type{});
+    }
 
     // ---- combine the four waves' states through LDS
     __syncthreads();                     // every wave is done with its stage
