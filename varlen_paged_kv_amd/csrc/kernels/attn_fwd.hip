@@ -1114,7 +1114,13 @@ struct Prefill : Src<D, FMT, PAGED> {
 
     // ---- staging of block j into stage j mod NS: this wave's WROWS rows of K
     //      and V (bf16), or the block through registers (fp8)
-    auto stage_of = [&](int j) { return smem + (j & (NS - 1)) * C::STAGE; };
+    // fp8 cache, head_dim 128: three bf16 stages and two raw-code areas in
+    // the same LDS (below); otherwise four bf16 stages
+    constexpr bool RAW8 = FMT == kKvFp8 && D == 128;
+    auto stage_of = [&](int j) {
+      if constexpr (RAW8) return smem + (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j)) % 3u) * C::STAGE;
+      else return smem + (j & (NS - 1)) * C::STAGE;
+    };
     auto stage_dma = [&](int j) {
       const int kbase = kbeg + j * kBlockN;
       uint16_t* const kt = stage_of(j);
@@ -1140,6 +1146,39 @@ struct Prefill : Src<D, FMT, PAGED> {
     auto f8_store = [&](int j) {
       B::template f8_store<F8PASS>(fk, stage_of(j), 0, kBlockN, t, NT);
       B::template f8_store<F8PASS>(fv, stage_of(j) + C::TILE, 0, kBlockN, t, NT);
+    };
+    // RAW8: block j's codes (64 rows of 128 bytes of K, then of V) go by DMA
+    // into raw area j mod 2, each wave its own 8 rows (one copy per tile);
+    // the same wave later widens those rows into bf16 stage j mod 3.  Lane l
+    // moves chunk l mod 8 (16 codes) of row 8 wave + l / 8 both times, so it
+    // reads back only what its own copy wrote.
+    uint8_t* const raw0 = reinterpret_cast<uint8_t*>(smem + 3 * C::STAGE);
+    auto raw_of = [&](int j) { return raw0 + (j & 1) * (2 * kBlockN * D); };
+    auto raw_dma = [&](int j) {
+      const int r = wave * 8 + (lane >> 3);
+      const char *kp, *vp;
+      const bool ok = B::template row_src<true>(p, it, kbeg + j * kBlockN + r, kp, vp);
+      const char* zeros = static_cast<const char*>(p.zeros);
+      const int off = (lane & 7) * 16;
+      uint8_t* const a = raw_of(j) + wave * 8 * D;
+      dma16<true>(ok ? kp + off : zeros, reinterpret_cast<uint16_t*>(a));
+      dma16<true>(ok ? vp + off : zeros, reinterpret_cast<uint16_t*>(a + kBlockN * D));
+    };
+    auto raw_convert = [&](int j) {
+      const int r = wave * 8 + (lane >> 3);
+      const int cc = lane & 7;
+      const uint8_t* const a = raw_of(j) + r * D + cc * 16;
+      uint16_t* const st = stage_of(j);
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const u32x4 codes = *reinterpret_cast<const u32x4*>(a + kv * kBlockN * D);
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) e4m3x4_to_bf16x4(codes[e], w[2 * e], w[2 * e + 1]);
+        uint16_t* const tile = st + kv * C::TILE;
+        *reinterpret_cast<u32x4*>(tile + C::at(r, 2 * cc)) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(tile + C::at(r, 2 * cc + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+      }
     };
 
     // Q rows first: their loads are older than the staging copies, so the
@@ -1187,7 +1226,20 @@ struct Prefill : Src<D, FMT, PAGED> {
 
     // ---- prologue: blocks 0..2 staged, 0 and 1 complete before the first
     //      barrier (fp8: all three stored)
-    if constexpr (FMT == kKvFp8) {
+    if constexpr (RAW8) {
+      // blocks 0 and 1 copied and widened; block 2 copied into the raw area
+      // block 0 has left
+      if (nblk > 0) raw_dma(0);
+      if (nblk > 1) raw_dma(1);
+      wait_vmem();
+      // Q is complete too: said here, before block 2's copy is issued, so
+      // that the compiler's own wait for Q does not cover that copy
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) asm volatile("" : : "v"(qf[s]));
+      if (nblk > 0) raw_convert(0);
+      if (nblk > 1) raw_convert(1);
+      if (nblk > 2) raw_dma(2);
+    } else if constexpr (FMT == kKvFp8) {
       for (int j = 0; j < 3 && j < nblk; ++j) {
         f8_load(j);
         f8_store(j);
@@ -1225,6 +1277,22 @@ struct Prefill : Src<D, FMT, PAGED> {
     // rest of the work, then wait for block n + 2 (bf16) or store block n + 3
     // (fp8)
     auto interval = [&](int n, auto&& first, auto&& rest) {
+      if constexpr (RAW8) {
+        // copy block n + 3 (into the raw area block n + 1 has left), then
+        // widen block n + 2 into the stage block n - 1 has left
+        first();
+        int issued = 0;
+        if (n + 3 < nblk) {
+          raw_dma(n + 3);
+          issued = 2;
+        }
+        rest();
+        if (n + 2 < nblk) {
+          wait_vmem_upto(issued);
+          raw_convert(n + 2);
+        }
+        return;
+      }
       first();
       int issued = 0;
       if constexpr (FMT == kKvFp8) {
