@@ -1,20 +1,33 @@
-"""Benchmark: one step = one attn_varlen_paged_fwd call (append + plan upload +
+"""Benchmark: one step = one attn_varlen_paged_fwd call (append + planning +
 attention + split merge) over a seeded synthetic batch on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rope]
 
-Default workload: varlen prefill without a cache (16 sequences, lengths
-U[256, 2048], 32 query / 8 kv heads, head_dim 128, bf16, causal).  Other names:
-paged_decode, chunked_prefill, mixed_fp8, tiny.
+Default (no --workload): the four full-size workloads in one run, one JSON
+line.  The headline (`value`, `roofline`, `cpu_baseline`) is varlen prefill
+without a cache (16 sequences, lengths U[256, 2048], 32 query / 8 kv heads,
+head_dim 128, bf16, causal): prefill TFLOP/s.  The line also carries
+`decode` (paged decode, KV GB/s against HBM), `chunked_prefill` (TFLOP/s) and
+`mixed_fp8` (the mixed prefill + decode batch over an fp8 cache: the step,
+the prefill rows alone, the decode rows alone, the fused / serial ratio and
+the combined roofline fraction), each with its own roofline and CPU baseline.
+With --workload NAME only that workload is measured and it is the headline
+(names: varlen_prefill, paged_decode, chunked_prefill, mixed_fp8, tiny).
 
-Prints ONE JSON line.  `value` is the algorithmic throughput of the whole step
-(inputs resident in HBM): prefill TFLOP/s (4 * D flops per visible (query, key)
-pair per query head) or, for pure decode, KV-cache GB/s (Lk * Hkv * D * 2 *
-bytes per element per sequence).  `roofline` is the attention kernel alone,
-timed with HIP events recorded by the library on the launch stream.
-With --rope each step is attn_varlen_paged_rope_fwd (rotary embedding of q
-and k_new first, rotary_dim = head_dim, half-split pairing) and the line also
-carries the rotation kernel's own time and bandwidth.
+Per workload: W warm-up steps, then untimed steps for --settle seconds (the
+GPU's clocks ramp up from idle over hundreds of milliseconds), then an
+instrumented pass (the library brackets
+every kernel launch with HIP events on its launch stream: per-kernel
+durations), then the timed pass of exactly K steps between two
+synchronisations (no per-launch events) that gives `value` and `ms_per_step`.
+Inputs rotate over several device copies so that the 256 MB MALL cannot
+serve a previous step's K/V.
+
+Algorithmic work: prefill FLOPs = 4 * D per visible (query, key) pair per
+query head; decode bytes = Lk * Hkv * D * 2 * bytes per cached element per
+sequence.  With --rope each step is attn_varlen_paged_rope_fwd (rotary
+embedding of q and k_new, rotary_dim = head_dim, half-split pairing) and the
+line carries the rotation kernel's own time and bandwidth.
 """
 from __future__ import annotations
 
@@ -35,6 +48,12 @@ PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/attn_fwd.hip", "varlen_paged_kv_amd/csrc/kernels/append_dev.h",
                   "varlen_paged_kv_amd/csrc/vpk_internal.h"]
+ROPE_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/rope.hip", "varlen_paged_kv_amd/csrc/vpk_internal.h"]
+SUITE = ["varlen_prefill", "paged_decode", "chunked_prefill", "mixed_fp8"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def visible_pairs(ql, kl, causal):
@@ -58,7 +77,9 @@ def work_of(wl):
     return flops, kv_bytes
 
 
-ROPE_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/rope.hip", "varlen_paged_kv_amd/csrc/vpk_internal.h"]
+def decode_rows(wl):
+    """Sequences served by the decode-mode grid (q_len * g <= 32 packed rows)."""
+    return wl.q_lens() * (wl.Hq // wl.Hkv) <= 32
 
 
 def kernel_sha(sources=None):
@@ -69,9 +90,9 @@ def kernel_sha(sources=None):
     return h.hexdigest()
 
 
-def load_traffic(workload, sources=None):
+def load_traffic(name, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(path):
         return None
     try:
@@ -84,7 +105,7 @@ def load_traffic(workload, sources=None):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s):
     """Time the oracle (as it stands) on a bounded sample of the same workload."""
     import oracle
     from threadpoolctl import threadpool_info
@@ -95,7 +116,7 @@ def cpu_baseline(wl, budget_s=12.0):
             threads = max(threads, int(info.get("num_threads", 0)))
     threads = threads or (os.cpu_count() or 1)
     flops, kv_bytes = work_of(wl)
-    decode = wl.name == "paged_decode"
+    by_bytes = wl.name == "paged_decode"
     # append first (part of the call), then attention sequence by sequence
     t0 = time.perf_counter()
     if wl.k_cache is not None and wl.k_new is not None:
@@ -106,7 +127,7 @@ def cpu_baseline(wl, budget_s=12.0):
         kc, vc = wl.k_cache, wl.v_cache
     t_append = time.perf_counter() - t0
     done, work, elapsed = [], 0.0, 0.0
-    order = np.argsort(-(flops if not decode else kv_bytes))[::-1]   # smallest first
+    order = np.argsort(-(kv_bytes if by_bytes else flops + kv_bytes))[::-1]   # smallest first
     passes = 0
     while elapsed < budget_s and passes < 8:   # the whole batch again while under budget
         passes += 1
@@ -122,13 +143,13 @@ def cpu_baseline(wl, budget_s=12.0):
                 oracle.attend(oracle.bf16_bits_to_f64(wl.q[s:e]), K, V, wl.causal, wl.scale)
             elapsed += time.perf_counter() - t0
             done.append(b)
-            work += float(kv_bytes[b] if decode else flops[b])
+            work += float(kv_bytes[b] if by_bytes else flops[b])
             if elapsed >= budget_s:
                 break
     # the append over the whole batch is charged pro rata to the sample
     frac = len(done) / wl.B
     elapsed += t_append * frac
-    if decode:
+    if by_bytes:
         value, unit = work / elapsed / 1e9, "GB/s"
     else:
         value, unit = work / elapsed / 1e12, "TFLOP/s"
@@ -138,18 +159,217 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"numpy float64, plus the batch's append pro rata; {elapsed:.1f} s"}
 
 
+class Runner:
+    """Device copies of one workload's inputs and the timing passes over them."""
+
+    def __init__(self, wl, dev, rotate, rope=False):
+        import torch
+        import varlen_paged_kv_amd as vpk
+        self.torch, self.vpk, self.wl = torch, vpk, wl
+        self.fp8 = wl.cache_dtype == "fp8"
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+        self.copies = []
+        for _ in range(max(1, rotate)):
+            c = dict(q=bf16(wl.q), cu_q=i32(wl.cu_seqlens_q))
+            c["k_new"] = bf16(wl.k_new) if wl.k_new is not None else None
+            c["v_new"] = bf16(wl.v_new) if wl.v_new is not None else None
+            c["cu_kn"] = i32(wl.cu_seqlens_knew) if wl.cu_seqlens_knew is not None else None
+            if wl.k_cache is not None:
+                mk = (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)) if self.fp8 else bf16
+                c["kc"], c["vc"] = mk(wl.k_cache), mk(wl.v_cache)
+                c["bt"], c["cl"] = i32(wl.block_table), i32(wl.cache_seqlens)
+            else:
+                c["kc"] = c["vc"] = c["bt"] = c["cl"] = None
+            c["out"] = torch.empty_like(c["q"])
+            c["lse"] = torch.empty((wl.Hq, wl.Tq), dtype=torch.float32, device=dev)
+            self.copies.append(c)
+        self.host = dict(cu_seqlens_q=wl.cu_seqlens_q, cu_seqlens_knew=wl.cu_seqlens_knew,
+                         cache_seqlens=wl.cache_seqlens, block_table=wl.block_table)
+        self.rope_kw = None
+        if rope:
+            from synth import rope_tables
+            cos, sin = rope_tables(int(wl.kv_lens().max()), wl.D)
+            self.rope_kw = dict(rope_cos=torch.from_numpy(cos).to(dev), rope_sin=torch.from_numpy(sin).to(dev),
+                                rotary_dim=wl.D, interleaved=False)
+
+    def step(self, i):
+        wl, c = self.wl, self.copies[i % len(self.copies)]
+        args = (c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"], c["vc"], c["bt"], c["cl"],
+                wl.page_size, wl.causal, wl.scale, wl.kv_scale if self.fp8 else None)
+        if self.rope_kw is None:
+            self.vpk.attn_varlen_paged_fwd(*args, out=c["out"], lse=c["lse"], host_index=self.host)
+        else:
+            self.vpk.attn_varlen_paged_rope_fwd(*args, **self.rope_kw, out=c["out"], lse=c["lse"],
+                                                host_index=self.host)
+
+    def timed(self, steps, instrumented):
+        """`steps` steps between two synchronisations; with `instrumented`, the library also
+        brackets every kernel launch with HIP events on its launch stream."""
+        torch, vpk = self.torch, self.vpk
+        vpk.timing_reset()
+        vpk.timing_enable(instrumented)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            self.step(i)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        vpk.timing_enable(False)
+        return start.elapsed_time(end), wall
+
+    def measure(self, steps, warmup, settle_s):
+        """Warm-up, clock settling, instrumented pass (per-kernel averages, us), timed pass (ms per step)."""
+        vpk = self.vpk
+        for i in range(warmup):
+            self.step(i)
+        self.torch.cuda.synchronize()
+        # keep the GPU busy until its clocks have settled (an idle GPU ramps up over
+        # hundreds of milliseconds; a short warm-up alone would time the ramp)
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < settle_s:
+            for _ in range(8):
+                self.step(n)
+                n += 1
+            self.torch.cuda.synchronize()
+        self.settle_steps = n
+        inst_ms, _ = self.timed(steps, True)
+        kern = {}
+        for key, kid in (("prefill_grid", vpk.KERNEL_ATTENTION), ("decode_grid", vpk.KERNEL_ATTENTION_DECODE),
+                         ("append", vpk.KERNEL_APPEND), ("merge", vpk.KERNEL_MERGE), ("rope", vpk.KERNEL_ROPE)):
+            ms, n = vpk.timing_read(kid)
+            kern[key] = (ms * 1e3 / n if n else 0.0, n)
+        gpu_ms, wall = self.timed(steps, False)
+        return dict(ms_per_step=gpu_ms / steps, host_us_per_step=wall * 1e6 / steps,
+                    inst_us_per_step=inst_ms * 1e3 / steps, kernels=kern, settle_steps=self.settle_steps)
+
+
+def kernel_note(m, steps):
+    return ("HIP events recorded by the library around each launch on its launch stream, over an "
+            f"instrumented pass of {steps} steps before the timed pass "
+            f"({m['inst_us_per_step']:.1f} us/step with the events)")
+
+
+def summary(name, m):
+    k = m["kernels"]
+    parts = ", ".join(f"{key} {us:.1f} us x{n}" for key, (us, n) in k.items() if n)
+    return (f"{name}: {m['ms_per_step'] * 1e3:.1f} us/step after {m['settle_steps']} settling steps "
+            f"(host {m['host_us_per_step']:.1f} us/step; "
+            f"instrumented pass {m['inst_us_per_step']:.1f} us/step); {parts}")
+
+
+def mfma_roof(flops, us, traffic, note):
+    ach = flops / (us / 1e6) / 1e12 if us > 0 else 0.0
+    return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": "attention (prefill-mode grid)",
+            "kernel_avg_us": us, "kernel_timing": note}
+
+
+def hbm_roof(nbytes, us, traffic, note, kernel="attention (decode-mode grid)"):
+    ach = nbytes / (us / 1e6) / 1e9 if us > 0 else 0.0
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "kernel": kernel,
+            "kernel_avg_us": us, "kernel_timing": note}
+
+
+def config_of(wl, flops, kv_bytes, rope):
+    return {"workload": wl.name, "batch": wl.B, "total_q": wl.Tq, "total_new": wl.Tn, "q_heads": wl.Hq,
+            "kv_heads": wl.Hkv, "head_dim": wl.D, "page_size": wl.page_size, "causal": wl.causal,
+            "kv_cache": wl.cache_dtype or "none", "pages": wl.num_pages, "flops_per_step": flops,
+            "kv_bytes_per_step": kv_bytes, "parallelism": "single GPU",
+            **({"rope": "rotary_dim=head_dim, half-split"} if rope else {})}
+
+
+def measure_workload(name, args, dev, cpu_budget):
+    """One workload's object: throughput of the whole step, roofline of its dominant kernel,
+    CPU baseline; the mixed batch also times its prefill and decode rows alone."""
+    from synth import make_workload, subset
+    t0 = time.perf_counter()
+    wl = make_workload(name)
+    flops, kv_bytes = work_of(wl)
+    step_flops, step_bytes = float(flops.sum()), float(kv_bytes.sum())
+    dec = decode_rows(wl)
+    pre_flops, dec_bytes = float(flops[~dec].sum()), float(kv_bytes[dec].sum())
+    log(f"{name}: Tq={wl.Tq} Tn={wl.Tn} pages={wl.num_pages} flops/step={step_flops:.3e} "
+        f"kv bytes/step={step_bytes:.3e} (inputs drawn in {time.perf_counter() - t0:.1f} s)")
+    r = Runner(wl, dev, args.rotate, rope=args.rope)
+    m = r.measure(args.steps, args.warmup, args.settle)
+    log(summary(name, m))
+    k = m["kernels"]
+    note = kernel_note(m, args.steps)
+    elapsed = m["ms_per_step"] / 1e3
+    obj = {"workload": name, "ms_per_step": m["ms_per_step"], "config": config_of(wl, step_flops, step_bytes,
+                                                                                      args.rope)}
+    if name == "paged_decode":
+        obj.update(value=step_bytes / elapsed / 1e9, unit="GB/s")
+        obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_HBM_GBS
+        obj["roofline"] = hbm_roof(dec_bytes, k["decode_grid"][0], load_traffic(name), note)
+        obj["roofline"]["merge_avg_us"] = k["merge"][0]
+    elif name == "mixed_fp8":
+        obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
+        obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
+        roof = mfma_roof(pre_flops, k["prefill_grid"][0], load_traffic(name), note)
+        roof["decode_grid"] = hbm_roof(dec_bytes, k["decode_grid"][0], None, note)
+        # the whole step against both roofs at once: prefill FLOPs at the bf16 peak plus
+        # decode KV bytes at the HBM peak, over the step time
+        roof["combined_frac"] = (pre_flops / (PEAK_BF16_TFLOPS * 1e12) + dec_bytes / (PEAK_HBM_GBS * 1e9)) / elapsed
+        obj["roofline"] = roof
+        del r
+        parts = {}
+        for label, seqs in (("prefill_rows", np.nonzero(~dec)[0]), ("decode_rows", np.nonzero(dec)[0])):
+            sub = subset(wl, seqs)
+            rs = Runner(sub, dev, args.rotate)
+            ms = rs.measure(args.steps, args.warmup, args.settle)
+            log(summary(f"{name} {label} alone", ms))
+            parts[label] = ms["ms_per_step"]
+            del rs
+        obj["parts_alone_ms"] = parts
+        obj["fused_over_serial"] = m["ms_per_step"] / (parts["prefill_rows"] + parts["decode_rows"])
+    else:
+        obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
+        obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
+        obj["roofline"] = mfma_roof(pre_flops, k["prefill_grid"][0], load_traffic(name), note)
+    if args.rope:
+        # algorithmic bytes: q and k_new read once and written once (bf16)
+        rbytes = 2.0 * 2.0 * wl.D * (wl.Tq * wl.Hq + wl.Tn * wl.Hkv)
+        rus = k["rope"][0]
+        obj["rope_kernel"] = {"kernel": "rotary embedding of q and k_new", "rotary_dim": wl.D,
+                              "interleaved": False, "kernel_avg_us": rus, "bytes": rbytes, "bound": "hbm",
+                              "achieved": rbytes / max(rus, 1e-9) * 1e-3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": rbytes / max(rus, 1e-9) * 1e-3 / PEAK_HBM_GBS,
+                              "traffic": load_traffic("rope_" + name, ROPE_SOURCES)}
+    obj["cpu_baseline"] = None
+    if cpu_budget > 0:
+        log(f"{name}: timing the CPU oracle on a bounded sample")
+        obj["cpu_baseline"] = cpu_baseline(wl, cpu_budget)
+    return obj
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="varlen_prefill",
-                    choices=["varlen_prefill", "paged_decode", "chunked_prefill", "mixed_fp8", "tiny"])
+    ap.add_argument("--workload", default=None,
+                    choices=["varlen_prefill", "paged_decode", "chunked_prefill", "mixed_fp8", "tiny"],
+                    help="measure this workload alone (default: the four full-size workloads)")
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through (defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=6.0, help="seconds of oracle time per workload")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps after the warm-up, before the passes (clock ramp)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for HBM counters)")
     ap.add_argument("--persistent", type=int, default=-1)
+    ap.add_argument("--plan-upload", type=int, default=0, help="library option plan_upload (0 or 1)")
     ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
     args = ap.parse_args()
 
@@ -160,46 +380,11 @@ def main():
 
     import torch
     import varlen_paged_kv_amd as vpk
-    from synth import make_workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    wl = make_workload(args.workload)
-    flops, kv_bytes = work_of(wl)
-    step_flops, step_bytes = float(flops.sum()), float(kv_bytes.sum())
-    decode = args.workload == "paged_decode"
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-
-    fp8 = wl.cache_dtype == "fp8"
-    copies = []
-    for _ in range(max(1, args.rotate)):
-        c = dict(q=bf16(wl.q), cu_q=i32(wl.cu_seqlens_q))
-        c["k_new"] = bf16(wl.k_new) if wl.k_new is not None else None
-        c["v_new"] = bf16(wl.v_new) if wl.v_new is not None else None
-        c["cu_kn"] = i32(wl.cu_seqlens_knew) if wl.cu_seqlens_knew is not None else None
-        if wl.k_cache is not None:
-            mk = (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)) if fp8 else bf16
-            c["kc"], c["vc"] = mk(wl.k_cache), mk(wl.v_cache)
-            c["bt"], c["cl"] = i32(wl.block_table), i32(wl.cache_seqlens)
-        else:
-            c["kc"] = c["vc"] = c["bt"] = c["cl"] = None
-        c["out"] = torch.empty_like(c["q"])
-        c["lse"] = torch.empty((wl.Hq, wl.Tq), dtype=torch.float32, device=dev)
-        copies.append(c)
-    host = dict(cu_seqlens_q=wl.cu_seqlens_q, cu_seqlens_knew=wl.cu_seqlens_knew,
-                cache_seqlens=wl.cache_seqlens, block_table=wl.block_table)
     vpk.set_option("persistent", args.persistent)
-    rope_kw = None
-    if args.rope:
-        from synth import rope_tables
-        cos, sin = rope_tables(int(wl.kv_lens().max()), wl.D)
-        rope_kw = dict(rope_cos=torch.from_numpy(cos).to(dev), rope_sin=torch.from_numpy(sin).to(dev),
-                       rotary_dim=wl.D, interleaved=False)
+    vpk.set_option("plan_upload", args.plan_upload)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -209,119 +394,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(i):
-        c = copies[i % len(copies)]
-        args_ = (c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"], c["vc"], c["bt"], c["cl"],
-                 wl.page_size, wl.causal, wl.scale, wl.kv_scale if fp8 else None)
-        if rope_kw is None:
-            vpk.attn_varlen_paged_fwd(*args_, out=c["out"], lse=c["lse"], host_index=host)
-        else:
-            vpk.attn_varlen_paged_rope_fwd(*args_, **rope_kw, out=c["out"], lse=c["lse"], host_index=host)
-
-    print(f"[bench] {args.workload}: Tq={wl.Tq} Tn={wl.Tn} pages={wl.num_pages} "
-          f"flops/step={step_flops:.3e} kv bytes/step={step_bytes:.3e}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    def timed(instrumented):
-        """K steps between two synchronisations; with `instrumented`, the
-        library also brackets every kernel launch with HIP events on its
-        launch stream (per-kernel durations; the extra events cost a few us
-        per launch, so the throughput figure comes from the plain pass)."""
-        vpk.timing_reset()
-        vpk.timing_enable(instrumented)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for i in range(args.steps):
-            step(i)
-        end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        vpk.timing_enable(False)
-        return start.elapsed_time(end), wall
-
-    gpu_ms, wall = timed(False)                 # the timed region of the throughput figure
-    inst_ms, _ = timed(True)                    # the same steps again, per-kernel events on
-    pre_ms, pre_n = vpk.timing_read(vpk.KERNEL_ATTENTION)
-    dec_ms, dec_n = vpk.timing_read(vpk.KERNEL_ATTENTION_DECODE)
-    app_ms, app_n = vpk.timing_read(vpk.KERNEL_APPEND)
-    mrg_ms, mrg_n = vpk.timing_read(vpk.KERNEL_MERGE)
-    rot_ms, rot_n = vpk.timing_read(vpk.KERNEL_ROPE)
-    elapsed = max(gpu_ms / 1e3, 1e-9)
-    ms_per_step = gpu_ms / args.steps
-    avg = lambda ms, n: ms / max(n, 1)
-    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (host {wall * 1e6 / args.steps:.1f} us/step; "
-          f"instrumented pass {inst_ms * 1e3 / args.steps:.1f} us/step); "
-          f"attention prefill-mode {avg(pre_ms, pre_n) * 1e3:.1f} us x{pre_n}, decode-mode "
-          f"{avg(dec_ms, dec_n) * 1e3:.1f} us x{dec_n}, standalone append {avg(app_ms, app_n) * 1e3:.1f} us x{app_n}, "
-          f"merge {avg(mrg_ms, mrg_n) * 1e3:.1f} us x{mrg_n}, rotary {avg(rot_ms, rot_n) * 1e3:.1f} us x{rot_n}",
-          file=sys.stderr, flush=True)
-
-    # work of the sequences each grid serves (decode-mode: q_len * g <= 32 rows)
-    dec_seq = wl.q_lens() * (wl.Hq // wl.Hkv) <= 32
-    pre_flops = float(flops[~dec_seq].sum())
-    dec_bytes = float(kv_bytes[dec_seq].sum())
-    if decode:
-        value, unit = step_bytes * args.steps / elapsed / 1e9, "GB/s"
-        kus = avg(dec_ms, dec_n) * 1e3
-        achieved = step_bytes / (kus / 1e6) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "kernel": "attention (decode-mode grid)"}
-    else:
-        value, unit = step_flops * args.steps / elapsed / 1e12, "TFLOP/s"
-        kus = avg(pre_ms, pre_n) * 1e3
-        achieved = pre_flops / (kus / 1e6) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "kernel": "attention (prefill-mode grid)"}
-        if dec_n:
-            dus = avg(dec_ms, dec_n) * 1e3
-            roof["decode_grid"] = {"bound": "hbm", "achieved": dec_bytes / (dus / 1e6) / 1e9,
-                                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "kernel_avg_us": dus}
-    roof["traffic"] = load_traffic(args.workload)
-    roof["kernel_avg_us"] = kus
-    roof["kernel_timing"] = ("HIP events recorded by the library around each launch on its launch stream, "
-                             f"over a second pass of the same {args.steps} steps "
-                             f"({inst_ms * 1e3 / args.steps:.1f} us/step with the events)")
-
-    rope_line = None
-    if args.rope:
-        # algorithmic bytes: q and k_new read once and written once (bf16); the
-        # angle tables (max_pos x D/2 x 8 bytes) are re-read through the caches
-        rbytes = 2.0 * 2.0 * wl.D * (wl.Tq * wl.Hq + wl.Tn * wl.Hkv)
-        rus = avg(rot_ms, rot_n) * 1e3
-        rope_line = {"kernel": "rotary embedding of q and k_new", "rotary_dim": wl.D, "interleaved": False,
-                     "kernel_avg_us": rus, "bytes": rbytes, "bound": "hbm",
-                     "achieved": rbytes / max(rus, 1e-9) * 1e-3, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": rbytes / max(rus, 1e-9) * 1e-3 / PEAK_HBM_GBS,
-                     "traffic": load_traffic("rope_" + args.workload, ROPE_SOURCES)}
-
-    cpu = None
-    if not args.no_cpu_baseline and not args.rope:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl)
-
+    names = [args.workload] if args.workload else SUITE
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_budget
+    objs = {}
+    for name in names:
+        objs[name] = measure_workload(name, args, dev, budget)
+        torch.cuda.empty_cache()
+    head = objs[names[0]]
     line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) values, lengths and page tables drawn per the workload recipe)",
-        "config": {"workload": args.workload, "batch": wl.B, "total_q": wl.Tq, "total_new": wl.Tn,
-                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D,
-                   "page_size": wl.page_size, "causal": wl.causal,
-                   "kv_cache": wl.cache_dtype or "none", "pages": wl.num_pages,
-                   "flops_per_step": step_flops, "kv_bytes_per_step": step_bytes,
-                   "parallelism": "single GPU", **({"rope": "rotary_dim=head_dim, half-split"}
-                                                   if args.rope else {})},
-        "pct_of_peak": 100.0 * value / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS),
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": head["config"], "pct_of_peak": head["pct_of_peak"], "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    if rope_line is not None:
-        line["rope_kernel"] = rope_line
+    if "rope_kernel" in head:
+        line["rope_kernel"] = head["rope_kernel"]
+    for name in names[1:]:
+        line["decode" if name == "paged_decode" else name] = objs[name]
     print(json.dumps(line), flush=True)
 
 

@@ -50,10 +50,16 @@
  * advances it, as with the cache-length parameter of the flash-attention page.
  * Device buffers must be 16-byte aligned (lse: 4-byte).
  *
- * The library keeps a per-device, per-stream workspace (work list, split
- * partials) that it allocates on first use and grows as needed; two calls that
- * overlap in time on one device must therefore use the same stream or
- * different streams, never the same stream from two host threads at once.
+ * Workspace: split partials, the device error flag and (attn_varlen_paged_rope_fwd)
+ * the turned copies of q and k_new live in a per-device, per-stream workspace
+ * in device memory.  The caller provides it with vpk_set_workspace (sized by
+ * vpk_workspace_bytes_upper_bound; the Python binding does this with a torch
+ * tensor, so that PyTorch owns the device memory); a stream without one gets a
+ * library-allocated workspace that grows as needed (the fallback).  The work
+ * list of a direct call is written into a small ring of pinned host buffers
+ * that the kernels read directly.  Two calls that overlap in time on one
+ * device must use the same stream or different streams, never the same stream
+ * from two host threads at once.
  *
  * Errors: every entry point returns a vpk_status; nothing throws or aborts.
  * vpk_last_error() gives a message for the calling thread's last failure.
@@ -102,11 +108,13 @@ typedef struct {
 /* Host copies of the index arrays (same contents as the device arrays).  The
  * work list is planned from these.  Any member may be NULL: the library then
  * copies the device array to the host with a blocking copy on `stream` (slow
- * path; not allowed inside stream capture).  block_table, when given, lets the
- * host reject page ids outside [0, num_pages) for the slots that are read or
- * written; without it the kernels skip such pages (their keys read as zero and
- * appends to them are dropped) and raise a device error flag that
- * vpk_device_error() returns. */
+ * path).  block_table, when given, lets the host reject page ids outside
+ * [0, num_pages) for the slots that are read or written; without it the
+ * kernels skip such pages and raise a device error flag that
+ * vpk_device_error() returns: appends to such a page are dropped and its
+ * slots read as zero keys and values (with a bf16 cache the new tokens
+ * themselves are read from k_new / v_new, so only its cached slots read as
+ * zero). */
 typedef struct {
   const int32_t* cu_seqlens_q;
   const int32_t* cu_seqlens_knew;
@@ -145,6 +153,12 @@ typedef struct {
  *
  * Returns VPK_SUCCESS once all work is enqueued.  Split-KV, the persistent
  * work schedule and the merge pass are internal choices of the library.
+ * A direct call plans on the host and may grow its workspace, so it cannot be
+ * captured into a graph: on a capturing stream it returns
+ * VPK_ERROR_NOT_SUPPORTED before anything is enqueued (prepared calls,
+ * vpk_plan_create / vpk_plan_run, are the capturable form).  The same holds
+ * for attn_varlen_paged_rope_fwd, attn_varlen_paged_list_fwd and
+ * kv_cache_append.
  */
 int32_t attn_varlen_paged_fwd(const vpk_dims* dims,
                               const void* q, const int32_t* cu_seqlens_q,
@@ -327,6 +341,41 @@ int32_t vpk_plan_device_error(vpk_plan plan, void* stream, int32_t* flags);
 /* Free a plan (NULL is accepted).  No run of it may still be pending. */
 int32_t vpk_plan_destroy(vpk_plan plan);
 
+/*
+ * vpk_set_workspace -- give the direct calls on `stream` (of the current
+ * device) caller-owned device memory for their workspace; ptr NULL goes back
+ * to the library's own.  The flash-attention page's interface leaves every
+ * buffer with the caller's tensors ("Add flash_attn_varlen_func_with_kvcache",
+ * Usage); this is the same for the scratch memory.
+ *   ptr     device memory, 256-byte aligned, at least 4608 bytes, borrowed:
+ *           it must stay valid, and untouched by anything else, until the
+ *           work of every call on `stream` that used it has run (replacing or
+ *           freeing it in stream order after those calls is fine).
+ *   bytes   its size.  A call needs at most
+ *           vpk_workspace_bytes_upper_bound(dims, ...) bytes; with less the
+ *           planner splits key ranges less (the results stay within the same
+ *           tolerances), and a call whose unsplit needs do not fit returns
+ *           VPK_ERROR_CAPACITY before anything is enqueued.
+ * The first 512 bytes are cleared on `stream` (error flag and zero rows).
+ * Not during stream capture (VPK_ERROR_NOT_SUPPORTED).
+ */
+int32_t vpk_set_workspace(void* stream, void* ptr, size_t bytes);
+
+/*
+ * vpk_workspace_bytes_upper_bound -- device bytes that suffice for the
+ * workspace of any direct call with these sizes (any lengths, any split the
+ * planner may choose): head, split partials (at most 2^17 rows of
+ * (head_dim + 1) floats), the plan records, and with rope != 0 the turned
+ * copies of q and k_new.  num_cus <= 0: those of the current device.
+ * Host only; returns 0 for invalid dims.
+ */
+size_t vpk_workspace_bytes_upper_bound(const vpk_dims* dims, int32_t num_cus, int32_t rope);
+
+/* Memory the library holds on its own: device bytes of its fallback
+ * workspaces (streams without vpk_set_workspace) and pinned host bytes of its
+ * plan buffers.  Prepared plans are not counted (each owns its buffer). */
+int32_t vpk_library_memory(size_t* device_bytes, size_t* pinned_bytes);
+
 /* Message describing the calling thread's last non-success status ("" if none). */
 const char* vpk_last_error(void);
 
@@ -342,6 +391,9 @@ int32_t vpk_abi_version(void);
  *                      1 = persistent grid with static per-workgroup queues.
  *   "split_min_keys"   smallest key range of a split part (default 256).
  *   "num_cus"          compute units assumed by the planner (0 = query device).
+ *   "plan_upload"      0 = the kernels read a direct call's work list from
+ *                      pinned host memory (default); 1 = it is copied into the
+ *                      workspace on the call's stream first.
  * Returns VPK_ERROR_INVALID_VALUE for an unknown name or value.
  */
 int32_t vpk_set_option(const char* name, int64_t value);

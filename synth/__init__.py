@@ -5,4 +5,4 @@ angle tables a rotary-embedding caller supplies). It
 holds none of the attention method's arithmetic: no append, no de-paging, no
 softmax. Both the CPU oracle and the GPU path consume what it produces.
 """
-from .workloads import WORKLOADS, Workload, make_workload, make_custom, rope_tables  # noqa: F401
+from .workloads import WORKLOADS, Workload, make_workload, make_custom, rope_tables, subset  # noqa: F401

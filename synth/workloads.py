@@ -304,3 +304,26 @@ def make_workload(name: str, rep: int = 0, *, poison: bool = False,
                        D=spec["D"], page_size=spec["page_size"], causal=spec["causal"],
                        cache_dtype=spec["cache_dtype"], seed=seed + 500, poison=poison,
                        name=name, tiny_table=(name == "tiny"), lengths_only=lengths_only)
+
+
+def subset(wl: Workload, seqs) -> Workload:
+    """The sub-batch of sequences ``seqs`` (in that order) of a workload, over the same page pools:
+    its query rows, new tokens, length arrays and block-table rows.  Input preparation only (used to
+    time the parts of a mixed batch alone)."""
+    seqs = [int(b) for b in seqs]
+    ql = wl.q_lens()[seqs]
+    cu_q = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    q = (np.concatenate([wl.q[wl.cu_seqlens_q[b]:wl.cu_seqlens_q[b + 1]] for b in seqs])
+         if seqs else wl.q[:0])
+    k_new = v_new = cu_kn = None
+    if wl.cu_seqlens_knew is not None:
+        nl = wl.new_lens()[seqs]
+        cu_kn = np.concatenate([[0], np.cumsum(nl)]).astype(np.int32)
+        sl = [slice(int(wl.cu_seqlens_knew[b]), int(wl.cu_seqlens_knew[b + 1])) for b in seqs]
+        k_new = np.concatenate([wl.k_new[s] for s in sl]) if seqs else wl.k_new[:0]
+        v_new = np.concatenate([wl.v_new[s] for s in sl]) if seqs else wl.v_new[:0]
+    bt = wl.block_table[seqs] if wl.block_table is not None else None
+    cl = wl.cache_seqlens[seqs] if wl.cache_seqlens is not None else None
+    return dataclasses.replace(wl, name=f"{wl.name}[{len(seqs)} seqs]", B=len(seqs), q=q, cu_seqlens_q=cu_q,
+                               k_new=k_new, v_new=v_new, cu_seqlens_knew=cu_kn, block_table=bt,
+                               cache_seqlens=cl, f32=None)

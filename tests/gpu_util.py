@@ -106,3 +106,24 @@ def check_attention(out_np, lse_np, ref_out, ref_lse, kind="bf16", rows=None, la
         assert le <= tol["lse"], f"{label}: lse max-abs {le:.3e} > {tol['lse']}"
         return mx, mean, le
     return 0.0, 0.0, 0.0
+
+
+def run_and_check(wl, label, with_new=True):
+    """One direct call on the device against the oracle's whole call: attention within tolerance,
+    appended cache bytes bit for bit."""
+    say(f"[case] {label}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} S={wl.page_size} "
+        f"causal={wl.causal} cache={wl.cache_dtype} seed={wl.seed}")
+    dc = DeviceCall(wl, with_new=with_new)
+    out, lse = dc.run()
+    torch.cuda.synchronize()
+    ref = oracle_full(wl, with_new=with_new)
+    kind = "fp8" if wl.cache_dtype == "fp8" else "bf16"
+    errs = check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"],
+                           ref["lse"], kind, label=label)
+    kc, vc = dc.cache_host()
+    if kc is not None:
+        assert np.array_equal(kc, ref["k_cache"]), f"{label}: k_cache bytes differ"
+        assert np.array_equal(vc, ref["v_cache"]), f"{label}: v_cache bytes differ"
+    say(f"[ok] {label}: max {errs[0]:.2e} mean {errs[1]:.2e} lse {errs[2]:.2e}")
+    return dc, out, lse
+

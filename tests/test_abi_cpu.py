@@ -256,3 +256,22 @@ def test_device_scale_run_errors_before_the_device():
     st = lib.vpk_plan_run_device_scale(None, vp(FAKE), None, None, None, None, None, 0.1, vp(FAKE), vp(FAKE),
                                        vp(FAKE), None)
     assert st == 1 and b"plan is NULL" in lib.vpk_last_error()
+
+
+def test_workspace_bound_host_only():
+    lib = _lib.load()
+    d = _lib.VpkDims(4, 100, 100, 32, 8, 128, 1000, 64, _lib.VPK_DTYPE_BF16)
+    b0 = lib.vpk_workspace_bytes_upper_bound(ctypes.byref(d), 256, 0)
+    b1 = lib.vpk_workspace_bytes_upper_bound(ctypes.byref(d), 256, 1)
+    # the rope copies of q and k_new in bf16
+    assert b1 - b0 >= 2 * (100 * 32 * 128 + 100 * 8 * 128)
+    # more rows never need less
+    d2 = _lib.VpkDims(4, 1000, 1000, 32, 8, 128, 1000, 64, _lib.VPK_DTYPE_BF16)
+    assert lib.vpk_workspace_bytes_upper_bound(ctypes.byref(d2), 256, 0) >= b0 > 512
+    bad = _lib.VpkDims(4, 100, 100, 30, 8, 128, 1000, 64, _lib.VPK_DTYPE_BF16)
+    assert lib.vpk_workspace_bytes_upper_bound(ctypes.byref(bad), 256, 0) == 0
+    assert lib.vpk_workspace_bytes_upper_bound(None, 256, 0) == 0
+    st = lib.vpk_set_workspace(None, ctypes.c_void_p(FAKE + 8), 1 << 20)
+    assert st == 1 and b"aligned" in lib.vpk_last_error()
+    st = lib.vpk_set_workspace(None, ctypes.c_void_p(FAKE), 1024)
+    assert st == 1 and b"at least" in lib.vpk_last_error()

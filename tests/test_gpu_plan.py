@@ -1,8 +1,11 @@
 """Prepared calls (vpk_plan_create / vpk_plan_run) on the GPU.
 
-A plan's run must give the direct call's bits (same kernels, same work list),
-and a run captured into a graph must give them on every replay, with the
+A plan's run must match the oracle (attention within tolerance, appended
+cache bytes exact) and give the direct call's bits (same kernels, same work
+list); a run captured into a graph must do both on every replay, with the
 program's own eager work between the replays."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -10,7 +13,7 @@ import torch
 import varlen_paged_kv_amd as vpk
 from synth import make_custom
 
-from gpu_util import DeviceCall, say
+from gpu_util import DeviceCall, check_attention, oracle_full, say, to_np_out
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +47,20 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
 
 
+def _check_oracle(dc, out, lse, label, q_bits=None):
+    """out / lse of a run on dc's inputs (q replaced by q_bits when given) against the oracle,
+    and the device caches against the oracle's append."""
+    wl = dc.wl
+    if q_bits is not None:
+        wl = dataclasses.replace(wl, q=q_bits)
+    ref = oracle_full(wl, with_new=dc.with_new)
+    check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                    "fp8" if dc.fp8 else "bf16", label=label)
+    kc, vc = dc.cache_host()
+    if kc is not None:
+        assert np.array_equal(kc, ref["k_cache"]) and np.array_equal(vc, ref["v_cache"]), f"{label}: cache bytes"
+
+
 def _mixed(cache_dtype, seed):
     # decode rows (q_len 1), a short and a long prefill, a sequence with no
     # cached prefix; page size 16
@@ -75,6 +92,7 @@ def test_plan_run_equals_direct_call(case, splits):
     plan = _plan_for(dc)
     out, lse = _run_plan(plan, dc)
     torch.cuda.synchronize()
+    _check_oracle(dc, out, lse, f"plan {case} splits={splits}")
     assert np.array_equal(_bits(out), _bits(ref_out)), f"{case}: out differs"
     assert np.array_equal(_bits(lse), _bits(ref_lse)), f"{case}: lse differs"
     assert plan.device_error() == 0
@@ -83,7 +101,7 @@ def test_plan_run_equals_direct_call(case, splits):
     torch.cuda.synchronize()
     assert np.array_equal(_bits(out2), _bits(ref_out)) and np.array_equal(_bits(lse2), _bits(ref_lse))
     plan.close()
-    say(f"[ok] plan {case} splits={splits}: bitwise equal to the direct call")
+    say(f"[ok] plan {case} splits={splits}: within the oracle tolerances, bitwise equal to the direct call")
 
 
 @pytest.mark.parametrize("case", ["mixed_bf16", "mixed_fp8"])
@@ -110,13 +128,15 @@ def test_plan_run_in_graph_replays(case):
         dc.q.copy_(torch.randn(dc.q.shape, generator=gen).to(torch.bfloat16).to(dc.q.device))
         g.replay()
         torch.cuda.synchronize()
+        q_bits = dc.q.view(torch.int16).cpu().numpy().view(np.uint16)
+        _check_oracle(dc, out, lse, f"{case} replay {rep}", q_bits=q_bits)
         ref_out, ref_lse = dc.run()
         torch.cuda.synchronize()
         assert np.array_equal(_bits(out), _bits(ref_out)), f"{case}: replay {rep} out differs"
         assert np.array_equal(_bits(lse), _bits(ref_lse)), f"{case}: replay {rep} lse differs"
     del g
     plan.close()
-    say(f"[ok] graph replays of {case}: bitwise equal to eager calls")
+    say(f"[ok] graph replays of {case}: within the oracle tolerances, bitwise equal to eager calls")
 
 
 def test_device_scales_follow_changes_between_graph_replays():
@@ -164,6 +184,12 @@ def test_device_scales_follow_changes_between_graph_replays():
         kc_g = dc.k_cache.cpu().numpy().copy()
         ref_out, ref_lse = direct(ks)
         torch.cuda.synchronize()
+        # the oracle with the same scales: the new tokens are quantised with them, the cached
+        # prefix keeps its codes and is read with them
+        ref = oracle_full(dataclasses.replace(wl, kv_scale=(np.float32(ks[0]), np.float32(ks[1]))))
+        check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"], "fp8",
+                        label=f"device scales replay {rep}")
+        assert np.array_equal(kc_g, ref["k_cache"]), f"replay {rep}: appended codes differ from the oracle"
         assert np.array_equal(got_o, _bits(ref_out)), f"replay {rep} (scales x{f}): out differs"
         assert np.array_equal(got_l, _bits(ref_lse)), f"replay {rep} (scales x{f}): lse differs"
         assert np.array_equal(kc_g, dc.k_cache.cpu().numpy()), f"replay {rep}: appended codes differ"

@@ -1,0 +1,121 @@
+"""Caller-owned workspace (vpk_set_workspace) on the GPU.
+
+The binding registers a torch tensor as the workspace of every stream it
+calls on; then the library allocates no device memory of its own.  Results
+are bitwise those of the library's own workspace, with the work list read
+from pinned host memory or uploaded into the workspace, and within the
+oracle's tolerances with a workspace too small for the planner's splits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import varlen_paged_kv_amd as vpk
+from synth import make_custom
+from varlen_paged_kv_amd import _lib
+
+from gpu_util import DeviceCall, check_attention, oracle_full, say, to_np_out
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _restore():
+    yield
+    vpk.AUTO_WORKSPACE = True
+    vpk.set_option("force_splits", 0)
+    vpk.set_option("plan_upload", 0)
+
+
+def _mixed(cache="bf16", seed=71):
+    return make_custom(q_lens=[1, 37, 1, 300, 1], new_lens=[1, 37, 1, 300, 1], cache_lens=[500, 40, 1000, 0, 77],
+                       Hq=8, Hkv=2, D=128, page_size=16, causal=True, cache_dtype=cache, seed=seed)
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+def _run(dc, stream):
+    with torch.cuda.stream(stream):
+        out, lse = dc.run(stream=stream)
+    stream.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_torch_workspace_means_no_library_allocation(cache):
+    vpk.set_option("force_splits", 3)     # split partials live in the workspace
+    wl = _mixed(cache)
+    dc = DeviceCall(wl)
+    s = torch.cuda.Stream()
+    dev0, pin0 = vpk.library_memory()
+    say(f"[case] torch workspace {cache}: library memory before {dev0} device / {pin0} pinned bytes")
+    out, lse = _run(dc, s)
+    dev1, _ = vpk.library_memory()
+    assert dev1 == dev0, f"the library allocated {dev1 - dev0} device bytes with a caller workspace"
+    ref = oracle_full(wl)
+    check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                    "fp8" if cache == "fp8" else "bf16", label=f"torch workspace {cache}")
+    say(f"[ok] torch workspace {cache}: no library device memory, within tolerance")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_caller_and_library_workspaces_give_the_same_bits(cache):
+    vpk.set_option("force_splits", 3)
+    wl = _mixed(cache, seed=72)
+    dc = DeviceCall(wl)
+    say(f"[case] library workspace vs caller workspace vs uploaded plan, {cache}")
+    vpk.AUTO_WORKSPACE = False
+    s_lib = torch.cuda.Stream()
+    o_lib, l_lib = _run(dc, s_lib)                   # library-owned workspace on a fresh stream
+    vpk.AUTO_WORKSPACE = True
+    s_user = torch.cuda.Stream()
+    o_user, l_user = _run(dc, s_user)                # torch tensor registered by the binding
+    vpk.set_option("plan_upload", 1)
+    o_up, l_up = _run(dc, s_user)                    # work list uploaded into that workspace
+    o_up_lib, l_up_lib = None, None
+    vpk.AUTO_WORKSPACE = False
+    o_up_lib, l_up_lib = _run(dc, s_lib)             # uploaded into the library's workspace
+    for name, o, l in (("caller", o_user, l_user), ("caller+upload", o_up, l_up), ("library+upload", o_up_lib, l_up_lib)):
+        assert np.array_equal(_bits(o), _bits(o_lib)), f"{name}: out differs"
+        assert np.array_equal(_bits(l), _bits(l_lib)), f"{name}: lse differs"
+    ref = oracle_full(wl)
+    check_attention(to_np_out(o_lib), l_lib.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                    "fp8" if cache == "fp8" else "bf16", label=f"workspaces {cache}")
+    say(f"[ok] workspaces {cache}: bitwise equal, within tolerance")
+
+
+def test_small_workspace_splits_less_and_too_small_is_refused():
+    wl = make_custom(q_lens=[1, 1, 2], new_lens=[1, 1, 2], cache_lens=[3000, 2500, 4000], Hq=8, Hkv=2, D=128,
+                     page_size=16, causal=True, cache_dtype="bf16", seed=73)
+    dc = DeviceCall(wl)
+    ref = oracle_full(wl)
+    vpk.AUTO_WORKSPACE = False
+    s = torch.cuda.Stream()
+    dims = _lib.VpkDims(wl.B, wl.Tq, wl.Tn, wl.Hq, wl.Hkv, wl.D, wl.num_pages, wl.block_table.shape[1],
+                        _lib.VPK_DTYPE_BF16)
+    full = vpk.workspace_bytes_upper_bound(dims)
+    # room for the head, the plan and a few hundred partial rows: the planner splits less
+    for size in (full, 64 * 1024, 8 * 1024):
+        buf = torch.empty(size, dtype=torch.uint8, device="cuda")
+        vpk.set_workspace(buf, stream=s)
+        say(f"[case] workspace of {size} bytes (bound {full})")
+        out, lse = _run(dc, s)
+        check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                        label=f"workspace {size} bytes")
+        del buf
+    # too small for the turned copies of q and k_new of a rope call
+    buf = torch.empty(8 * 1024, dtype=torch.uint8, device="cuda")
+    vpk.set_workspace(buf, stream=s)
+    from synth import rope_tables
+    cos, sin = rope_tables(5000, wl.D)
+    with pytest.raises(vpk.VpkError) as ei:
+        with torch.cuda.stream(s):
+            vpk.attn_varlen_paged_rope_fwd(dc.q, dc.cu_q, dc.k_new, dc.v_new, dc.cu_kn, dc.k_cache, dc.v_cache, dc.bt,
+                                           dc.cl, wl.page_size, wl.causal, wl.scale, rope_cos=torch.from_numpy(cos).cuda(),
+                                           rope_sin=torch.from_numpy(sin).cuda(), host_index=dc.host, stream=s)
+    assert ei.value.status == _lib.VPK_ERROR_CAPACITY, ei.value
+    vpk.set_workspace(None, stream=s)
+    s.synchronize()
+    say(f"[ok] small workspaces within tolerance; too small refused: {ei.value.msg}")

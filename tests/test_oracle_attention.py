@@ -254,6 +254,29 @@ def test_append_fp8_codes_and_dequant_error():
         assert np.all(np.abs(deq - x) <= np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * ks) + 1e-12)
 
 
+def test_append_fp8_special_values_keep_the_input_sign():
+    """Specials through the fp8 append, against the e4m3fn bit definition (sign bit 7, exponent
+    bits 6..3, mantissa bits 2..0; S.1111.111 is NaN; 448 = 0.1111.110 the largest finite value):
+    a NaN is stored as the NaN code of its own sign, infinities and values past 448 saturate to
+    +-448 with their sign, and -0 keeps its sign.  The pages leave NaN handling open; the reading
+    taken is that the stored code carries the input's sign bit (1/scale > 0 cannot change it)."""
+    specials = {0x7FC0: 0x7F, 0xFFC0: 0xFF, 0x7F81: 0x7F, 0xFF81: 0xFF, 0x7FFF: 0x7F, 0xFFFF: 0xFF,
+                0x7F80: 0x7E, 0xFF80: 0xFE, 0x0000: 0x00, 0x8000: 0x80, 0x4580: 0x7E, 0xC580: 0xFE}
+    bits = np.array(list(specials), np.uint16)            # 12 values: one row of one token
+    expect = np.array(list(specials.values()), np.uint8)
+    for scale in (np.float32(1.0), np.float32(0.25)):
+        k_new = np.zeros((1, 1, 16), np.uint16)
+        k_new[0, 0, :12] = bits
+        cache = np.full((1, 4, 1, 16), 0x11, np.uint8)
+        kc, vc = oracle.append(k_new, k_new.copy(), np.array([0, 1], np.int32), cache, cache.copy(),
+                               np.array([[0]], np.int32), np.array([2], np.int32), 4, "fp8", (scale, scale))
+        got = kc[0, 2, 0, :12]
+        # with scale 1/4 every finite non-zero value is multiplied by 4 and still saturates or stays
+        # zero; NaN and the sign of zero do not depend on the scale
+        assert np.array_equal(got, expect), (scale, [hex(x) for x in got])
+        assert np.array_equal(kc[0, [0, 1, 3]], cache[0, [0, 1, 3]])   # other slots untouched
+
+
 # ------------------------------------------------------------------- brute force
 
 def _brute(q, k, v, lq, lk, causal, scale, g):

@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 
-__all__ = ["attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
+__all__ = ["set_workspace", "workspace_bytes_upper_bound", "library_memory", "attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE", "KERNEL_ROPE",
            "attn_varlen_paged_rope_fwd"]
@@ -60,6 +60,35 @@ def _dev(t: Optional[torch.Tensor], name: str, dtypes) -> Optional[torch.Tensor]
     return t
 
 
+def _out_lse(out, lse, Tq, Hq, D, device):
+    """Validate caller-supplied outputs: out bf16 [Tq, Hq, D], lse fp32 [Hq, Tq], contiguous, on q's device
+    (the kernels write them densely with these shapes)."""
+    if out is not None:
+        out = _dev(out, "out", _BF16)
+        if tuple(out.shape) != (Tq, Hq, D):
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"out has shape {tuple(out.shape)}, expected {(Tq, Hq, D)}")
+        if out.device != device:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"out is on {out.device}, q on {device}")
+    if lse is not None:
+        lse = _dev(lse, "lse", (torch.float32,))
+        if tuple(lse.shape) != (Hq, Tq):
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"lse has shape {tuple(lse.shape)}, expected {(Hq, Tq)}")
+        if lse.device != device:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"lse is on {lse.device}, q on {device}")
+    return out, lse
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} is on {t.device}, q on {device}")
+
+
+def _length(name, n, expected):
+    if n != expected:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has {n} entries, expected {expected}")
+
+
 def _host_i32(x) -> Optional[np.ndarray]:
     if x is None:
         return None
@@ -77,6 +106,61 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+# Device workspace of each (device, stream) the binding has called on: a torch
+# uint8 tensor registered with vpk_set_workspace, so that PyTorch owns the
+# library's scratch memory (split partials, error flag, rope copies).
+_WORKSPACES = {}
+# set to False to leave streams without a caller workspace (the library then uses its own)
+AUTO_WORKSPACE = True
+
+
+def workspace_bytes_upper_bound(dims: VpkDims, rope: bool = False, num_cus: int = 0) -> int:
+    """Device bytes that suffice for the workspace of any call with these sizes."""
+    return int(_lib.load().vpk_workspace_bytes_upper_bound(ctypes.byref(dims), int(num_cus), int(bool(rope))))
+
+
+def set_workspace(buf: Optional[torch.Tensor], stream=None):
+    """Use ``buf`` (a contiguous device tensor, 256-byte aligned) as the workspace of the calls on
+    ``stream``; None goes back to the library's own.  The binding manages one per stream by itself;
+    this is for callers that bring their own."""
+    h = _stream_handle(stream)
+    if buf is None:
+        _check(_lib.load().vpk_set_workspace(h, None, 0))
+        return
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "the workspace must be a contiguous GPU tensor")
+    _check(_lib.load().vpk_set_workspace(h, ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()))
+
+
+def library_memory():
+    """(device bytes, pinned host bytes) the library holds on its own (fallback workspaces, plan buffers)."""
+    d, h = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(_lib.load().vpk_library_memory(ctypes.byref(d), ctypes.byref(h)))
+    return d.value, h.value
+
+
+def _ensure_workspace(dims: VpkDims, device, stream_handle, rope: bool = False):
+    """Register a torch-allocated workspace of at least the bound for this call's sizes on its stream
+    (grown by replacing it: the old tensor goes back to torch's allocator in the stream's order)."""
+    if not AUTO_WORKSPACE:
+        return
+    need = workspace_bytes_upper_bound(dims, rope)
+    key = (device.index, stream_handle.value)
+    cur = _WORKSPACES.get(key)
+    if cur is not None and cur.numel() >= need:
+        return
+    size = max(need + need // 4, 1 << 20)
+    size = (size + 4095) // 4096 * 4096
+    ext = torch.cuda.ExternalStream(stream_handle.value, device=device) if stream_handle.value else None
+    if ext is not None:
+        with torch.cuda.stream(ext):
+            buf = torch.empty(size, dtype=torch.uint8, device=device)
+    else:
+        buf = torch.empty(size, dtype=torch.uint8, device=device)
+    _check(_lib.load().vpk_set_workspace(stream_handle, ctypes.c_void_p(buf.data_ptr()), size))
+    _WORKSPACES[key] = buf
 
 
 def _host_index(cu_q, cu_kn, cache_lens, block_table):
@@ -170,9 +254,22 @@ def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache
                          ("v_cache", v_cache, (P, page_size, Hkv, D))):
         if t is not None and tuple(t.shape) != shp:
             raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    _same_device(q.device, cu_seqlens_q=cu_seqlens_q, k_new=k_new, v_new=v_new, cu_seqlens_knew=cu_seqlens_knew,
+                 k_cache=k_cache, v_cache=v_cache, block_table=block_table, cache_seqlens=cache_seqlens)
+    if cu_seqlens_q.dim() != 1 or B < 0:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "cu_seqlens_q must be [batch + 1]")
+    if cu_seqlens_knew is not None:
+        _length("cu_seqlens_knew", cu_seqlens_knew.numel(), B + 1)
+    if cache_seqlens is not None:
+        _length("cache_seqlens", cache_seqlens.numel(), B)
+    if block_table is not None:
+        if block_table.dim() != 2:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "block_table must be [batch, max_pages_per_seq]")
+        _length("block_table rows", block_table.shape[0], B)
     maxp = 0 if block_table is None else block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    out, lse = _out_lse(out, lse, Tq, Hq, D, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -187,10 +284,16 @@ def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache
     h = host_index or {}
     hi, keep = _host_index(h.get("cu_seqlens_q"), h.get("cu_seqlens_knew"),
                            h.get("cache_seqlens"), h.get("block_table"))
+    for name, a, n in (("host cu_seqlens_q", keep[0], B + 1), ("host cu_seqlens_knew", keep[1], B + 1),
+                       ("host cache_seqlens", keep[2], B), ("host block_table", keep[3], B * maxp)):
+        if a is not None:
+            _length(name, a.size, n)
     args = (ctypes.byref(dims), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_knew),
             _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens), int(page_size),
             int(bool(causal)), float(scale), ks)
-    tail = (_ptr(out), _ptr(lse), ctypes.byref(hi), _stream_handle(stream))
+    sh = _stream_handle(stream)
+    _ensure_workspace(dims, q.device, sh, rope is not None)
+    tail = (_ptr(out), _ptr(lse), ctypes.byref(hi), sh)
     if rope is None:
         st = lib.attn_varlen_paged_fwd(*args, *tail)
     else:
@@ -236,8 +339,15 @@ def attn_varlen_paged_list_fwd(q: torch.Tensor, q_start, q_len, k_new=None, v_ne
                          ("v_cache", v_cache, (P, page_size, Hkv, D))):
         if t is not None and tuple(t.shape) != shp:
             raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    _same_device(q.device, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, kv_indices=kv_indices)
+    _length("q_len", ql.size, B)
+    for name, a, n in (("cu_seqlens_knew", cu_seqlens_knew, B + 1), ("cache_seqlens", cache_seqlens, B),
+                       ("kv_indptr", kv_indptr, B + 1)):
+        if a is not None:
+            _length(name, _host_i32(a).size, n)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    out, lse = _out_lse(out, lse, Tq, Hq, D, q.device)
     if out is None:
         out = torch.zeros_like(q)
     if lse is None and return_lse:
@@ -251,10 +361,13 @@ def attn_varlen_paged_list_fwd(q: torch.Tensor, q_start, q_len, k_new=None, v_ne
     keep = [qs, ql, _host_i32(cu_seqlens_knew), _host_i32(cache_seqlens), _host_i32(kv_indptr),
             _host_i32(kv_indices_host)]
     hp = VpkHostPages(*[None if a is None else a.ctypes.data for a in keep])
+    sh = _stream_handle(stream)
+    wdims = VpkDims(*[getattr(dims, f) for f, _ in VpkDims._fields_])
+    wdims.max_pages_per_seq = int(np.diff(keep[4]).max()) if keep[4] is not None and B else 0
+    _ensure_workspace(wdims, q.device, sh)
     st = lib.attn_varlen_paged_list_fwd(ctypes.byref(dims), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                         _ptr(v_cache), _ptr(kv_indices), int(page_size), int(bool(causal)),
-                                        float(scale), ks, _ptr(out), _ptr(lse), ctypes.byref(hp),
-                                        _stream_handle(stream))
+                                        float(scale), ks, _ptr(out), _ptr(lse), ctypes.byref(hp), sh)
     del keep
     _check(st)
     return out, lse
@@ -330,8 +443,10 @@ class Plan:
         if block_table is not None and tuple(block_table.shape) != (self.batch, self.max_pages):
             raise VpkError(_lib.VPK_ERROR_INVALID_VALUE,
                            f"block_table has shape {tuple(block_table.shape)}, expected {(self.batch, self.max_pages)}")
+        _same_device(q.device, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, block_table=block_table)
         if scale is None:
             scale = 1.0 / math.sqrt(D)
+        out, lse = _out_lse(out, lse, self.total_q, Hq, D, q.device)
         if out is None:
             out = torch.empty_like(q)
         if lse is None and return_lse:
@@ -385,8 +500,22 @@ def kv_cache_append(k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table
     v_cache = _dev(v_cache, "v_cache", _FP8 if fp8 else _BF16)
     block_table = _dev(block_table, "block_table", _I32)
     cache_seqlens = _dev(cache_seqlens, "cache_seqlens", _I32)
+    if k_new.dim() != 3:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "k_new must be [total_knew, num_kv_heads, head_dim]")
     Tn, Hkv, D = k_new.shape
     B = cu_seqlens_knew.numel() - 1
+    _same_device(k_new.device, v_new=v_new, cu_seqlens_knew=cu_seqlens_knew, k_cache=k_cache, v_cache=v_cache,
+                 block_table=block_table, cache_seqlens=cache_seqlens)
+    for name, t, shp in (("v_new", v_new, (Tn, Hkv, D)), ("k_cache", k_cache, (k_cache.shape[0], page_size, Hkv, D)),
+                         ("v_cache", v_cache, (k_cache.shape[0], page_size, Hkv, D))):
+        if tuple(t.shape) != shp:
+            raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    _length("cache_seqlens", cache_seqlens.numel(), B)
+    if block_table.dim() != 2:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "block_table must be [batch, max_pages_per_seq]")
+    _length("block_table rows", block_table.shape[0], B)
+    if fp8 and kv_scale is None:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "kv_scale is required for an fp8 cache")
     dims = VpkDims(B, 0, Tn, Hkv, Hkv, D, k_cache.shape[0], block_table.shape[1],
                    _lib.VPK_DTYPE_FP8_E4M3FN if fp8 else _lib.VPK_DTYPE_BF16)
     ks = None
@@ -394,9 +523,11 @@ def kv_cache_append(k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table
         ks = (ctypes.c_float * 2)(float(kv_scale[0]), float(kv_scale[1]))
     h = host_index or {}
     hi, keep = _host_index(None, h.get("cu_seqlens_knew"), h.get("cache_seqlens"), h.get("block_table"))
+    sh = _stream_handle(stream)
+    _ensure_workspace(dims, k_new.device, sh)
     st = lib.kv_cache_append(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens_knew),
                              _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens),
-                             int(page_size), ks, ctypes.byref(hi), _stream_handle(stream))
+                             int(page_size), ks, ctypes.byref(hi), sh)
     del keep
     _check(st)
 

@@ -28,7 +28,7 @@ EXPORTS = (
     "vpk_set_option", "vpk_timing_enable", "vpk_timing_reset", "vpk_timing_read",
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
     "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
-    "vpk_plan_run_device_scale",
+    "vpk_plan_run_device_scale", "vpk_set_workspace", "vpk_workspace_bytes_upper_bound", "vpk_library_memory",
 )
 
 
@@ -119,5 +119,11 @@ def load() -> ctypes.CDLL:
     lib.vpk_plan_device_error.argtypes = [vp, vp, P(i32)]
     lib.vpk_plan_destroy.restype = i32
     lib.vpk_plan_destroy.argtypes = [vp]
+    lib.vpk_set_workspace.restype = i32
+    lib.vpk_set_workspace.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.vpk_workspace_bytes_upper_bound.restype = ctypes.c_size_t
+    lib.vpk_workspace_bytes_upper_bound.argtypes = [P(VpkDims), i32, i32]
+    lib.vpk_library_memory.restype = i32
+    lib.vpk_library_memory.argtypes = [P(ctypes.c_size_t), P(ctypes.c_size_t)]
     _lib = lib
     return lib

@@ -46,6 +46,7 @@ struct Options {
   std::atomic<int64_t> persistent{-1};
   std::atomic<int64_t> split_min_keys{256};
   std::atomic<int64_t> num_cus{0};
+  std::atomic<int64_t> plan_upload{0};
 } g_opt;
 
 // ------------------------------------------------------------------ timing
@@ -115,18 +116,28 @@ struct PlanBuf {
   bool pending = false;
 };
 
+// Split-partial rows one call may use at most, whatever its workspace (the
+// planner scales its splits down to stay within it; the workloads measured
+// here use at most a quarter of it).
+constexpr int64_t kPartRowsCap = int64_t(1) << 17;
+
 struct Workspace {
   int device = -1;
-  char* dev = nullptr;       // [flag | zeros][split partials]
+  // library-owned device memory (fallback): [flag | zeros][split partials, rope copies][plan records]
+  char* dev = nullptr;
   size_t bytes = 0;
   size_t part_cap = 0;
+  // caller-owned device memory (vpk_set_workspace), same layout; used instead of `dev` when set
+  char* user = nullptr;
+  size_t user_bytes = 0;
   PlanBuf plan[kPlanRing];
   int next = 0;
   // side stream for running the decode-mode grid next to the prefill-mode grid
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_join = nullptr;
-  char* parts() const { return dev + kFlagBytes; }
+  char* head() const { return user ? user : dev; }
+  char* parts() const { return head() + kFlagBytes; }
 };
 
 int32_t ensure_aux(Workspace* w) {
@@ -145,9 +156,8 @@ std::map<std::pair<int, void*>, Workspace*> g_ws;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The workspace of (current device, stream) with `part_need` bytes of split
-// partials in device memory.
-int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
+// The bookkeeping of (current device, stream), created on first use.
+int32_t find_workspace(hipStream_t stream, Workspace** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -158,6 +168,27 @@ int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
     if (!w) return fail(VPK_ERROR_OUT_OF_MEMORY, "workspace bookkeeping");
     w->device = dev;
   }
+  *out = w;
+  return VPK_SUCCESS;
+}
+
+// The workspace of (current device, stream) with `part_need` bytes after its
+// head in device memory: the caller's (which must hold them) or the library's
+// own, grown as needed.
+int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
+  Workspace* w = nullptr;
+  int32_t st = find_workspace(stream, &w);
+  if (st) return st;
+  *out = w;
+  if (w->user) {
+    if (kFlagBytes + part_need > w->user_bytes)
+      return fail(VPK_ERROR_CAPACITY, "the workspace set with vpk_set_workspace holds " + std::to_string(w->user_bytes) +
+                                          " bytes, this call needs " + std::to_string(kFlagBytes + part_need) +
+                                          " (see vpk_workspace_bytes_upper_bound)");
+    return VPK_SUCCESS;
+  }
+  hipError_t e;
+  std::lock_guard<std::mutex> lk(g_wmu);
   if (!w->dev || w->part_cap < part_need) {
     if (w->dev) {
       // everything that may still read the old buffer is on these streams
@@ -238,6 +269,21 @@ int32_t fetch_index(const int32_t* dev, size_t n, hipStream_t stream, std::vecto
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Direct calls plan on the host and hand the kernels a plan buffer from a
+// ring that the next calls reuse, and may grow their workspace: a graph
+// captured around one would replay a later call's work list.  They refuse
+// stream capture; prepared calls (vpk_plan_create / vpk_plan_run) are the
+// capturable form.
+int32_t refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(VPK_ERROR_NOT_SUPPORTED,
+                "direct calls cannot be captured into a graph: use vpk_plan_create / vpk_plan_run");
+  return VPK_SUCCESS;
+}
 
 struct Mirrors {
   const int32_t* cu_q = nullptr;
@@ -384,6 +430,51 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
   in.force_splits = static_cast<int32_t>(g_opt.force_splits.load());
   in.persistent = static_cast<int32_t>(g_opt.persistent.load());
   in.split_min_keys = static_cast<int32_t>(g_opt.split_min_keys.load());
+  in.max_part_rows = kPartRowsCap;
+}
+
+// ---- workspace sizes.  Bounds over every call with the sizes of `d` (any
+//      lengths), for a workspace laid out as [head][split partials, rope
+//      copies][plan records].
+
+// most parts one tile is cut into: the split limit, or the parts a key range
+// needs so that each fits the LDS page-id list (ceil(max_pages / 1023) + 1)
+int64_t parts_per_tile_bound(const vpk_dims* d) {
+  return std::max<int64_t>(vpk::kMaxSplits, d->max_pages_per_seq / (vpk::kMaxItemPages - 1) + 2);
+}
+
+size_t part_bytes_for(int64_t rows, int32_t D) {
+  return align_up(sizeof(float) * static_cast<size_t>(D) * rows, 256) + align_up(sizeof(float) * rows, 256);
+}
+
+size_t rope_bytes_for(const vpk_dims* d) {
+  return align_up(2 * static_cast<size_t>(d->total_q) * d->num_q_heads * d->head_dim, 256) +
+         align_up(2 * static_cast<size_t>(d->total_knew) * d->num_kv_heads * d->head_dim, 256);
+}
+
+size_t plan_bytes_bound(const vpk_dims* d, int32_t num_cus, bool rope) {
+  const int64_t B = d->batch, hkv = d->num_kv_heads, g = d->num_q_heads / d->num_kv_heads;
+  const int64_t tiles = B + (static_cast<int64_t>(d->total_q) * g + vpk::kPrefillRows - 1) / vpk::kPrefillRows;
+  const int64_t units = tiles * parts_per_tile_bound(d);
+  const int64_t queue_starts = 2 * (2 * static_cast<int64_t>(std::max(num_cus, 1)) + 1);
+  size_t b = sizeof(SeqInfo) * B + 2 * sizeof(int32_t) * static_cast<size_t>(d->total_knew) +
+             sizeof(WorkItem) * units + sizeof(MergeGroup) * tiles * hkv + sizeof(int32_t) * queue_starts +
+             sizeof(int32_t) * units * hkv;
+  if (rope) b += sizeof(int32_t) * (static_cast<size_t>(d->total_q) + d->total_knew);
+  return align_up(b + 8 * 64, 256);
+}
+
+int64_t part_rows_bound(const vpk_dims* d) {
+  return std::min<int64_t>(kPartRowsCap,
+                           parts_per_tile_bound(d) * static_cast<int64_t>(d->total_q) * d->num_q_heads);
+}
+
+// split-partial rows that fit a workspace of `bytes` next to everything else a call puts there
+int64_t part_rows_fitting(size_t bytes, const vpk_dims* d, int32_t num_cus, bool rope, bool plan_inside) {
+  const size_t fixed = kFlagBytes + 512 + (rope ? rope_bytes_for(d) : 0) +
+                       (plan_inside ? plan_bytes_bound(d, num_cus, rope) : 0);
+  if (bytes <= fixed) return 0;
+  return static_cast<int64_t>((bytes - fixed) / (sizeof(float) * (static_cast<size_t>(d->head_dim) + 1)));
 }
 
 // Plan buffer layout (pinned host memory, offsets from its start):
@@ -697,15 +788,17 @@ int32_t check_rope_args(const Call& c, const vpk_rope* rope) {
 }
 
 // Every turned row needs a position in [0, max_positions): Lq <= Lk and Lk <= max_positions.
-int32_t check_rope_positions(const Plan& plan, int32_t B, const vpk_rope* rope) {
-  for (int32_t b = 0; b < B; ++b) {
-    const SeqInfo& q = plan.seqs[b];
-    if (q.q_len > q.kv_len)
+int32_t check_rope_positions(const PlanInput& in, const vpk_rope* rope) {
+  for (int32_t b = 0; b < in.batch; ++b) {
+    const int64_t q_len = in.q_start ? in.q_len[b] : in.cu_q[b + 1] - in.cu_q[b];
+    const int64_t new_len = in.has_new ? in.cu_kn[b + 1] - in.cu_kn[b] : 0;
+    const int64_t kv_len = ((in.has_cache && in.cache_lens) ? in.cache_lens[b] : 0) + new_len;
+    if (q_len > kv_len)
       return fail(VPK_ERROR_INVALID_VALUE, "sequence " + std::to_string(b) + ": with rotary embedding a sequence needs "
                                            "no more query rows than keys (query row i sits at Lk - Lq + i)");
-    if ((q.q_len > 0 || q.new_len > 0) && q.kv_len > rope->max_positions)
+    if ((q_len > 0 || new_len > 0) && kv_len > rope->max_positions)
       return fail(VPK_ERROR_INVALID_VALUE, "sequence " + std::to_string(b) + " reaches position " +
-                                               std::to_string(q.kv_len - 1) + ", past rope->max_positions");
+                                               std::to_string(kv_len - 1) + ", past rope->max_positions");
   }
   return VPK_SUCCESS;
 }
@@ -717,23 +810,40 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   const int32_t B = dims->batch;
   int32_t st;
   PlanInput in;
-  fill_plan_input(c, m, causal, device_cus(), in);
+  fill_plan_input(c, m, causal, 0, in);
+  if (rope && (st = check_rope_positions(in, rope))) return st;
+  if ((st = refuse_capture(stream))) return st;
+  Workspace* w = nullptr;
+  if ((st = find_workspace(stream, &w))) return st;
+  // plan records: read by the kernels from the pinned plan buffer, or
+  // uploaded into the workspace first (option "plan_upload")
+  const bool upload = g_opt.plan_upload.load() != 0;
+  const int32_t num_cus = device_cus();
+  in.num_cus = num_cus;
+  if (w->user)
+    in.max_part_rows = std::min<int64_t>(in.max_part_rows,
+                                         part_rows_fitting(w->user_bytes, dims, num_cus, rope != nullptr, upload));
   Plan plan;
   try {
     vpk::build_plan(in, plan);
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
-  if (rope && (st = check_rope_positions(plan, B, rope))) return st;
   const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr);
-  Workspace* w = nullptr;
-  if ((st = get_workspace(stream, L.part_end, &w))) return st;
+  if ((st = get_workspace(stream, L.part_end + (upload ? L.plan_end : 0), &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
-  const Bases bases{w->plan[region].host, w->parts(), w->dev};
+  char* R = w->plan[region].host;
+  if (rope) write_rope_positions(plan, L, B, dims->total_q, R);
+  if (upload) {
+    char* const dR = w->parts() + L.part_end;
+    const hipError_t e = hipMemcpyAsync(dR, R, L.plan_end, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
+    R = dR;
+  }
+  const Bases bases{R, w->parts(), w->head()};
   if (rope) {
     // turn q and k_new into copies; everything after reads the copies
-    write_rope_positions(plan, L, B, dims->total_q, bases.R);
     vpk::RopeParams rp{};
     rp.q = static_cast<const uint16_t*>(q);
     rp.q_out = reinterpret_cast<uint16_t*>(bases.PA + L.rot_q);
@@ -924,6 +1034,7 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   Mirrors m;
   if ((st = get_mirrors(c, nullptr, cu_seqlens_knew, cache_seqlens, host, stream, false, m))) return st;
   if ((st = check_contents(c, m, false))) return st;
+  if ((st = refuse_capture(stream))) return st;
   Plan plan;
   plan.seqs.resize(B);
   for (int32_t b = 0; b < B; ++b) {
@@ -940,7 +1051,7 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
-  if ((st = enqueue_append(append_params(c, w->dev, w->plan[region].host, L, k_new, v_new, k_cache,
+  if ((st = enqueue_append(append_params(c, w->head(), w->plan[region].host, L, k_new, v_new, k_cache,
                                          v_cache, block_table),
                            stream)))
     return st;
@@ -1177,6 +1288,57 @@ int32_t kv_cache_append(const vpk_dims* dims, const void* k_new, const void* v_n
   }
 }
 
+int32_t vpk_set_workspace(void* stream_v, void* ptr, size_t bytes) {
+  try {
+    g_err.clear();
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    if (ptr && !aligned(ptr, 256)) return fail(VPK_ERROR_INVALID_VALUE, "the workspace must be 256-byte aligned");
+    if (ptr && bytes < kFlagBytes + 4096)
+      return fail(VPK_ERROR_INVALID_VALUE, "the workspace must hold at least " + std::to_string(kFlagBytes + 4096) +
+                                               " bytes");
+    int32_t st = refuse_capture(stream);
+    if (st) return st;
+    Workspace* w = nullptr;
+    if ((st = find_workspace(stream, &w))) return st;
+    if (ptr) {
+      // a clear error flag and zero rows, in stream order before any call that uses them
+      const hipError_t e = hipMemsetAsync(ptr, 0, kFlagBytes, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync (workspace head)");
+    }
+    std::lock_guard<std::mutex> lk(g_wmu);
+    w->user = static_cast<char*>(ptr);
+    w->user_bytes = ptr ? bytes : 0;
+    return VPK_SUCCESS;
+  } catch (...) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host exception in vpk_set_workspace");
+  }
+}
+
+int32_t vpk_library_memory(size_t* device_bytes, size_t* pinned_bytes) {
+  size_t d = 0, h = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_wmu);
+    for (const auto& kv : g_ws) {
+      const Workspace* w = kv.second;
+      if (!w) continue;
+      d += w->dev ? w->bytes : 0;
+      for (const PlanBuf& pb : w->plan) h += pb.bytes;
+    }
+  }
+  if (device_bytes) *device_bytes = d;
+  if (pinned_bytes) *pinned_bytes = h;
+  return VPK_SUCCESS;
+}
+
+size_t vpk_workspace_bytes_upper_bound(const vpk_dims* dims, int32_t num_cus, int32_t rope) {
+  if (!dims || dims->batch < 0 || dims->total_q < 0 || dims->total_knew < 0 || dims->num_kv_heads <= 0 ||
+      dims->num_q_heads <= 0 || dims->head_dim <= 0 || dims->num_q_heads % dims->num_kv_heads != 0)
+    return 0;
+  if (num_cus <= 0) num_cus = device_cus();
+  return kFlagBytes + part_bytes_for(part_rows_bound(dims), dims->head_dim) +
+         (rope ? rope_bytes_for(dims) : 0) + plan_bytes_bound(dims, num_cus, rope != 0);
+}
+
 const char* vpk_last_error(void) { return g_err.c_str(); }
 
 int32_t vpk_abi_version(void) { return VPK_ABI_VERSION; }
@@ -1193,6 +1355,9 @@ int32_t vpk_set_option(const char* name, int64_t value) {
   } else if (n == "split_min_keys") {
     if (value < 1 || value > (1 << 24)) return fail(VPK_ERROR_INVALID_VALUE, "split_min_keys out of range");
     g_opt.split_min_keys = value;
+  } else if (n == "plan_upload") {
+    if (value < 0 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "plan_upload must be 0 or 1");
+    g_opt.plan_upload = value;
   } else if (n == "num_cus") {
     if (value < 0 || value > 4096) return fail(VPK_ERROR_INVALID_VALUE, "num_cus out of range");
     g_opt.num_cus = value;
@@ -1254,12 +1419,12 @@ int32_t vpk_device_error(void* stream_v, int32_t* flags) {
   {
     std::lock_guard<std::mutex> lk(g_wmu);
     auto it = g_ws.find(std::make_pair(dev, stream_v));
-    if (it == g_ws.end() || !it->second->dev) return VPK_SUCCESS;
+    if (it == g_ws.end() || !it->second->head()) return VPK_SUCCESS;
     w = it->second;
   }
   int32_t v = 0;
-  if ((e = hipMemcpy(&v, w->dev, sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy flag");
-  if ((e = hipMemset(w->dev, 0, sizeof(v))) != hipSuccess) return hip_fail(e, "hipMemset flag");
+  if ((e = hipMemcpy(&v, w->head(), sizeof(v), hipMemcpyDeviceToHost)) != hipSuccess) return hip_fail(e, "hipMemcpy flag");
+  if ((e = hipMemset(w->head(), 0, sizeof(v))) != hipSuccess) return hip_fail(e, "hipMemset flag");
   *flags = v;
   return VPK_SUCCESS;
 }

@@ -58,6 +58,7 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.items.clear();
   out.groups.clear();
   out.queue_start.clear();
+  out.queue_work.clear();
   out.part_rows = 0;
   out.persistent = false;
   out.prefill = Launch();
@@ -155,9 +156,9 @@ void build_plan(const PlanInput& in, Plan& out) {
     double cost;
     int32_t tile, part, b0, b1, nsplit, group;
   };
-  static thread_local std::vector<Unit> units;
-  units.clear();
-  int32_t ngroups = 0;
+  // parts per tile
+  static thread_local std::vector<int32_t> nparts;
+  nparts.assign(tiles.size(), 1);
   for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
     const Tile& t = tiles[ti];
     const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;
@@ -176,13 +177,45 @@ void build_plan(const PlanInput& in, Plan& out) {
       n = static_cast<int32_t>(std::ceil(t.cost / std::max(target_pre, 1e-9)));
       n = std::min(n, split_limit(t));
     }
-    // every part must fit the LDS page-id list
-    if (in.has_cache && nblk > 0) {
-      const int64_t blocks_per_part_max =
-          std::max<int64_t>(1, (static_cast<int64_t>(kMaxItemPages - 1) * in.page_size) / kBlockN);
-      const int32_t need = static_cast<int32_t>((nblk + blocks_per_part_max - 1) / blocks_per_part_max);
-      n = std::max(n, need);
+    nparts[ti] = std::max(n, 1);
+  }
+  // Every part must fit the LDS page-id list: the fewest parts a tile can have.
+  auto min_parts = [&](const Tile& t) {
+    const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;
+    if (!in.has_cache || nblk == 0) return 1;
+    const int64_t blocks_per_part_max =
+        std::max<int64_t>(1, (static_cast<int64_t>(kMaxItemPages - 1) * in.page_size) / kBlockN);
+    return static_cast<int32_t>((nblk + blocks_per_part_max - 1) / blocks_per_part_max);
+  };
+  auto part_rows_of = [&]() {
+    int64_t r = 0;
+    for (size_t ti = 0; ti < tiles.size(); ++ti) {
+      const int32_t n = std::max(nparts[ti], min_parts(tiles[ti]));
+      if (n > 1) r += static_cast<int64_t>(n) * tiles[ti].nrows * in.hkv;
     }
+    return r;
+  };
+  if (in.max_part_rows >= 0) {
+    // a bounded workspace: scale the split counts down until the partials fit
+    // (with no split beyond the page-id limit the plan needs the least)
+    for (int64_t r = part_rows_of(); r > in.max_part_rows;) {
+      bool changed = false;
+      for (int32_t& n : nparts)
+        if (n > 1) {
+          n = std::max(1, n / 2);
+          changed = true;
+        }
+      r = part_rows_of();
+      if (!changed) break;
+    }
+  }
+  static thread_local std::vector<Unit> units;
+  units.clear();
+  int32_t ngroups = 0;
+  for (int32_t ti = 0; ti < static_cast<int32_t>(tiles.size()); ++ti) {
+    const Tile& t = tiles[ti];
+    const int32_t nblk = (t.kend + kBlockN - 1) / kBlockN;
+    const int32_t n = std::max(nparts[ti], min_parts(t));
     if (n <= 1) {
       units.push_back(Unit{t.cost, ti, 0, 0, nblk, 1, -1});
       continue;

@@ -33,6 +33,9 @@ struct PlanInput {
   int32_t force_splits = 0;             // 0: planner decides
   int32_t persistent = -1;              // -1 planner, 0 off, 1 on
   int32_t split_min_keys = 256;
+  // largest number of split-partial rows the workspace holds (< 0: no limit);
+  // splits are reduced, down to none, until the plan fits
+  int64_t max_part_rows = -1;
 };
 
 // One attention grid: items [first, first + count) of Plan::items, run by the

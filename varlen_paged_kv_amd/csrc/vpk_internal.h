@@ -1,6 +1,7 @@
 // Internal structures shared by the host runtime and the HIP kernels of libvpk.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace vpk {
