@@ -9,6 +9,8 @@
   are allocated with spare pages past the declared num_pages, so even a
   broken guard would read and write inside the allocation.
 """
+import gc
+
 import numpy as np
 import pytest
 import torch
@@ -29,7 +31,14 @@ def _small(cache="bf16", seed=61):
 
 
 def _capture_and_call(fn):
-    """Run fn() inside a graph capture (next to one ordinary captured op) and return the VpkError it raised."""
+    """Run fn() inside a graph capture (next to one ordinary captured op); return the (status, message)
+    of the VpkError it raised, or None.
+
+    Only the status and message are kept: the exception's traceback references this frame, and with it
+    the graph, so keeping the exception would leave the graph to the cyclic garbage collector, which
+    may then destroy it in the middle of a later capture (an abort).  The graph is destroyed here,
+    outside any capture."""
+    gc.collect()                      # no earlier graph may be collected during this capture
     x = torch.zeros(16, device="cuda")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -41,11 +50,14 @@ def _capture_and_call(fn):
             try:
                 fn(s)
             except vpk.VpkError as e:
-                err = e
+                err = (e.status, e.msg)
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
     assert float(x[0]) == 1.0
+    del g
+    gc.collect()
+    torch.cuda.synchronize()
     return err
 
 
@@ -70,10 +82,10 @@ def test_direct_calls_refuse_stream_capture(entry):
                                            wl.page_size, wl.causal, wl.scale, stream=s)
 
     err = _capture_and_call(call)
-    assert err is not None and err.status == _lib.VPK_ERROR_NOT_SUPPORTED, err
+    assert err is not None and err[0] == _lib.VPK_ERROR_NOT_SUPPORTED, err
     kc1, vc1 = dc.cache_host()
     assert np.array_equal(kc0, kc1) and np.array_equal(vc0, vc1), "a refused call changed the cache"
-    say(f"[ok] capture refusal {entry}: {err.msg}")
+    say(f"[ok] capture refusal {entry}: {err[1]}")
 
 
 def test_binding_rejects_bad_outputs_and_index_lengths():

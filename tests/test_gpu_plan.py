@@ -5,6 +5,7 @@ cache bytes exact) and give the direct call's bits (same kernels, same work
 list); a run captured into a graph must do both on every replay, with the
 program's own eager work between the replays."""
 import dataclasses
+import gc
 
 import numpy as np
 import pytest
@@ -118,6 +119,7 @@ def test_plan_run_in_graph_replays(case):
         _run_plan(plan, dc, out, lse)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    gc.collect()   # no earlier graph may be collected during the capture
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         _run_plan(plan, dc, out, lse)
@@ -135,6 +137,7 @@ def test_plan_run_in_graph_replays(case):
         assert np.array_equal(_bits(out), _bits(ref_out)), f"{case}: replay {rep} out differs"
         assert np.array_equal(_bits(lse), _bits(ref_lse)), f"{case}: replay {rep} lse differs"
     del g
+    gc.collect()
     plan.close()
     say(f"[ok] graph replays of {case}: within the oracle tolerances, bitwise equal to eager calls")
 
@@ -170,6 +173,7 @@ def test_device_scales_follow_changes_between_graph_replays():
                  out=out, lse=lse)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    gc.collect()   # no earlier graph may be collected during the capture
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         plan.run(dc.q, dc.k_new, dc.v_new, dc.k_cache, dc.v_cache, dc.bt, scale=wl.scale, kv_scale=ks_dev,
@@ -194,5 +198,6 @@ def test_device_scales_follow_changes_between_graph_replays():
         assert np.array_equal(got_l, _bits(ref_lse)), f"replay {rep} (scales x{f}): lse differs"
         assert np.array_equal(kc_g, dc.k_cache.cpu().numpy()), f"replay {rep}: appended codes differ"
     del g
+    gc.collect()
     plan.close()
     say("[ok] device scales: plan runs and graph replays follow the scale buffer bit for bit")
