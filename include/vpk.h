@@ -172,6 +172,40 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims,
                               const vpk_host_index* host, void* stream);
 
 /*
+ * attn_varlen_paged_fwd_noalloc -- attn_varlen_paged_fwd for callers that
+ * cannot allocate memory (tight serving loops, harnesses that forbid device
+ * allocation).  It allocates no device or pinned memory, creates no stream or
+ * event and never synchronises: its work list and split partials go to a
+ * fixed 64 MiB scratch array in device memory that the library's code object
+ * holds on each device it runs on (until the process ends).  The work list is
+ * copied there from pageable host memory with one hipMemcpyAsync on `stream`.
+ *   Arguments and results as for attn_varlen_paged_fwd, except:
+ *   host    required, with every index array the call uses (cu_seqlens_q,
+ *           cu_seqlens_knew with new tokens, cache_seqlens and block_table
+ *           with a cache): nothing is read back from the device, and page
+ *           ids are range-checked on the host.
+ *   The planner limits its key-range splits to what the scratch array holds;
+ *   a call whose work list and unsplit needs exceed it returns
+ *   VPK_ERROR_CAPACITY before anything is enqueued.  A mixed batch runs its
+ *   two grids one after the other on `stream`.
+ * Every call on a device shares that device's scratch array, which keeps the
+ * last call's contents: calls that overlap in time on one device (two
+ * streams, or two host threads) race and must not be issued; consecutive
+ * calls on one stream are ordered.  Not during stream capture
+ * (VPK_ERROR_NOT_SUPPORTED): the copy reads host memory.
+ */
+int32_t attn_varlen_paged_fwd_noalloc(const vpk_dims* dims,
+                                      const void* q, const int32_t* cu_seqlens_q,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* cu_seqlens_knew,
+                                      void* k_cache, void* v_cache,
+                                      const int32_t* block_table, const int32_t* cache_seqlens,
+                                      int32_t page_size, int32_t causal, float scale,
+                                      const float* kv_scale,
+                                      void* out, float* lse,
+                                      const vpk_host_index* host, void* stream);
+
+/*
  * Rotary position embedding applied by attn_varlen_paged_rope_fwd.  The
  * TransformerEngine KV-cache page ("Add KV cache for paged/non-paged
  * attention", Description) names RoPE for inference as the step that comes

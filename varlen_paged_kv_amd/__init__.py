@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 
-__all__ = ["set_workspace", "workspace_bytes_upper_bound", "library_memory", "attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
+__all__ = ["attn_varlen_paged_fwd_noalloc", "set_workspace", "workspace_bytes_upper_bound", "library_memory", "attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE", "KERNEL_ROPE",
            "attn_varlen_paged_rope_fwd"]
@@ -195,6 +195,26 @@ def attn_varlen_paged_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
                        stream, None)
 
 
+def attn_varlen_paged_fwd_noalloc(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                  k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                                  cu_seqlens_knew: Optional[torch.Tensor] = None,
+                                  k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
+                                  block_table: Optional[torch.Tensor] = None,
+                                  cache_seqlens: Optional[torch.Tensor] = None,
+                                  page_size: int = 0, causal: bool = True, scale: Optional[float] = None,
+                                  kv_scale: Optional[Sequence[float]] = None, *,
+                                  out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                                  host_index: dict, stream=None):
+    """attn_varlen_paged_fwd through the allocation-free entry point: the caller passes ``out`` (and
+    ``lse`` to get it) and host copies of every index array in ``host_index``; the library's
+    static device scratch holds the work list and the split partials.  Returns (out, lse)."""
+    if out is None:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "the allocation-free call writes into a given out")
+    return _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                       cache_seqlens, page_size, causal, scale, kv_scale, out, lse, lse is not None, host_index,
+                       stream, None, noalloc=True)
+
+
 def attn_varlen_paged_rope_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
                                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
                                cu_seqlens_knew: Optional[torch.Tensor] = None,
@@ -230,7 +250,7 @@ def attn_varlen_paged_rope_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
 
 
 def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table, cache_seqlens,
-                page_size, causal, scale, kv_scale, out, lse, return_lse, host_index, stream, rope):
+                page_size, causal, scale, kv_scale, out, lse, return_lse, host_index, stream, rope, noalloc=False):
     lib = _lib.load()
     q = _dev(q, "q", _BF16)
     cu_seqlens_q = _dev(cu_seqlens_q, "cu_seqlens_q", _I32)
@@ -292,8 +312,13 @@ def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache
             _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens), int(page_size),
             int(bool(causal)), float(scale), ks)
     sh = _stream_handle(stream)
-    _ensure_workspace(dims, q.device, sh, rope is not None)
     tail = (_ptr(out), _ptr(lse), ctypes.byref(hi), sh)
+    if noalloc:
+        st = lib.attn_varlen_paged_fwd_noalloc(*args, *tail)
+        del keep
+        _check(st)
+        return out, lse
+    _ensure_workspace(dims, q.device, sh, rope is not None)
     if rope is None:
         st = lib.attn_varlen_paged_fwd(*args, *tail)
     else:

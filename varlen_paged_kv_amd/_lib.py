@@ -29,6 +29,7 @@ EXPORTS = (
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
     "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
     "vpk_plan_run_device_scale", "vpk_set_workspace", "vpk_workspace_bytes_upper_bound", "vpk_library_memory",
+    "attn_varlen_paged_fwd_noalloc",
 )
 
 
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.attn_varlen_paged_fwd.argtypes = [
         P(VpkDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32, P(f32), vp, vp,
         P(VpkHostIndex), vp]
+    lib.attn_varlen_paged_fwd_noalloc.restype = i32
+    lib.attn_varlen_paged_fwd_noalloc.argtypes = lib.attn_varlen_paged_fwd.argtypes
     lib.kv_cache_append.restype = i32
     lib.kv_cache_append.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, vp, i32, P(f32),
                                     P(VpkHostIndex), vp]

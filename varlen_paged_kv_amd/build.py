@@ -26,6 +26,7 @@ SOURCES = [
     "kernels/append.hip",
     "kernels/merge.hip",
     "kernels/rope.hip",
+    "kernels/scratch.hip",
     "host/plan.cpp",
     "host/abi.cpp",
 ]

@@ -873,12 +873,57 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   return release_plan_buffer(w, stream, region);
 }
 
+// The allocation-free form of a direct call: the plan records go, behind a
+// cleared head, into this device's static scratch array with one copy on
+// `stream`, and the split partials after them; the planner limits its splits
+// to what the array holds.  No device or pinned memory is allocated, no event
+// or stream is created; host planning reuses this thread's buffers.  The
+// source of the copy is pageable host memory, which the runtime has staged by
+// the time the copy call returns.
+int32_t plan_and_enqueue_noalloc(const Call& c, const Mirrors& m, int32_t causal, const void* q, const void* k_new,
+                                 const void* v_new, void* k_cache, void* v_cache, const int32_t* block_table,
+                                 float scale, void* out, float* lse, hipStream_t stream) {
+  const vpk_dims* dims = c.d;
+  const int32_t B = dims->batch;
+  int32_t st;
+  if ((st = refuse_capture(stream))) return st;
+  void* sp = nullptr;
+  const int rc = vpk::scratch_address(&sp);
+  if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "hipGetSymbolAddress (scratch)");
+  char* const base = static_cast<char*>(sp);
+  const int32_t num_cus = device_cus();
+  PlanInput in;
+  fill_plan_input(c, m, causal, num_cus, in);
+  in.max_part_rows = std::min<int64_t>(in.max_part_rows,
+                                       part_rows_fitting(vpk::kScratchBytes, dims, num_cus, false, true));
+  static thread_local Plan plan;
+  try {
+    vpk::build_plan(in, plan);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
+  }
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
+  const size_t need = kFlagBytes + L.plan_end + L.part_end;
+  if (need > vpk::kScratchBytes)
+    return fail(VPK_ERROR_CAPACITY, "the call needs " + std::to_string(need) + " bytes of scratch, the "
+                                        "allocation-free entry point has " + std::to_string(vpk::kScratchBytes));
+  // [head: error flag and zero rows][plan records][split partials]
+  static thread_local std::vector<char> stage;
+  stage.assign(kFlagBytes + L.plan_end, 0);
+  serialize_plan(plan, L, m.cu_kn, B, c.page_size, stage.data() + kFlagBytes);
+  const hipError_t e = hipMemcpyAsync(base, stage.data(), stage.size(), hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan into scratch)");
+  const Bases bases{base + kFlagBytes, base + kFlagBytes + L.plan_end, base};
+  return enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale, out, lse,
+                     stream, nullptr, false);
+}
+
 int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
                   const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
                   void* k_cache, void* v_cache, const int32_t* block_table,
                   const int32_t* cache_seqlens, int32_t page_size, int32_t causal, float scale,
                   const float* kv_scale, void* out, float* lse, const vpk_host_index* host,
-                  void* stream_v, const vpk_rope* rope = nullptr) {
+                  void* stream_v, const vpk_rope* rope = nullptr, bool noalloc = false) {
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
   // new tokens are present when any of their arrays is given; with total_knew == 0
@@ -915,11 +960,19 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
     if (lse && !aligned(lse, 4)) return fail(VPK_ERROR_INVALID_VALUE, "lse is not 4-byte aligned");
   }
   if (rope && (st = check_rope_args(c, rope))) return st;
+  if (noalloc && !(host && host->cu_seqlens_q && (!c.has_new || host->cu_seqlens_knew) &&
+                   (!c.has_cache || (host->cache_seqlens && host->block_table))))
+    return fail(VPK_ERROR_INVALID_VALUE, "the allocation-free call needs host copies of every index array "
+                                         "(cu_seqlens_q, and cu_seqlens_knew / cache_seqlens and block_table "
+                                         "when there are new tokens / a cache)");
   if (B == 0) return VPK_SUCCESS;
 
   Mirrors m;
   if ((st = get_mirrors(c, cu_seqlens_q, cu_seqlens_knew, cache_seqlens, host, stream, true, m))) return st;
   if ((st = check_contents(c, m, true))) return st;
+  if (noalloc)
+    return plan_and_enqueue_noalloc(c, m, causal, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse,
+                                    stream);
   return plan_and_enqueue(c, m, causal, q, k_new, v_new, k_cache, v_cache, block_table, scale, out, lse, stream,
                           rope);
 }
@@ -1231,6 +1284,24 @@ int32_t attn_varlen_paged_fwd(const vpk_dims* dims, const void* q, const int32_t
     return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache,
                      block_table, cache_seqlens, page_size, causal, scale, kv_scale, out, lse,
                      host, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
+int32_t attn_varlen_paged_fwd_noalloc(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
+                                      const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
+                                      void* k_cache, void* v_cache, const int32_t* block_table,
+                                      const int32_t* cache_seqlens, int32_t page_size, int32_t causal,
+                                      float scale, const float* kv_scale, void* out, float* lse,
+                                      const vpk_host_index* host, void* stream) {
+  try {
+    g_err.clear();
+    return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache,
+                     block_table, cache_seqlens, page_size, causal, scale, kv_scale, out, lse,
+                     host, stream, nullptr, true);
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
   } catch (...) {

@@ -161,6 +161,11 @@ struct RopeParams {
   int32_t interleaved;
 };
 
+// Size of the device scratch array of the allocation-free entry point, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+int scratch_address(void** ptr);
+
 // Kernel launchers (defined in the .hip files); they return hipError_t as int.
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
                      bool decode, void* stream);
