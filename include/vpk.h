@@ -237,7 +237,12 @@ typedef struct {
  * so a decode row over a cache of Lk keys sits at Lk - 1.  The turned rows
  * are bf16: each product and the difference / sum rounded to float32, then
  * round to nearest even; the cache stores the turned keys.  q and k_new are
- * not modified (the turned copies live in library workspace).
+ * not modified: the attention kernels turn the query rows of prefill-mode
+ * sequences as they load them (interleaved pairs, or half-split pairs with
+ * rotary_dim a multiple of 32), an fp8 cache's append turns the new keys as
+ * it quantises them, and the other rows (decode-mode query rows, other
+ * rotary dims, the new keys of a bf16 cache or of a call without a cache)
+ * are turned into copies in the workspace first.
  * Extra errors: VPK_ERROR_INVALID_VALUE when rope is NULL or its fields break
  * the rules above, when a sequence has more query rows than keys, or when a
  * position reaches max_positions.  Other arguments and errors as for

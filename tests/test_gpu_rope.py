@@ -46,6 +46,10 @@ CASES = [
     ("no_cache_D64_R32", [200, 3, 90], [200, 3, 90], [0, 0, 0], 4, 4, 64, 0, True, None, 32, False),
     ("cache_only_R128_interleaved", [1, 1, 3], None, [300, 1200, 64], 8, 2, 128, 64, True, "bf16", 128, True),
     ("noncausal_S5_D64_R48", [3, 70, 1], [3, 70, 1], [10, 0, 257], 4, 1, 64, 5, False, "bf16", 48, False),
+    # half-split pairs three k-steps apart (rotary_dim 96), turned in the kernels, decode rows between
+    ("mixed_fp8_R96", [1, 50, 1, 1, 90], [1, 50, 1, 1, 90], [700, 20, 0, 64, 300], 8, 2, 128, 16, True, "fp8",
+     96, False),
+    ("prefill_bf16_R64_S64", [130, 257, 8], [130, 257, 8], [33, 0, 500], 8, 2, 128, 64, True, "bf16", 64, False),
 ]
 
 

@@ -484,9 +484,18 @@ struct Layout {
   size_t seqs, tok, items, groups, queues, work, qpos, kpos, plan_end, part_o, part_lse, rot_q, rot_k, part_end;
 };
 
-// `rope`: the call turns q and k_new first; their positions go into the plan
-// and the turned copies into device memory after the split partials.
-Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dims* rope = nullptr) {
+// Rotary embedding (`rope` set): the positions of the query rows and new
+// tokens go into the plan; turned copies of q (rows the attention kernels do
+// not turn themselves) and of k_new (a call without a cache) go into device
+// memory after the split partials.
+struct RopeCopies {
+  bool positions = false;
+  bool q = false;
+  bool k = false;
+};
+
+Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dims* rope = nullptr,
+                  RopeCopies rc = RopeCopies{}) {
   Layout L;
   L.seqs = 0;
   L.tok = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
@@ -502,8 +511,8 @@ Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dim
   L.part_lse = align_up(sizeof(float) * D * static_cast<size_t>(p.part_rows), 256);
   L.rot_q = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
   const size_t hq = rope ? static_cast<size_t>(rope->num_q_heads) : 0, hkv = rope ? static_cast<size_t>(rope->num_kv_heads) : 0;
-  L.rot_k = align_up(L.rot_q + 2 * tq * hq * D, 256);
-  L.part_end = align_up(L.rot_k + 2 * tn * hkv * D, 256);
+  L.rot_k = align_up(L.rot_q + (rc.q ? 2 * tq * hq * D : 0), 256);
+  L.part_end = align_up(L.rot_k + (rc.k ? 2 * tn * hkv * D : 0), 256);
   return L;
 }
 
@@ -545,13 +554,17 @@ int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* 
 // Positions of the rows the rotary embedding turns: query row i of a sequence
 // at Lk - Lq + i (the key its end-aligned causal bound stops at), new token j
 // at Lc + j (the slot the append writes); rows no sequence names get -1.
-void write_rope_positions(const Plan& p, const Layout& L, int32_t B, int32_t Tq, char* base) {
+// With `g` > 0 only the query rows of decode-mode sequences (q_len * g <= 32
+// packed rows) get a position: the others are turned by the prefill-mode
+// kernel as it loads them.
+void write_rope_positions(const Plan& p, const Layout& L, int32_t B, int32_t Tq, char* base, int32_t g = 0) {
   int32_t* qpos = reinterpret_cast<int32_t*>(base + L.qpos);
   int32_t* kpos = reinterpret_cast<int32_t*>(base + L.kpos);
   std::fill(qpos, qpos + Tq, -1);
   for (int32_t b = 0; b < B; ++b) {
     const SeqInfo& q = p.seqs[b];
-    for (int32_t i = 0; i < q.q_len; ++i) qpos[q.q_start + i] = q.kv_len - q.q_len + i;
+    if (g == 0 || static_cast<int64_t>(q.q_len) * g <= vpk::kWaveRows)
+      for (int32_t i = 0; i < q.q_len; ++i) qpos[q.q_start + i] = q.kv_len - q.q_len + i;
     for (int32_t j = 0; j < q.new_len; ++j) kpos[q.kn_start + j] = q.cache_len + j;
   }
 }
@@ -645,10 +658,14 @@ struct Bases {
 // it the two grids run one after the other on `stream` (no events: nothing
 // here allocates, synchronises or records on another stream, so the whole
 // sequence can be captured into a graph).
+// `rq`: query rows turned by the attention kernels as they load them; `rk`:
+// new keys turned by the append (dim 0: no rotation); `q_dec`: if set, the
+// decode-mode grid reads its query rows from there, already turned.
 int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Bases& bs, const void* q,
                     const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int32_t* block_table, int32_t causal, float scale, void* out, float* lse,
-                    hipStream_t stream, Workspace* side, bool timed) {
+                    hipStream_t stream, Workspace* side, bool timed, const vpk::RopeArgs& rq = vpk::RopeArgs{},
+                    const vpk::RopeArgs& rk = vpk::RopeArgs{}, const void* q_dec = nullptr) {
   const vpk_dims* dims = c.d;
   const float* kv_scale = c.kv_scale;
   const int32_t page_size = c.page_size;
@@ -656,11 +673,15 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
   char* const PA = bs.PA;
   int32_t st;
   const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
-  const AppendParams ap = append_params(c, bs.head, R, L, k_new, v_new, k_cache, v_cache, block_table);
+  AppendParams ap = append_params(c, bs.head, R, L, k_new, v_new, k_cache, v_cache, block_table);
+  ap.rope = rk;
+  ap.kpos = reinterpret_cast<const int32_t*>(R + L.kpos);
+  ap.head_dim = dims->head_dim;
   // bf16 cache: attention reads the new tokens from k_new / v_new (the same
   // bytes the append stores), so the append can run inside an attention grid.
-  // fp8 cache: attention must see the quantised bytes, so the append runs first.
-  const bool new_direct = do_append && !c.fp8;
+  // fp8 cache, or keys turned by the append: attention must see the stored
+  // bytes, so the append runs first.
+  const bool new_direct = do_append && !c.fp8 && rk.dim == 0;
   const bool run_pre = plan.prefill.grid > 0;
   const bool run_dec = plan.decode.grid > 0;
   const bool fuse_append = new_direct && (run_pre || run_dec);
@@ -707,6 +728,7 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
     p.qk_scale_log2 = static_cast<float>(p.scale_log2e * (host_scales ? static_cast<double>(kv_scale[0]) : 1.0));
     p.v_scale = host_scales ? kv_scale[1] : 1.0f;
     p.kv_scale_dev = c.fp8 ? c.kv_scale_dev : nullptr;
+    p.rope = rq;
     p.app = ap;
     const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
     // `with_append`: this grid also runs one workgroup per new token
@@ -721,6 +743,11 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       // new tokens in groups: 32 per 512-thread prefill workgroup, 16 per
       // 256-thread decode workgroup
       a.app.tokens_per_wg = dec ? 16 : 32;
+      if (dec && q_dec) {
+        // the decode-mode rows come already turned (a copy)
+        a.q = static_cast<const uint16_t*>(q_dec);
+        a.rope = vpk::RopeArgs{};
+      }
       const int grid = Lc.grid + (with_append ? (dims->total_knew + a.app.tokens_per_wg - 1) / a.app.tokens_per_wg : 0);
       int rc;
       if (timed) {
@@ -829,12 +856,40 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
-  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr);
+  // Rotary embedding: the attention kernels turn the query rows as they load
+  // them (interleaved pairs, or half-split pairs whose two chunks one lane
+  // holds: rotary_dim a multiple of 32); with an fp8 cache the append, which
+  // runs first anyway, turns the new keys as it quantises them; otherwise the
+  // new keys are turned into a copy first (attention and the in-grid append
+  // of a bf16 cache read it), and so are the query rows of other rotary dims.
+  // Decode-mode rows are few and their items short, so turning them in the
+  // kernel would put the angle loads on each item's critical path: they are
+  // turned into the copy instead (measured on the paged decode batch: 146
+  // against 136 us per step).
+  RopeCopies rc;
+  vpk::RopeArgs rq{}, rk{};
+  bool q_dec_copy = false;
+  if (rope) {
+    rc.positions = true;
+    const vpk::RopeArgs ra{rope->cos, rope->sin, rope->rotary_dim, rope->interleaved};
+    const bool fused_q = rope->interleaved != 0 || rope->rotary_dim % 32 == 0;
+    q_dec_copy = fused_q && plan.decode.grid > 0;
+    rc.q = (!fused_q || q_dec_copy) && dims->total_q > 0;
+    if (fused_q) rq = ra;
+    if (c.has_cache && c.fp8) {
+      if (c.has_new) rk = ra;
+    } else {
+      rc.k = k_new != nullptr && dims->total_knew > 0;
+    }
+  }
+  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr, rc);
   if ((st = get_workspace(stream, L.part_end + (upload ? L.plan_end : 0), &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
   char* R = w->plan[region].host;
-  if (rope) write_rope_positions(plan, L, B, dims->total_q, R);
+  if (rope)
+    write_rope_positions(plan, L, B, dims->total_q, R,
+                         q_dec_copy && plan.prefill.grid > 0 ? dims->num_q_heads / dims->num_kv_heads : 0);
   if (upload) {
     char* const dR = w->parts() + L.part_end;
     const hipError_t e = hipMemcpyAsync(dR, R, L.plan_end, hipMemcpyHostToDevice, stream);
@@ -842,8 +897,9 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
     R = dR;
   }
   const Bases bases{R, w->parts(), w->head()};
-  if (rope) {
-    // turn q and k_new into copies; everything after reads the copies
+  if (rc.q || rc.k) {
+    // turned copies of q (rows the kernels do not turn) and of k_new (no
+    // cache); everything after reads the copies
     vpk::RopeParams rp{};
     rp.q = static_cast<const uint16_t*>(q);
     rp.q_out = reinterpret_cast<uint16_t*>(bases.PA + L.rot_q);
@@ -853,8 +909,23 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
     rp.kpos = reinterpret_cast<const int32_t*>(bases.R + L.kpos);
     rp.cos = rope->cos;
     rp.sin = rope->sin;
-    rp.q_rows = dims->total_q;
-    rp.k_rows = k_new ? dims->total_knew : 0;
+    rp.q_rows = rc.q ? dims->total_q : 0;
+    rp.k_rows = rc.k ? dims->total_knew : 0;
+    if (q_dec_copy && plan.prefill.grid > 0) {
+      // only the decode-mode rows are copied: the span of rows they occupy
+      const int32_t g = dims->num_q_heads / dims->num_kv_heads;
+      int32_t lo = dims->total_q, hi = 0;
+      for (const SeqInfo& sq : plan.seqs)
+        if (sq.q_len > 0 && static_cast<int64_t>(sq.q_len) * g <= vpk::kWaveRows) {
+          lo = std::min(lo, sq.q_start);
+          hi = std::max(hi, sq.q_start + sq.q_len);
+        }
+      const size_t off = static_cast<size_t>(std::min(lo, hi)) * dims->num_q_heads * dims->head_dim;
+      rp.q += off;
+      rp.q_out += off;
+      rp.qpos += std::min(lo, hi);
+      rp.q_rows = std::max(0, hi - lo);
+    }
     rp.hq = dims->num_q_heads;
     rp.hkv = dims->num_kv_heads;
     rp.rot_dim = rope->rotary_dim;
@@ -864,11 +935,12 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
       const int rc = vpk::launch_rope(rp, dims->head_dim, stream);
       if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "rotary embedding launch");
     }
-    q = rp.q_out;
-    if (k_new) k_new = rp.k_out;
+    if (rc.q && !q_dec_copy) q = rp.q_out;
+    if (rc.k) k_new = rp.k_out;
   }
+  const void* q_dec = q_dec_copy ? static_cast<const void*>(bases.PA + L.rot_q) : nullptr;
   if ((st = enqueue_all(c, plan, L, bases, q, k_new, v_new, k_cache, v_cache, block_table, causal, scale,
-                        out, lse, stream, w, true)))
+                        out, lse, stream, w, true, rq, rk, q_dec)))
     return st;
   return release_plan_buffer(w, stream, region);
 }

@@ -12,7 +12,8 @@ namespace vpk {
 namespace {
 
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  __shared__ int64_t dst[kAppendTokensMax];
+  // destination rows, then (rotary embedding) the tokens' positions
+  __shared__ int64_t dst[kAppendTokensMax + kAppendTokensMax / 2];
   append_tokens(p, blockIdx.x, threadIdx.x, blockDim.x, dst);
 }
 

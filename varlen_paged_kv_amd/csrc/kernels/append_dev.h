@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "../vpk_internal.h"
+#include "rope_dev.h"
 
 namespace vpk {
 namespace append_detail {
@@ -55,15 +56,21 @@ __device__ __forceinline__ uint32_t enc2(uint32_t two_bf16, float inv) {
 // Store the new tokens of workgroup `wg` (tokens [wg * tokens_per_wg, ...) of
 // the call) with `nthreads` threads of index `tid`.  First each token's
 // destination row (page read from block_table at the index the plan carries,
-// slot from the plan) goes to `dst` in LDS (tokens_per_wg entries), then the
-// threads copy 16-byte chunks, whose sources and destinations are then known
-// up front.  A page id outside [0, num_pages) drops the token and raises bit
-// 0 of the device error flag instead of writing out of bounds.
+// slot from the plan) goes to `dst` in LDS (tokens_per_wg entries, followed
+// by as many int32 positions when the keys are turned by rotary embedding),
+// then the threads copy 16-byte chunks, whose sources and destinations are
+// then known up front.  A page id outside [0, num_pages) drops the token and
+// raises bit 0 of the device error flag instead of writing out of bounds.
+// With p.rope.dim > 0 each key chunk is turned at its token's position before
+// it is stored (or quantised), so the cache holds the turned keys.
 __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int tid, int nthreads,
                                               int64_t* dst) {
   using namespace append_detail;
   const int t0 = wg * p.tokens_per_wg;
   const int nt = min(p.tokens_per_wg, p.total_knew - t0);
+  int32_t* const tpos = reinterpret_cast<int32_t*>(dst + kAppendTokensMax);
+  if (p.rope.dim > 0)
+    for (int i = tid; i < nt; i += nthreads) tpos[i] = p.kpos[t0 + i];
   for (int i = tid; i < nt; i += nthreads) {
     // block_table index of the token's page id (inside its sequence's row:
     // the host checked the capacity) and the slot in that page
@@ -115,6 +122,13 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
       if (dst_row < 0) continue;
       const bool is_v = c >= chunks;
       const int cc = is_v ? c - chunks : c;
+      if (!is_v && p.rope.dim > 0) {
+        // chunk cc of the token row = chunk cc % (D / 8) of head cc / (D / 8)
+        const int hc = p.head_dim / 8;
+        const int head = cc / hc;
+        const uint16_t* hrow = p.k_new + static_cast<int64_t>(t0 + i) * p.row_elems + head * p.head_dim;
+        x[k] = rope_chunk(p.rope, hrow, cc - head * hc, x[k], tpos[i]);
+      }
       if (p.fp8) {
         const float inv = is_v ? v_inv : k_inv;
         uint8_t* d = static_cast<uint8_t*>(is_v ? p.v_cache : p.k_cache) + dst_row + cc * 8;

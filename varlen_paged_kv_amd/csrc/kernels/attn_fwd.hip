@@ -375,6 +375,99 @@ struct Src {
     }
   }
 
+  // Rotary embedding of this lane's query chunks (chunk 2 s + lg at k-step s)
+  // at position `pos` = Lk - Lq + token (the key the row's end-aligned causal
+  // bound stops at).  The angles are loaded first (rope_load, issued with the
+  // Q loads and the first staging copies, so one memory round trip covers
+  // them all) and applied once they have arrived (rope_apply).  The caller
+  // turns only rotary dims that are multiples of 32 in the half-split
+  // pairing, so that both chunks of a pair (c and c + dim / 16, k-steps s and
+  // s + dim / 32) sit in one lane; interleaved pairs sit inside one chunk.
+  // Angle slots: interleaved, a[s] = {cos, sin} of k-step s's 4 pairs;
+  // half-split, a[s] = cos and a[s + KSTEPS / 2] = sin of the 8 pairs whose
+  // first chunk is at k-step s.
+  struct QAngles {
+    float4 a[C::KSTEPS][2];
+  };
+  __device__ static __forceinline__ void rope_load(const RopeArgs& r, int pos, int lg, QAngles& g) {
+    const int half = r.dim >> 1;
+    const float* cr = r.cos + static_cast<int64_t>(pos) * half;
+    const float* sr = r.sin + static_cast<int64_t>(pos) * half;
+    if (r.interleaved) {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        const int d0 = 16 * s + 8 * lg;
+        if (d0 < r.dim) {
+          g.a[s][0] = *reinterpret_cast<const float4*>(cr + (d0 >> 1));
+          g.a[s][1] = *reinterpret_cast<const float4*>(sr + (d0 >> 1));
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS / 2; ++s) {
+      if (16 * s < half) {
+        const int i0 = 16 * s + 8 * lg;
+        g.a[s][0] = *reinterpret_cast<const float4*>(cr + i0);
+        g.a[s][1] = *reinterpret_cast<const float4*>(cr + i0 + 4);
+        g.a[s + C::KSTEPS / 2][0] = *reinterpret_cast<const float4*>(sr + i0);
+        g.a[s + C::KSTEPS / 2][1] = *reinterpret_cast<const float4*>(sr + i0 + 4);
+      }
+    }
+  }
+  __device__ static __forceinline__ void rope_apply(const RopeArgs& r, int lg, const QAngles& g,
+                                                    bf16x8 (&qf)[C::KSTEPS]) {
+    using namespace rope_detail;
+    if (r.interleaved) {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+        if (16 * s + 8 * lg < r.dim) {
+          const float cs[4] = {g.a[s][0].x, g.a[s][0].y, g.a[s][0].z, g.a[s][0].w};
+          const float sn[4] = {g.a[s][1].x, g.a[s][1].y, g.a[s][1].z, g.a[s][1].w};
+          u32x4 x = __builtin_bit_cast(u32x4, qf[s]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint16_t ra, rb;
+            turn(bf16_lo(x[q]), bf16_hi(x[q]), cs[q], sn[q], ra, rb);
+            x[q] = ra | (static_cast<uint32_t>(rb) << 16);
+          }
+          qf[s] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+      return;
+    }
+    switch (r.dim >> 5) {
+      case 1: rope_pairs<1>(g, qf); break;
+      case 2: rope_pairs<2>(g, qf); break;
+      case 3: if constexpr (C::KSTEPS >= 6) rope_pairs<3>(g, qf); break;
+      case 4: if constexpr (C::KSTEPS >= 8) rope_pairs<4>(g, qf); break;
+      default: break;
+    }
+  }
+  template <int DS>
+  __device__ static __forceinline__ void rope_pairs(const QAngles& g, bf16x8 (&qf)[C::KSTEPS]) {
+    using namespace rope_detail;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const float4 c0 = g.a[s][0], c1 = g.a[s][1];
+      const float4 s0 = g.a[s + C::KSTEPS / 2][0], s1 = g.a[s + C::KSTEPS / 2][1];
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      u32x4 a = __builtin_bit_cast(u32x4, qf[s]);
+      u32x4 b = __builtin_bit_cast(u32x4, qf[s + DS]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint16_t a0, b0, a1, b1;
+        turn(bf16_lo(a[q]), bf16_lo(b[q]), cs[2 * q], sn[2 * q], a0, b0);
+        turn(bf16_hi(a[q]), bf16_hi(b[q]), cs[2 * q + 1], sn[2 * q + 1], a1, b1);
+        a[q] = a0 | (static_cast<uint32_t>(a1) << 16);
+        b[q] = b0 | (static_cast<uint32_t>(b1) << 16);
+      }
+      qf[s] = __builtin_bit_cast(bf16x8, a);
+      qf[s + DS] = __builtin_bit_cast(bf16x8, b);
+    }
+  }
+
   // a7: 4 consecutive head-dim values (from d0) of tile row r, to out / lse or
   // to the split partials
   __device__ static __forceinline__ void store4(const AttnParams& p, int part, int q_start, int r, int token,
@@ -896,7 +989,7 @@ __device__ __forceinline__ void scales(const AttnParams& p, float& qk, float& vs
   }
 }
 
-template <int D, int FMT, bool PAGED>
+template <int D, int FMT, bool PAGED, bool ROPE>
 struct Decode : Src<D, FMT, PAGED> {
   using B = Src<D, FMT, PAGED>;
   using C = Cfg<D>;
@@ -915,7 +1008,7 @@ struct Decode : Src<D, FMT, PAGED> {
   // in its own half of an LDS stage (no workgroup barrier in the loop), and
   // keeps its own running max / sum / output; the four partial states are
   // merged through LDS at the end.
-  __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
+  __device__ static __forceinline__ void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
                               uint16_t* smem, float c, float v_scale, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
@@ -931,6 +1024,12 @@ struct Decode : Src<D, FMT, PAGED> {
     bf16x8 qf[C::KSTEPS];
     int token, qh;
     B::load_q(p, sq, it.kvh, item.row0 + lr, row_ok, lg, qf, token, qh);
+    if constexpr (ROPE) {
+      // angles loaded beside Q, applied once both have arrived
+      typename B::QAngles qa;
+      if (row_ok) B::rope_load(p.rope, sq.kv_len - sq.q_len + token, lg, qa);
+      if (row_ok) B::rope_apply(p.rope, lg, qa, qf);
+    }
     const int shift = sq.kv_len - sq.q_len;
     int lim = it.kend - 1;
     if (p.causal) lim = min(lim, token + shift);
@@ -1063,7 +1162,7 @@ struct Decode : Src<D, FMT, PAGED> {
     }
   }
 
-  __device__ static void run(const AttnParams& p) {
+  __device__ static __forceinline__ void run(const AttnParams& p) {
     // two K/V stages used as four per-wave half stages, then as the area
     // where the waves combine their partial softmax states
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE + kCombineExtra];
@@ -1088,7 +1187,7 @@ struct Decode : Src<D, FMT, PAGED> {
 };
 
 // ----------------------------------------------------------------- prefill mode
-template <int D, int FMT, bool PAGED>
+template <int D, int FMT, bool PAGED, bool ROPE>
 struct Prefill : Src<D, FMT, PAGED> {
   using B = Src<D, FMT, PAGED>;
   using C = Cfg<D>;
@@ -1104,7 +1203,7 @@ struct Prefill : Src<D, FMT, PAGED> {
   static constexpr int DBLK = C::DBLK;
   static constexpr int F8PASS = (kBlockN * B::F8CH + NT - 1) / NT;
 
-  __device__ static void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
+  __device__ static __forceinline__ void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq, const Item& it,
                               uint16_t* smem, int* lims, float c, float v_scale, int wave, int lr, int lg, int t) {
     const int lane = t & 63;
     const int kbeg = item.key_begin;
@@ -1188,6 +1287,12 @@ struct Prefill : Src<D, FMT, PAGED> {
     bf16x8 qf[KSTEPS];
     int token, qh;
     B::load_q(p, sq, it.kvh, item.row0 + wrow, row_ok, lg, qf, token, qh);
+    // rotary embedding: the angles are loaded now, beside Q and before the
+    // first staging copies, and applied after the prologue's wait for them
+    typename B::QAngles qa;
+    if constexpr (ROPE) {
+      if (row_ok) B::rope_load(p.rope, sq.kv_len - sq.q_len + token, lg, qa);
+    }
 
     // per-row and per-wave key bounds
     const int shift = sq.kv_len - sq.q_len;
@@ -1211,16 +1316,22 @@ struct Prefill : Src<D, FMT, PAGED> {
     const int n_full = min(nb_w, max(0, (wlo - kbeg + 1) / kBlockN));
 
     f32x16 o[DBLK];
+    float m_run, l_run;
+    auto init_state = [&] {
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
+      for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    float m_run = -INFINITY;
-    // opaque start value: otherwise the compiler folds the first block's
-    // threshold m c + 8 into a constant that it keeps live (and spills)
-    // across the whole loop
-    asm volatile("" : "+v"(m_run));
-    float l_run = 0.f;
+        for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+      m_run = -INFINITY;
+      // opaque start value: otherwise the compiler folds the first block's
+      // threshold m c + 8 into a constant that it keeps live (and spills)
+      // across the whole loop
+      asm volatile("" : "+v"(m_run));
+      l_run = 0.f;
+    };
+    // (with rotary embedding the running state is set after the prologue,
+    // where the angles are no longer live)
+    if constexpr (!ROPE) init_state();
     f32x16 acc[2];
     bf16x8 pf[2][2];
 
@@ -1247,6 +1358,10 @@ struct Prefill : Src<D, FMT, PAGED> {
     } else {
       for (int j = 0; j < 3 && j < nblk; ++j) stage_dma(j);
       wait_vmem_upto(nblk > 2 ? 2 * DMA_PER_TILE : 0);
+    }
+    if constexpr (ROPE) {
+      if (row_ok) B::rope_apply(p.rope, lg, qa, qf);
+      init_state();
     }
     // Q is complete here (its loads are older than the copies just waited
     // for); an empty use tells the compiler so, which keeps it from placing a
@@ -1394,7 +1509,7 @@ struct Prefill : Src<D, FMT, PAGED> {
     }
   }
 
-  __device__ static void run(const AttnParams& p) {
+  __device__ static __forceinline__ void run(const AttnParams& p) {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * C::STAGE];
     __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
     __shared__ int lims[NT];
@@ -1417,23 +1532,33 @@ struct Prefill : Src<D, FMT, PAGED> {
   }
 };
 
-template <int D, int FMT, bool PAGED>
+// ROPE: the query rows are turned by rotary embedding as they are loaded
+// (separate instantiations, so that the other kernels' register allocation
+// does not carry the rotation code)
+template <int D, int FMT, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(const AttnParams p) {
-  Decode<D, FMT, PAGED>::run(p);
+  Decode<D, FMT, PAGED, ROPE>::run(p);
 }
 
-template <int D, int FMT, bool PAGED>
+template <int D, int FMT, bool PAGED, bool ROPE>
 __global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_prefill_kernel(const AttnParams p) {
-  Prefill<D, FMT, PAGED>::run(p);
+  Prefill<D, FMT, PAGED, ROPE>::run(p);
 }
 
-template <int D, int FMT, bool PAGED>
+template <int D, int FMT, bool PAGED, bool ROPE>
 int launch_t(const AttnParams& p, int grid, bool decode, hipStream_t s) {
   if (decode)
-    hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, FMT, PAGED>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_prefill_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
   return static_cast<int>(hipGetLastError());
+}
+
+template <int D, bool ROPE>
+int launch_d(const AttnParams& p, int grid, int kv_format, bool paged, bool decode, hipStream_t s) {
+  if (!paged) return launch_t<D, kKvBf16, false, ROPE>(p, grid, decode, s);
+  if (kv_format == kKvFp8) return launch_t<D, kKvFp8, true, ROPE>(p, grid, decode, s);
+  return launch_t<D, kKvBf16, true, ROPE>(p, grid, decode, s);
 }
 
 }  // namespace
@@ -1441,16 +1566,13 @@ int launch_t(const AttnParams& p, int grid, bool decode, hipStream_t s) {
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
                      bool decode, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (head_dim == 128) {
-    if (!paged) return launch_t<128, kKvBf16, false>(p, grid, decode, s);
-    if (kv_format == kKvFp8) return launch_t<128, kKvFp8, true>(p, grid, decode, s);
-    return launch_t<128, kKvBf16, true>(p, grid, decode, s);
-  }
-  if (head_dim == 64) {
-    if (!paged) return launch_t<64, kKvBf16, false>(p, grid, decode, s);
-    if (kv_format == kKvFp8) return launch_t<64, kKvFp8, true>(p, grid, decode, s);
-    return launch_t<64, kKvBf16, true>(p, grid, decode, s);
-  }
+  const bool rope = p.rope.dim > 0;
+  if (head_dim == 128)
+    return rope ? launch_d<128, true>(p, grid, kv_format, paged, decode, s)
+                : launch_d<128, false>(p, grid, kv_format, paged, decode, s);
+  if (head_dim == 64)
+    return rope ? launch_d<64, true>(p, grid, kv_format, paged, decode, s)
+                : launch_d<64, false>(p, grid, kv_format, paged, decode, s);
   return static_cast<int>(hipErrorInvalidValue);
 }
 

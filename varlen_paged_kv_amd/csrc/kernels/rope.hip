@@ -1,18 +1,8 @@
-// Rotary position embedding of the query rows and the new key rows, gfx950.
-//
-// The rotation is the one of "RoFormer: Enhanced Transformer with Rotary
-// Position Embedding" (Su et al., section 3.4): coordinates are taken in pairs
-// (a, b) and pair i of a row at position m is turned by the angle m * theta_i,
-// whose cosine and sine the caller supplies as tables [max_positions,
-// rotary_dim / 2] (float32).  Pairing: half-split (coordinate i with
-// i + rotary_dim / 2) or interleaved (2i with 2i + 1).  Coordinates at or past
-// rotary_dim are copied.  The TransformerEngine KV-cache page ("Add KV cache
-// for paged/non-paged attention", Description) names RoPE for inference as the
-// step that comes with the cache path.
-//
-// Arithmetic (the turned rows are bf16 codes, so it is fixed): each product
-// rounded to float32, their difference or sum rounded to float32 (no fused
-// multiply-add), then round to nearest even to bf16.
+// Rotary position embedding of rows into turned copies, gfx950 (the rotation
+// and its arithmetic are described in rope_dev.h).  Used for the new key rows
+// of a call without a cache, which attention reads straight from k_new; query
+// rows are turned inside the attention kernels and the new keys of a cached
+// call inside the append.
 //
 // The pass is HBM-bound and elementwise: a thread turns 16-byte chunks of
 // output (8 coordinates of one head of one row); in the half-split form it
@@ -26,26 +16,15 @@
 #include <algorithm>
 
 #include "../vpk_internal.h"
+#include "rope_dev.h"
 
 namespace vpk {
 namespace {
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+using rope_detail::bf16_rne;
+using rope_detail::turn;
 
 __device__ __forceinline__ float bf16_f32(uint32_t half_word) { return __uint_as_float(half_word << 16); }
-
-// a' = a c - b s, b' = a s + b c with every operation rounded on its own
-__device__ __forceinline__ void turn(float a, float b, float c, float s, uint16_t& ra, uint16_t& rb) {
-#pragma clang fp contract(off)
-  const float ac = a * c, bs = b * s, as = a * s, bc = b * c;
-  ra = bf16_rne(ac - bs);
-  rb = bf16_rne(as + bc);
-}
 
 __device__ __forceinline__ void unpack8(const uint4 v, float* x) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};

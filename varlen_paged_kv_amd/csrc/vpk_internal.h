@@ -66,6 +66,15 @@ struct MergeGroup {
 
 enum KvFormat : int32_t { kKvBf16 = 0, kKvFp8 = 1 };
 
+// Rotary embedding applied inside the attention kernels (query rows, as they
+// are loaded) and the append (new key rows, as they are stored).
+struct RopeArgs {
+  const float* cos;           // [max_positions, dim / 2]
+  const float* sin;
+  int32_t dim;                // rotary_dim (multiple of 16), or 0: no rotation
+  int32_t interleaved;        // 0: pairs (i, i + dim / 2); 1: pairs (2i, 2i + 1)
+};
+
 // largest number of new tokens one append workgroup stores
 constexpr int kAppendTokensMax = 32;
 
@@ -88,6 +97,9 @@ struct AppendParams {
   float k_inv_scale;          // fp32(1 / k_scale)
   float v_inv_scale;
   const float* kv_scale_dev;  // fp8: {k_scale, v_scale} in device memory, read at run time (overrides the two above)
+  RopeArgs rope;              // new key rows turned before they are stored (dim 0: none)
+  const int32_t* kpos;        // with rope: [Tn] position of each new token
+  int32_t head_dim;
 };
 
 struct AttnParams {
@@ -123,6 +135,7 @@ struct AttnParams {
   float v_scale;              // 1 (bf16) or v_scale (fp8)
   const float* kv_scale_dev;  // fp8: {k_scale, v_scale} in device memory (overrides the two above)
   double scale_log2e;         // scale * log2(e) in double, for the device-scale product
+  RopeArgs rope;              // query rows turned as they are loaded (dim 0: none)
   AppendParams app;           // the append, when it runs inside this grid
 };
 
