@@ -163,11 +163,12 @@ def cpu_baseline(wl, budget_s):
 class Runner:
     """Device copies of one workload's inputs and the timing passes over them."""
 
-    def __init__(self, wl, dev, rotate, rope=False):
+    def __init__(self, wl, dev, rotate, rope=False, mode="direct"):
         import torch
         import varlen_paged_kv_amd as vpk
         self.torch, self.vpk, self.wl = torch, vpk, wl
         self.fp8 = wl.cache_dtype == "fp8"
+        self.mode = mode
 
         def bf16(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -192,6 +193,33 @@ class Runner:
             self.copies.append(c)
         self.host = dict(cu_seqlens_q=wl.cu_seqlens_q, cu_seqlens_knew=wl.cu_seqlens_knew,
                          cache_seqlens=wl.cache_seqlens, block_table=wl.block_table)
+        self.plan = None
+        self.graphs = []
+        if mode in ("prepared", "graph"):
+            # one plan for the lengths (all copies share them); a graph of one run per copy
+            has_cache = wl.k_cache is not None
+            self.plan = vpk.Plan(wl.cu_seqlens_q, wl.Hq, wl.Hkv, wl.D, cu_seqlens_knew=wl.cu_seqlens_knew,
+                                 cache_seqlens=wl.cache_seqlens if has_cache else None,
+                                 block_table=wl.block_table if has_cache else None,
+                                 page_size=wl.page_size if has_cache else 0, num_pages=wl.num_pages,
+                                 max_pages_per_seq=wl.block_table.shape[1] if has_cache else 0,
+                                 cache_dtype=wl.cache_dtype or "bf16", causal=wl.causal)
+        if mode == "graph":
+            import gc
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in range(len(self.copies)):
+                    self._plan_run(i)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            gc.collect()
+            for i in range(len(self.copies)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self._plan_run(i)
+                self.graphs.append(g)
+            torch.cuda.synchronize()
         self.rope_kw = None
         if rope:
             from synth import rope_tables
@@ -199,7 +227,18 @@ class Runner:
             self.rope_kw = dict(rope_cos=torch.from_numpy(cos).to(dev), rope_sin=torch.from_numpy(sin).to(dev),
                                 rotary_dim=wl.D, interleaved=False)
 
+    def _plan_run(self, i):
+        wl, c = self.wl, self.copies[i % len(self.copies)]
+        self.plan.run(c["q"], c["k_new"], c["v_new"], c["kc"], c["vc"], c["bt"], scale=wl.scale,
+                      kv_scale=wl.kv_scale if self.fp8 else None, out=c["out"], lse=c["lse"])
+
     def step(self, i):
+        if self.mode == "graph":
+            self.graphs[i % len(self.graphs)].replay()
+            return
+        if self.mode == "prepared":
+            self._plan_run(i)
+            return
         wl, c = self.wl, self.copies[i % len(self.copies)]
         args = (c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"], c["vc"], c["bt"], c["cl"],
                 wl.page_size, wl.causal, wl.scale, wl.kv_scale if self.fp8 else None)
@@ -245,7 +284,8 @@ class Runner:
         inst_ms, _ = self.timed(steps, True)
         kern = {}
         for key, kid in (("prefill_grid", vpk.KERNEL_ATTENTION), ("decode_grid", vpk.KERNEL_ATTENTION_DECODE),
-                         ("append", vpk.KERNEL_APPEND), ("merge", vpk.KERNEL_MERGE), ("rope", vpk.KERNEL_ROPE)):
+                         ("mixed_grid", vpk.KERNEL_ATTENTION_MIXED), ("append", vpk.KERNEL_APPEND),
+                         ("merge", vpk.KERNEL_MERGE), ("rope", vpk.KERNEL_ROPE)):
             ms, n = vpk.timing_read(kid)
             kern[key] = (ms * 1e3 / n if n else 0.0, n)
         gpu_ms, wall = self.timed(steps, False)
@@ -301,7 +341,7 @@ def measure_workload(name, args, dev, cpu_budget):
     pre_flops, dec_bytes = float(flops[~dec].sum()), float(kv_bytes[dec].sum())
     log(f"{name}: Tq={wl.Tq} Tn={wl.Tn} pages={wl.num_pages} flops/step={step_flops:.3e} "
         f"kv bytes/step={step_bytes:.3e} (inputs drawn in {time.perf_counter() - t0:.1f} s)")
-    r = Runner(wl, dev, args.rotate, rope=args.rope)
+    r = Runner(wl, dev, args.rotate, rope=args.rope, mode=args.mode)
     m = r.measure(args.steps, args.warmup, args.settle)
     log(summary(name, m))
     k = m["kernels"]
@@ -317,8 +357,17 @@ def measure_workload(name, args, dev, cpu_budget):
     elif name == "mixed_fp8":
         obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
-        roof = mfma_roof(pre_flops, k["prefill_grid"][0], load_traffic(name), note)
-        roof["decode_grid"] = hbm_roof(dec_bytes, k["decode_grid"][0], None, note)
+        if k["mixed_grid"][1]:
+            # one launch for both kinds of items: its prefill FLOPs and decode bytes over its time
+            mus = k["mixed_grid"][0]
+            roof = mfma_roof(pre_flops, mus, load_traffic(name), note)
+            roof["kernel"] = "attention (mixed grid: prefill-mode tiles and decode-mode splits in one launch)"
+            roof["decode_part"] = hbm_roof(dec_bytes, mus, None, note, kernel="the same launch's decode-mode items")
+            roof["combined_frac_kernel"] = (pre_flops / (PEAK_BF16_TFLOPS * 1e12) +
+                                            dec_bytes / (PEAK_HBM_GBS * 1e9)) / (mus / 1e6)
+        else:
+            roof = mfma_roof(pre_flops, k["prefill_grid"][0], load_traffic(name), note)
+            roof["decode_grid"] = hbm_roof(dec_bytes, k["decode_grid"][0], None, note)
         # the whole step against both roofs at once: prefill FLOPs at the bf16 peak plus
         # decode KV bytes at the HBM peak, over the step time
         roof["combined_frac"] = (pre_flops / (PEAK_BF16_TFLOPS * 1e12) + dec_bytes / (PEAK_HBM_GBS * 1e9)) / elapsed
@@ -327,7 +376,7 @@ def measure_workload(name, args, dev, cpu_budget):
         parts = {}
         for label, seqs in (("prefill_rows", np.nonzero(~dec)[0]), ("decode_rows", np.nonzero(dec)[0])):
             sub = subset(wl, seqs)
-            rs = Runner(sub, dev, args.rotate)
+            rs = Runner(sub, dev, args.rotate, mode=args.mode)
             ms = rs.measure(args.steps, args.warmup, args.settle)
             log(summary(f"{name} {label} alone", ms))
             parts[label] = ms["ms_per_step"]
@@ -368,7 +417,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference kernel for HBM counters)")
     ap.add_argument("--persistent", type=int, default=-1)
+    ap.add_argument("--mode", default="direct", choices=["direct", "prepared", "graph"],
+                    help="each step a direct call, a prepared-plan run (vpk_plan_run), or a graph replay of one")
     ap.add_argument("--plan-upload", type=int, default=0, help="library option plan_upload (0 or 1)")
+    ap.add_argument("--mixed-grid", type=int, default=-2, help="library option mixed_grid (-1, 0 or 1; default: the library's)")
+    ap.add_argument("--mixed-dec-parts", type=int, default=0, help="library option mixed_dec_parts (0: the library's)")
     ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
     args = ap.parse_args()
 
@@ -384,6 +437,10 @@ def main():
     dev = torch.device("cuda:0")
     vpk.set_option("persistent", args.persistent)
     vpk.set_option("plan_upload", args.plan_upload)
+    if args.mixed_grid >= -1:
+        vpk.set_option("mixed_grid", args.mixed_grid)
+    if args.mixed_dec_parts > 0:
+        vpk.set_option("mixed_dec_parts", args.mixed_dec_parts)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

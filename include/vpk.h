@@ -430,6 +430,16 @@ int32_t vpk_abi_version(void);
  *                      1 = persistent grid with static per-workgroup queues.
  *   "split_min_keys"   smallest key range of a split part (default 256).
  *   "num_cus"          compute units assumed by the planner (0 = query device).
+ *   "mixed_grid"       for a call with both prefill-mode items (more than 32
+ *                      packed rows per kv head) and decode-mode items: 1 = one
+ *                      launch of 512-thread workgroups, prefill tiles first;
+ *                      0 = two grids (side by side for direct calls, one after
+ *                      the other for prepared ones and the allocation-free
+ *                      form); -1 (default) = two grids side by side for direct
+ *                      calls, one launch where they would run one after the
+ *                      other.  Plans built while it is 0 have no one-launch grid.
+ *   "mixed_dec_parts"  decode-mode split size in such a call: parts of the
+ *                      total decode work / (num_cus * this); default 1.
  *   "plan_upload"      0 = the kernels read a direct call's work list from
  *                      pinned host memory (default); 1 = it is copied into the
  *                      workspace on the call's stream first.
@@ -448,7 +458,9 @@ int32_t vpk_set_option(const char* name, int64_t value);
  *               or kv_cache_append),
  *           2 = attention grid of decode-mode items (likewise),
  *           3 = LSE merge of split parts,
- *           4 = rotary embedding of q / k_new (attn_varlen_paged_rope_fwd).
+ *           4 = rotary embedding of the rows turned into copies before attention,
+ *           5 = mixed attention grid (prefill-mode and decode-mode items of one
+ *               call in one launch, option "mixed_grid").
  */
 int32_t vpk_timing_enable(int32_t enable);
 int32_t vpk_timing_reset(void);

@@ -29,6 +29,7 @@ def _reset_options():
     vpk.set_option("force_splits", 0)
     vpk.set_option("persistent", -1)
     vpk.set_option("num_cus", 0)
+    vpk.set_option("mixed_grid", 1)
 
 
 _run_and_check = run_and_check
@@ -311,3 +312,29 @@ def test_full_size_workloads(name):
             check_attention(o_all[s:e], l_all[:, s:e], ref["out"][s:e], ref["lse"][:, s:e], kind,
                             label=f"{name} seq {b}")
     say(f"[ok] {name}: all {wl.B} sequences; max {errs[0]:.2e} mean {errs[1]:.2e} lse {errs[2]:.2e}")
+
+
+MIXED_CASES = [
+    # label, q_lens, cache_lens, Hq, Hkv, D, S, cache
+    ("bf16_D128", [1, 300, 1, 1, 40, 1], [3000, 100, 700, 0, 50, 5000], 8, 2, 128, 16, "bf16"),
+    ("fp8_D128_S64", [2, 1, 513, 1, 1], [900, 4000, 0, 64, 2500], 8, 2, 128, 64, "fp8"),
+    ("bf16_D64_g8", [1, 1, 130, 1], [2000, 33, 70, 1000], 16, 2, 64, 16, "bf16"),
+    ("fp8_D64_S5", [3, 90, 1, 1], [77, 10, 900, 3], 4, 1, 64, 5, "fp8"),
+]
+
+
+@pytest.mark.parametrize("persistent", [0, 1])
+@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("case", MIXED_CASES, ids=[c[0] for c in MIXED_CASES])
+def test_mixed_batches_one_launch_and_two_grids(case, grid, persistent):
+    """A batch with both decode-mode and prefill-mode items: in one launch (the mixed grid, decode
+    items on eight waves) and in two grids, with and without persistent queues, against the oracle."""
+    label, ql, cl, hq, hkv, d, s, cache = case
+    vpk.set_option("mixed_grid", grid)
+    vpk.set_option("persistent", persistent)
+    try:
+        wl = make_custom(q_lens=ql, new_lens=ql, cache_lens=cl, Hq=hq, Hkv=hkv, D=d, page_size=s, causal=True,
+                         cache_dtype=cache, seed=zlib.crc32(label.encode()) % 1000)
+        _run_and_check(wl, f"mixed {label} grid={grid} persistent={persistent}")
+    finally:
+        vpk.set_option("mixed_grid", 1)

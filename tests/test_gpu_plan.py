@@ -21,8 +21,14 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def _reset_options():
+    # a batch with both kinds of items runs in one launch in both the direct
+    # call and the plan run, so that the two can be compared bit for bit (by
+    # default a direct call runs two grids side by side and a plan run the
+    # one launch; each is checked against the oracle elsewhere as well)
+    vpk.set_option("mixed_grid", 1)
     yield
     vpk.set_option("force_splits", 0)
+    vpk.set_option("mixed_grid", -1)
 
 
 def _plan_for(dc):
@@ -82,13 +88,15 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("mixed_grid", [0, 1])
 @pytest.mark.parametrize("splits", [0, 3])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_plan_run_equals_direct_call(case, splits):
+def test_plan_run_equals_direct_call(case, splits, mixed_grid):
     vpk.set_option("force_splits", splits)
+    vpk.set_option("mixed_grid", mixed_grid)
     wl = CASES[case]()
     dc = DeviceCall(wl, with_new=wl.k_new is not None)
-    say(f"[case] plan {case} splits={splits}")
+    say(f"[case] plan {case} splits={splits} mixed_grid={mixed_grid}")
     ref_out, ref_lse = dc.run()
     plan = _plan_for(dc)
     out, lse = _run_plan(plan, dc)

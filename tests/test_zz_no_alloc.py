@@ -28,6 +28,16 @@ def _noalloc(dc):
         wl.causal, wl.scale, wl.kv_scale if dc.fp8 else None, out=out, lse=lse, host_index=dc.host)
 
 
+@pytest.fixture(autouse=True)
+def _one_launch():
+    # the allocation-free call runs a batch with both kinds of items in one
+    # launch (it has no side stream for two grids); the direct call it is
+    # compared with bit for bit does the same under this option
+    vpk.set_option("mixed_grid", 1)
+    yield
+    vpk.set_option("mixed_grid", -1)
+
+
 def test_noalloc_two_calls_match_the_direct_call():
     cases = [
         # a mixed batch over an fp8 cache: both grids, split parts (merge pass) from the scratch

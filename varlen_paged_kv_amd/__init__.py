@@ -25,11 +25,14 @@ from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 __all__ = ["attn_varlen_paged_fwd_noalloc", "set_workspace", "workspace_bytes_upper_bound", "library_memory", "attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE", "KERNEL_ROPE",
+           "KERNEL_ATTENTION_MIXED",
            "attn_varlen_paged_rope_fwd"]
 
 # kernel ids of the timing API: the prefill-mode attention grid, the standalone
-# append, the decode-mode attention grid, the split merge
-KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE, KERNEL_ROPE = 0, 1, 2, 3, 4
+# append, the decode-mode attention grid, the split merge, the rotary copies,
+# the mixed attention grid (both kinds of items in one launch)
+KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE, KERNEL_ROPE, KERNEL_ATTENTION_MIXED = \
+    0, 1, 2, 3, 4, 5
 
 
 class VpkError(RuntimeError):

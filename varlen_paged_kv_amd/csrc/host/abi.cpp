@@ -47,6 +47,8 @@ struct Options {
   std::atomic<int64_t> split_min_keys{256};
   std::atomic<int64_t> num_cus{0};
   std::atomic<int64_t> plan_upload{0};
+  std::atomic<int64_t> mixed_grid{-1};
+  std::atomic<int64_t> mixed_dec_parts{1};
 } g_opt;
 
 // ------------------------------------------------------------------ timing
@@ -59,9 +61,10 @@ std::mutex g_tmu;
 std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_tpending;
 std::vector<hipEvent_t> g_tfree;
-constexpr int kTimedKernels = 5;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge, 4 rotary embedding
-double g_tms[kTimedKernels] = {0, 0, 0, 0, 0};
-int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0, 0};
+constexpr int kTimedKernels = 6;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge,
+                                   // 4 rotary embedding, 5 mixed attention grid
+double g_tms[kTimedKernels] = {0, 0, 0, 0, 0, 0};
+int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0, 0, 0};
 
 hipEvent_t take_event() {
   if (!g_tfree.empty()) {
@@ -431,6 +434,8 @@ void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t nu
   in.persistent = static_cast<int32_t>(g_opt.persistent.load());
   in.split_min_keys = static_cast<int32_t>(g_opt.split_min_keys.load());
   in.max_part_rows = kPartRowsCap;
+  in.mixed = g_opt.mixed_grid.load() != 0;
+  in.mixed_dec_parts = static_cast<int32_t>(g_opt.mixed_dec_parts.load());
 }
 
 // ---- workspace sizes.  Bounds over every call with the sizes of `d` (any
@@ -684,6 +689,11 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
   const bool new_direct = do_append && !c.fp8 && rk.dim == 0;
   const bool run_pre = plan.prefill.grid > 0;
   const bool run_dec = plan.decode.grid > 0;
+  // both kinds of items: one launch when asked to, or (default) when the two
+  // grids would otherwise run one after the other (no side stream: prepared
+  // runs, graphs, the allocation-free form); side by side otherwise
+  const int64_t mixed_mode = g_opt.mixed_grid.load();
+  const bool run_mixed = run_pre && run_dec && plan.mixed.grid > 0 && (mixed_mode == 1 || (mixed_mode < 0 && !side));
   const bool fuse_append = new_direct && (run_pre || run_dec);
   if (do_append && !fuse_append) {
     if (timed) {
@@ -732,8 +742,10 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
     p.app = ap;
     const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
     // `with_append`: this grid also runs one workgroup per new token
-    auto launch = [&](const vpk::Launch& Lc, bool dec, hipStream_t s, bool with_append) -> int32_t {
+    auto launch = [&](const vpk::Launch& Lc, int mode, hipStream_t s, bool with_append) -> int32_t {
+      const bool dec = mode == vpk::kGridDecode;
       AttnParams a = p;
+      a.num_pre_units = mode == vpk::kGridPrefill ? Lc.count : mode == vpk::kGridMixed ? plan.num_pre_units : 0;
       a.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
       a.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
       a.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
@@ -751,29 +763,32 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       const int grid = Lc.grid + (with_append ? (dims->total_knew + a.app.tokens_per_wg - 1) / a.app.tokens_per_wg : 0);
       int rc;
       if (timed) {
-        KernelTimer tm(dec ? 2 : 0, s);
-        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, dec, s);
+        KernelTimer tm(mode == vpk::kGridMixed ? 5 : dec ? 2 : 0, s);
+        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, mode, s);
       } else {
-        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, dec, s);
+        rc = vpk::launch_attention(a, grid, dims->head_dim, fmt, c.has_cache, mode, s);
       }
       if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch");
       return VPK_SUCCESS;
     };
-    if (run_pre && run_dec && side) {
+    if (run_mixed) {
+      // a9: prefill-mode tiles and decode-mode splits in one launch
+      if ((st = launch(plan.mixed, vpk::kGridMixed, stream, fuse_append))) return st;
+    } else if (run_pre && run_dec && side) {
       // both grids at once: the decode-mode grid (HBM-bound) on the side
       // stream next to the prefill-mode grid (MFMA-bound), joined at the end
       if ((st = ensure_aux(side))) return st;
       hipError_t e;
       if ((e = hipEventRecord(side->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
       if ((e = hipStreamWaitEvent(side->aux, side->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
-      if ((st = launch(plan.decode, true, side->aux, fuse_append))) return st;
+      if ((st = launch(plan.decode, vpk::kGridDecode, side->aux, fuse_append))) return st;
       if ((e = hipEventRecord(side->ev_join, side->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
-      if ((st = launch(plan.prefill, false, stream, false))) return st;
+      if ((st = launch(plan.prefill, vpk::kGridPrefill, stream, false))) return st;
       if ((e = hipStreamWaitEvent(stream, side->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
     } else {
       // the new tokens ride with the first grid launched
-      if (run_dec && (st = launch(plan.decode, true, stream, fuse_append))) return st;
-      if (run_pre && (st = launch(plan.prefill, false, stream, fuse_append && !run_dec))) return st;
+      if (run_dec && (st = launch(plan.decode, vpk::kGridDecode, stream, fuse_append))) return st;
+      if (run_pre && (st = launch(plan.prefill, vpk::kGridPrefill, stream, fuse_append && !run_dec))) return st;
     }
   }
   if (!plan.groups.empty()) {
@@ -873,7 +888,7 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
     rc.positions = true;
     const vpk::RopeArgs ra{rope->cos, rope->sin, rope->rotary_dim, rope->interleaved};
     const bool fused_q = rope->interleaved != 0 || rope->rotary_dim % 32 == 0;
-    q_dec_copy = fused_q && plan.decode.grid > 0;
+    q_dec_copy = fused_q && plan.decode.grid > 0 && !(plan.mixed.grid > 0 && g_opt.mixed_grid.load() == 1);
     rc.q = (!fused_q || q_dec_copy) && dims->total_q > 0;
     if (fused_q) rq = ra;
     if (c.has_cache && c.fp8) {
@@ -1501,6 +1516,12 @@ int32_t vpk_set_option(const char* name, int64_t value) {
   } else if (n == "plan_upload") {
     if (value < 0 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "plan_upload must be 0 or 1");
     g_opt.plan_upload = value;
+  } else if (n == "mixed_dec_parts") {
+    if (value < 1 || value > 64) return fail(VPK_ERROR_INVALID_VALUE, "mixed_dec_parts must be in [1, 64]");
+    g_opt.mixed_dec_parts = value;
+  } else if (n == "mixed_grid") {
+    if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "mixed_grid must be -1, 0 or 1");
+    g_opt.mixed_grid = value;
   } else if (n == "num_cus") {
     if (value < 0 || value > 4096) return fail(VPK_ERROR_INVALID_VALUE, "num_cus out of range");
     g_opt.num_cus = value;
@@ -1531,7 +1552,7 @@ int32_t vpk_timing_reset(void) {
 }
 
 int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..4");
+  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..5");
   std::lock_guard<std::mutex> lk(g_tmu);
   for (const TimingRec& r : g_tpending) {
     hipError_t e = hipEventSynchronize(r.b);

@@ -63,6 +63,8 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.persistent = false;
   out.prefill = Launch();
   out.decode = Launch();
+  out.mixed = Launch();
+  out.num_pre_units = 0;
   const int32_t B = in.batch;
   const int32_t g = in.hq / in.hkv;
   out.seqs.resize(B);
@@ -126,9 +128,12 @@ void build_plan(const PlanInput& in, Plan& out) {
   double part_dec = 0.0;   // decode-mode part size (cost units), 0: no split
   bool ceil_dec = false;   // split only tiles above part_dec, into ceil(cost / part_dec) parts
   if (total_dec > 0.0 && total_pre > 0.0) {
-    // both grids share the device, so the decode grid has no fixed number of
-    // slots: parts of half the average load of a decode slot
-    part_dec = total_dec / static_cast<double>(2 * cus * std::max(1, in.wg_per_cu));
+    // both kinds share the device, so the decode-mode items have no fixed
+    // number of slots: parts of 1 / mixed_dec_parts of the average decode
+    // load of a CU (on the mixed fp8 batch, 1 part per CU gave the shortest
+    // step with the grids side by side and in one launch alike: 309.5 / 321.6
+    // us against 318.7 / 334.2 at 4 and 331.3 / 359.4 at 8)
+    part_dec = total_dec / static_cast<double>(cus * std::max(1, in.mixed_dec_parts));
     ceil_dec = true;
   } else if (total_dec > 0.0) {
     const int64_t slots_dec = cus * std::max(1, in.wg_per_cu);
@@ -296,6 +301,12 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.prefill.count = n_prefill_units;
   out.decode.first = n_prefill_units;
   out.decode.count = static_cast<int32_t>(out.items.size()) - n_prefill_units;
+  out.num_pre_units = n_prefill_units;
+  const bool with_mixed = in.mixed && out.prefill.count > 0 && out.decode.count > 0;
+  if (with_mixed) {
+    out.mixed.first = 0;
+    out.mixed.count = static_cast<int32_t>(out.items.size());
+  }
 
   // ---- per launch: one workgroup per (unit, kv head), or (persistent)
   //      greedy least-loaded queues over its ordered work.  A persistent grid
@@ -310,10 +321,11 @@ void build_plan(const PlanInput& in, Plan& out) {
   static thread_local std::vector<double> heap_key;
   static thread_local std::vector<int32_t> heap_queue;
   out.persistent = false;
-  for (Launch* L : {&out.prefill, &out.decode}) {
+  for (Launch* L : {&out.prefill, &out.decode, &out.mixed}) {
+    if (L == &out.mixed && !with_mixed) continue;
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
     const int64_t lslots = static_cast<int64_t>(std::max(1, in.num_cus)) *
-                           std::max(1, L == &out.prefill ? in.pre_wg_per_cu : in.wg_per_cu);
+                           std::max(1, L == &out.decode ? in.wg_per_cu : in.pre_wg_per_cu);
     L->persistent = in.persistent == 1 || (in.persistent == -1 && nwork >= 4 * lslots);
     L->queue_first = static_cast<int32_t>(out.queue_start.size());
     L->work_first = static_cast<int32_t>(out.queue_work.size());
@@ -341,14 +353,22 @@ void build_plan(const PlanInput& in, Plan& out) {
     std::iota(ub.begin(), ub.end(), 0);
     const int32_t* const ord = order.data() + L->first;
     const Unit* const un = units.data();
-    std::stable_sort(ub.begin(), ub.end(), [&](int32_t a, int32_t b) { return un[ord[a]].cost > un[ord[b]].cost; });
+    // in the mixed grid a decode-mode unit runs on all eight waves of a
+    // workgroup that holds the whole CU: half the slot time of its cost,
+    // which counts a four-wave workgroup sharing the CU with another
+    const bool halve_dec = L == &out.mixed;
+    auto cost_of = [&](int32_t u) {
+      const double c = un[ord[u]].cost;
+      return halve_dec && L->first + u >= n_prefill_units ? 0.5 * c : c;
+    };
+    std::stable_sort(ub.begin(), ub.end(), [&](int32_t a, int32_t b) { return cost_of(a) > cost_of(b); });
     // binary min-heap of (load, queue), ties to the lower queue index
     hk.assign(nq, 0.0);
     hq.resize(nq);
     std::iota(hq.begin(), hq.end(), 0);
     auto less = [&](int32_t i, int32_t j) { return hk[i] < hk[j] || (hk[i] == hk[j] && hq[i] < hq[j]); };
     for (const int32_t u : ub) {
-      const double c = un[ord[u]].cost;
+      const double c = cost_of(u);
       for (int32_t h = 0; h < in.hkv; ++h) {
         const int64_t w = static_cast<int64_t>(u) * in.hkv + h;
         const int32_t q = hq[0];

@@ -32,6 +32,8 @@ struct PlanInput {
   // knobs
   int32_t force_splits = 0;             // 0: planner decides
   int32_t persistent = -1;              // -1 planner, 0 off, 1 on
+  bool mixed = false;                   // a batch with both kinds of items also gets the one-launch grid
+  int32_t mixed_dec_parts = 1;          // with both kinds: decode-mode parts of total / (num_cus * this)
   int32_t split_min_keys = 256;
   // largest number of split-partial rows the workspace holds (< 0: no limit);
   // splits are reduced, down to none, until the plan fits
@@ -59,6 +61,10 @@ struct Plan {
   int64_t part_rows = 0;                // rows of split partials
   bool persistent = false;
   Launch prefill, decode;
+  // with PlanInput::mixed and both kinds of items: every unit in one grid of
+  // 512-thread workgroups (prefill-mode units first, then decode-mode ones)
+  Launch mixed;
+  int32_t num_pre_units = 0;            // prefill-mode units (they come first in items)
 };
 
 constexpr int32_t kMaxSplits = 64;

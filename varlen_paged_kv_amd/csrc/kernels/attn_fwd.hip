@@ -526,7 +526,8 @@ struct Src {
   struct QEntry {
     WorkItem item;       // with its sequence's facts in item.s
     int32_t kvh;
-    int32_t pad[3];
+    int32_t dec;         // decode-mode item (unit at or past p.num_pre_units)
+    int32_t pad[2];
   };
   static constexpr int kQueueChunk = 48;
 
@@ -543,6 +544,7 @@ struct Src {
       if (item.part >= 0) item.part += kvh * item.part_stride;
       q[i].item = item;
       q[i].kvh = kvh;
+      q[i].dec = unit >= p.num_pre_units ? 1 : 0;
     }
   }
 
@@ -586,7 +588,8 @@ struct Src {
 
   // The workgroup's items: [blockIdx, blockIdx + 1) of the grid, or its queue
   // when persistent; `body(entry, item)` runs each, all threads together.
-  template <typename Body>
+  // FILTER 0 / 1: only the prefill-mode / decode-mode entries (-1: all).
+  template <int FILTER = -1, typename Body>
   __device__ static __forceinline__ void for_each_item(const AttnParams& p, QEntry* qbuf, int32_t* pids, int t,
                                                        int nt, Body&& body) {
     int w0 = blockIdx.x, w_end = blockIdx.x + 1;
@@ -600,6 +603,9 @@ struct Src {
       __syncthreads();
       for (int k = 0; k < n; ++k) {
         const QEntry& e = qbuf[k];
+        if constexpr (FILTER >= 0) {
+          if (__builtin_amdgcn_readfirstlane(e.dec) != FILTER) continue;
+        }
         Item it;
         setup_item(p, e, pids, t, nt, it);
         body(e, it);
@@ -989,18 +995,22 @@ __device__ __forceinline__ void scales(const AttnParams& p, float& qk, float& vs
   }
 }
 
-template <int D, int FMT, bool PAGED, bool ROPE>
+// NWV: waves of the workgroup (4 in the decode-mode grid; 8 when a decode-mode
+// item runs in the 512-thread workgroup of the mixed grid)
+template <int D, int FMT, bool PAGED, bool ROPE, int NWV = kWaves>
 struct Decode : Src<D, FMT, PAGED> {
   using B = Src<D, FMT, PAGED>;
   using C = Cfg<D>;
   using Item = typename B::Item;
-  static constexpr int NT = kThreads;               // 4 waves
+  static constexpr int kWaves = NWV;
+  static constexpr int NT = kWaves * 64;
   static constexpr int DK = 32;                     // keys per wave block
   static constexpr int F8PASS = (DK * B::F8CH + 63) / 64;   // per lane, one wave moving 32 rows
   // the combine area is [4][32][D] fp32 outputs plus [4][32] maxima and
   // [4][32] sums: the two stages hold the outputs, this tail the rest
+  static constexpr int kStages = kWaves / 2;        // each wave uses half a stage
   static constexpr int kCombineExtra = 2 * kWaves * kWaveRows * 2;   // bf16 elements
-  static_assert(kWaves * kWaveRows * D * 4 <= 2 * C::STAGE * 2, "combine area fits the stages");
+  static_assert(kWaves * kWaveRows * D * 4 <= kStages * C::STAGE * 2, "combine area fits the stages");
 
   // Items with at most 32 packed rows (decode steps: q_len * g rows) would
   // leave three of four waves without rows, so the waves split the keys
@@ -1107,9 +1117,9 @@ struct Decode : Src<D, FMT, PAGED> {
 
     // ---- combine the four waves' states through LDS
     __syncthreads();                     // every wave is done with its stage
-    float* const so = reinterpret_cast<float*>(smem);              // [4][32][D]
-    float* const sm = so + kWaves * kWaveRows * D;                 // [4][32]
-    float* const sl = sm + kWaves * kWaveRows;                     // [4][32]
+    float* const so = reinterpret_cast<float*>(smem);              // [waves][32][D]
+    float* const sm = so + kWaves * kWaveRows * D;                 // [waves][32]
+    float* const sl = sm + kWaves * kWaveRows;                     // [waves][32]
     const float l_tot = wave_pair_sum(l_run);
     if (row_ok) {
 #pragma unroll
@@ -1165,7 +1175,7 @@ struct Decode : Src<D, FMT, PAGED> {
   __device__ static __forceinline__ void run(const AttnParams& p) {
     // two K/V stages used as four per-wave half stages, then as the area
     // where the waves combine their partial softmax states
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * C::STAGE + kCombineExtra];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[kStages * C::STAGE + kCombineExtra];
     __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -1532,6 +1542,56 @@ struct Prefill : Src<D, FMT, PAGED> {
   }
 };
 
+// ---------------------------------------------------------------- mixed grid
+// One launch for a batch that mixes prefill-mode tiles and decode-mode
+// splits: 512-thread workgroups (one per CU) whose items are either kind.  A
+// prefill-mode item runs as in the prefill-mode grid; a decode-mode item runs
+// on all eight waves, which split its keys.  The items are listed prefill-mode
+// first (the longest work starts first), then decode-mode, so the decode
+// splits fill the compute units the prefill tiles leave idle.  (The FlashInfer
+// PoD-Attention page, "[Refactor] Uniform PoDAttention API with Horizontal
+// Fusion SMs Schedule", Key Changes: prefill and decode requests share one
+// persistent launch.)
+template <int D, int FMT, bool PAGED, bool ROPE>
+struct Mixed {
+  using Pf = Prefill<D, FMT, PAGED, ROPE>;
+  using Dc = Decode<D, FMT, PAGED, ROPE, kPrefillWaves>;
+  using B = Src<D, FMT, PAGED>;
+  using C = Cfg<D>;
+  using Item = typename B::Item;
+  static constexpr int NT = kPrefillWaves * 64;
+  static constexpr int SMEM = Pf::NS * C::STAGE > Dc::kStages * C::STAGE + Dc::kCombineExtra
+                                  ? Pf::NS * C::STAGE
+                                  : Dc::kStages * C::STAGE + Dc::kCombineExtra;
+
+  __device__ static __forceinline__ void run(const AttnParams& p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
+    __shared__ int32_t pids[PAGED ? kMaxItemPages : 1];
+    __shared__ int lims[NT];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int lr = lane & 31;
+    const int lg = lane >> 5;
+    if (static_cast<int>(blockIdx.x) >= p.attn_blocks) {
+      append_tokens(p.app, blockIdx.x - p.attn_blocks, t, NT, reinterpret_cast<int64_t*>(smem));
+      return;
+    }
+    float qk, vs;
+    scales(p, qk, vs);
+    __shared__ typename B::QEntry qbuf[B::kQueueChunk];
+    // two passes over the workgroup's entries, prefill-mode items first (each
+    // queue lists them first anyway): with both item bodies inside one loop
+    // the register allocator spilled 54-127 VGPRs; each pass alone spills none
+    B::template for_each_item<0>(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      Pf::item(p, e.item, e.item.s, it, smem, lims, qk, vs, wave, lr, lg, t);
+    });
+    B::template for_each_item<1>(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      Dc::item(p, e.item, e.item.s, it, smem, qk, vs, wave, lr, lg, t);
+    });
+  }
+};
+
 // ROPE: the query rows are turned by rotary embedding as they are loaded
 // (separate instantiations, so that the other kernels' register allocation
 // does not carry the rotation code)
@@ -1546,33 +1606,40 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_prefill_kernel(con
 }
 
 template <int D, int FMT, bool PAGED, bool ROPE>
-int launch_t(const AttnParams& p, int grid, bool decode, hipStream_t s) {
-  if (decode)
+__global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_mixed_kernel(const AttnParams p) {
+  Mixed<D, FMT, PAGED, ROPE>::run(p);
+}
+
+template <int D, int FMT, bool PAGED, bool ROPE>
+int launch_t(const AttnParams& p, int grid, int mode, hipStream_t s) {
+  if (mode == kGridDecode)
     hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kThreads), 0, s, p);
+  else if (mode == kGridMixed)
+    hipLaunchKernelGGL((attn_mixed_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
   else
     hipLaunchKernelGGL((attn_prefill_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
   return static_cast<int>(hipGetLastError());
 }
 
 template <int D, bool ROPE>
-int launch_d(const AttnParams& p, int grid, int kv_format, bool paged, bool decode, hipStream_t s) {
-  if (!paged) return launch_t<D, kKvBf16, false, ROPE>(p, grid, decode, s);
-  if (kv_format == kKvFp8) return launch_t<D, kKvFp8, true, ROPE>(p, grid, decode, s);
-  return launch_t<D, kKvBf16, true, ROPE>(p, grid, decode, s);
+int launch_d(const AttnParams& p, int grid, int kv_format, bool paged, int mode, hipStream_t s) {
+  if (!paged) return launch_t<D, kKvBf16, false, ROPE>(p, grid, mode, s);
+  if (kv_format == kKvFp8) return launch_t<D, kKvFp8, true, ROPE>(p, grid, mode, s);
+  return launch_t<D, kKvBf16, true, ROPE>(p, grid, mode, s);
 }
 
 }  // namespace
 
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
-                     bool decode, void* stream) {
+                     int mode, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool rope = p.rope.dim > 0;
   if (head_dim == 128)
-    return rope ? launch_d<128, true>(p, grid, kv_format, paged, decode, s)
-                : launch_d<128, false>(p, grid, kv_format, paged, decode, s);
+    return rope ? launch_d<128, true>(p, grid, kv_format, paged, mode, s)
+                : launch_d<128, false>(p, grid, kv_format, paged, mode, s);
   if (head_dim == 64)
-    return rope ? launch_d<64, true>(p, grid, kv_format, paged, decode, s)
-                : launch_d<64, false>(p, grid, kv_format, paged, decode, s);
+    return rope ? launch_d<64, true>(p, grid, kv_format, paged, mode, s)
+                : launch_d<64, false>(p, grid, kv_format, paged, mode, s);
   return static_cast<int>(hipErrorInvalidValue);
 }
 

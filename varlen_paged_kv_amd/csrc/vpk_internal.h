@@ -119,6 +119,7 @@ struct AttnParams {
   int32_t* err_flag;
   const void* zeros;          // >= 256 zero bytes: source of rows past the keys
   int32_t num_items;
+  int32_t num_pre_units;      // units of this launch below this index run in prefill mode
   int32_t persistent;
   int32_t new_direct;         // keys >= cache_len come from k_new / v_new (bf16 cache)
   int32_t attn_blocks;        // workgroups past this index run the append instead
@@ -179,9 +180,13 @@ struct RopeParams {
 constexpr size_t kScratchBytes = size_t(64) << 20;
 int scratch_address(void** ptr);
 
+// Attention grids: prefill-mode items, decode-mode items, or both kinds in one
+// launch (units below AttnParams::num_pre_units run in prefill mode).
+enum GridMode : int { kGridPrefill = 0, kGridDecode = 1, kGridMixed = 2 };
+
 // Kernel launchers (defined in the .hip files); they return hipError_t as int.
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
-                     bool decode, void* stream);
+                     int mode, void* stream);
 int launch_append(const AppendParams& p, void* stream);
 int launch_merge(const MergeParams& p, void* stream);
 int launch_rope(const RopeParams& p, int head_dim, void* stream);
