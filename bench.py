@@ -373,6 +373,9 @@ def measure_workload(name, args, dev, cpu_budget):
         roof["combined_frac"] = (pre_flops / (PEAK_BF16_TFLOPS * 1e12) + dec_bytes / (PEAK_HBM_GBS * 1e9)) / elapsed
         obj["roofline"] = roof
         del r
+        if args.no_parts:
+            obj["cpu_baseline"] = cpu_baseline(wl, cpu_budget) if cpu_budget > 0 else None
+            return obj
         parts = {}
         for label, seqs in (("prefill_rows", np.nonzero(~dec)[0]), ("decode_rows", np.nonzero(dec)[0])):
             sub = subset(wl, seqs)
@@ -411,6 +414,7 @@ def main():
                     help="measure this workload alone (default: the four full-size workloads)")
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through (defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parts", action="store_true", help="mixed batch: do not time its parts alone")
     ap.add_argument("--cpu-budget", type=float, default=6.0, help="seconds of oracle time per workload")
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps after the warm-up, before the passes (clock ramp)")
