@@ -1009,8 +1009,16 @@ struct Decode : Src<D, FMT, PAGED> {
   // the combine area is [4][32][D] fp32 outputs plus [4][32] maxima and
   // [4][32] sums: the two stages hold the outputs, this tail the rest
   static constexpr int kStages = kWaves / 2;        // each wave uses half a stage
-  static constexpr int kCombineExtra = 2 * kWaves * kWaveRows * 2;   // bf16 elements
-  static_assert(kWaves * kWaveRows * D * 4 <= kStages * C::STAGE * 2, "combine area fits the stages");
+  // Row stride (fp32) of the combine area: padded by 16 bytes, so that a
+  // wave's 32 rows written at one head-dim offset fall into different banks
+  // (with a stride of D floats they all hit the same ones)
+  static constexpr int kCombStride = D + 4;
+  // the combine area, [waves][32][kCombStride] fp32 outputs plus [waves][32]
+  // maxima and sums, over the stages and past them: its size past the stages
+  // (bf16 elements)
+  static constexpr int kCombineExtra =
+      (kWaves * kWaveRows * (kCombStride + 2) * 4 - kStages * C::STAGE * 2) / 2;
+  static_assert(kCombineExtra > 0, "combine area extends past the stages");
 
   // Items with at most 32 packed rows (decode steps: q_len * g rows) would
   // leave three of four waves without rows, so the waves split the keys
@@ -1118,7 +1126,7 @@ struct Decode : Src<D, FMT, PAGED> {
     // ---- combine the four waves' states through LDS
     __syncthreads();                     // every wave is done with its stage
     float* const so = reinterpret_cast<float*>(smem);              // [waves][32][D]
-    float* const sm = so + kWaves * kWaveRows * D;                 // [waves][32]
+    float* const sm = so + kWaves * kWaveRows * kCombStride;       // [waves][32]
     float* const sl = sm + kWaves * kWaveRows;                     // [waves][32]
     const float l_tot = wave_pair_sum(l_run);
     if (row_ok) {
@@ -1127,7 +1135,7 @@ struct Decode : Src<D, FMT, PAGED> {
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int d0 = d * 32 + i4 * 8 + lg * 4;
-          *reinterpret_cast<float4*>(so + (wave * kWaveRows + lr) * D + d0) =
+          *reinterpret_cast<float4*>(so + (wave * kWaveRows + lr) * kCombStride + d0) =
               make_float4(o[d][i4 * 4 + 0], o[d][i4 * 4 + 1], o[d][i4 * 4 + 2], o[d][i4 * 4 + 3]);
         }
       if (lg == 0) {
@@ -1153,7 +1161,7 @@ struct Decode : Src<D, FMT, PAGED> {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
           const float wt = __builtin_amdgcn_exp2f((mw[w] - mmax) * c);
-          const float4 f = *reinterpret_cast<const float4*>(so + (w * kWaveRows + r) * D + d0);
+          const float4 f = *reinterpret_cast<const float4*>(so + (w * kWaveRows + r) * kCombStride + d0);
           lsum += wt * sl[w * kWaveRows + r];
           acc4.x += wt * f.x;
           acc4.y += wt * f.y;
