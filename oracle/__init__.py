@@ -17,7 +17,10 @@ It computes, plainly and slowly, in float64 (numpy):
     range -- ``merge_partials``;
   * rotary position embedding of the query rows and the new key rows before
     the append (optional) -- ``rope.positions`` / ``rope.rotate_bf16`` and
-    ``run_call(rope=...)``.
+    ``run_call(rope=...)``;
+  * fp8 "QKV-Prob" attention: fp8 query codes, and the softmax quantised to
+    fp8 before the second product -- ``prob8.attend`` and
+    ``run_call(prob8=...)``.
 
 Pages this follows (cited by title and section):
   * "Add flash_attn_varlen_func_with_kvcache" (flash-attention PR), sections
@@ -38,9 +41,9 @@ Every function is pinned in tests/test_oracle_*.py against facts fixed by the
 mathematics or by library routines (see each function's docstring).
 """
 from .formats import (  # noqa: F401
-    bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode, e4m3fn_value_table,
+    bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode, e4m3fn_encode_f64, e4m3fn_value_table,
 )
-from . import rope  # noqa: F401
+from . import prob8, rope  # noqa: F401
 from .attention import (  # noqa: F401
     append, attend, attend_rows, depage, merge_partials, run_call, run_workload, sequence_kv,
 )

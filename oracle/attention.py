@@ -40,6 +40,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
+from . import prob8 as _prob8
 from . import rope as _rope
 from .formats import bf16_bits_to_f64, e4m3fn_decode, e4m3fn_encode
 
@@ -205,7 +206,7 @@ def merge_partials(parts):
 def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k_cache=None,
              v_cache=None, block_table=None, cache_seqlens=None, page_size=0, causal=True,
              scale=None, kv_scale=None, cache_dtype=None, Hkv=None, q_dtype="bf16",
-             new_dtype="bf16", seqs: Optional[Sequence[int]] = None, rope=None):
+             new_dtype="bf16", seqs: Optional[Sequence[int]] = None, rope=None, prob8=None):
     """One whole call: append, then attention for every sequence.
 
     Returns dict(out [Tq, Hq, D], lse [Hq, Tq], k_cache, v_cache) with float64
@@ -213,7 +214,10 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
     attention to some sequences (rows of the others stay 0 / -inf).  ``rope``
     (dict with cos, sin, rotary_dim, interleaved) first turns the query rows
     and the new key rows by their positions (``oracle.rope``); values and the
-    cached rows are not turned.
+    cached rows are not turned.  ``prob8`` (dict with q_scale, p_scale and
+    optionally band; fp8 cache only) runs the attention as fp8 "QKV-Prob"
+    (``oracle.prob8``): the query codes are taken after the rotation, and the
+    result also holds q_codes [Tq, Hq, D] and, with a band, bound [Tq, Hq, D].
     """
     if rope is not None:
         if q_dtype != "bf16" or new_dtype != "bf16":
@@ -225,6 +229,13 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
             k_new = _rope.rotate_bf16(k_new, kpos, *args)
     Q = _decode(q, q_dtype)
     Tq, Hq, D = Q.shape
+    band = None
+    if prob8 is not None:
+        if q_dtype != "bf16" or cache_dtype != "fp8" or k_cache is None:
+            raise ValueError("QKV-Prob attention is defined here for bf16 queries over an fp8 cache")
+        q_codes = _encode(q, "bf16", "fp8", prob8["q_scale"])
+        band = prob8.get("band")
+        bound = np.zeros((Tq, Hq, D), np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if k_cache is not None and k_new is not None:
@@ -241,11 +252,23 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
                            k_cache=kc, v_cache=vc, block_table=block_table,
                            cache_seqlens=cache_seqlens, page_size=page_size,
                            cache_dtype=cache_dtype, kv_scale=kv_scale, new_dtype=new_dtype)
-        if e > s:
+        if e > s and prob8 is not None:
+            r = _prob8.attend(q_codes[s:e], prob8["q_scale"], K, V, causal, scale, prob8["p_scale"],
+                              band=band)
+            out[s:e] = r[0]
+            lse[:, s:e] = r[1]
+            if band is not None:
+                bound[s:e] = r[2]
+        elif e > s:
             o, l = attend(Q[s:e], K, V, causal, scale)
             out[s:e] = o
             lse[:, s:e] = l
-    return dict(out=out, lse=lse, k_cache=kc, v_cache=vc)
+    res = dict(out=out, lse=lse, k_cache=kc, v_cache=vc)
+    if prob8 is not None:
+        res["q_codes"] = q_codes
+        if band is not None:
+            res["bound"] = bound
+    return res
 
 
 def run_workload(wl, seqs=None):

@@ -70,7 +70,13 @@ def e4m3fn_encode(x32: np.ndarray) -> np.ndarray:
     mantissa LSB is 0); magnitudes at or beyond 448 (including infinity) become
     448.
     """
-    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    return e4m3fn_encode_f64(np.asarray(x32, dtype=np.float32).astype(np.float64))
+
+
+def e4m3fn_encode_f64(x64: np.ndarray) -> np.ndarray:
+    """float64 values -> e4m3fn codes by the same rule, deciding on the float64
+    value itself (no float32 rounding first)."""
+    x = np.asarray(x64, dtype=np.float64)
     neg = np.signbit(x)
     a = np.abs(x)
     nan = np.isnan(a)
