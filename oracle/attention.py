@@ -215,9 +215,10 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
     (dict with cos, sin, rotary_dim, interleaved) first turns the query rows
     and the new key rows by their positions (``oracle.rope``); values and the
     cached rows are not turned.  ``prob8`` (dict with q_scale, p_scale and
-    optionally band; fp8 cache only) runs the attention as fp8 "QKV-Prob"
-    (``oracle.prob8``): the query codes are taken after the rotation, and the
-    result also holds q_codes [Tq, Hq, D] and, with a band, bound [Tq, Hq, D].
+    optionally band and score_err; fp8 cache only) runs the attention as fp8
+    "QKV-Prob" (``oracle.prob8``): the query codes are taken after the
+    rotation, and the result also holds q_codes [Tq, Hq, D] and, with a band,
+    bound and absum [Tq, Hq, D] and tmax [Hq, Tq].
     """
     if rope is not None:
         if q_dtype != "bf16" or new_dtype != "bf16":
@@ -236,6 +237,8 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
         q_codes = _encode(q, "bf16", "fp8", prob8["q_scale"])
         band = prob8.get("band")
         bound = np.zeros((Tq, Hq, D), np.float64)
+        absum = np.zeros((Tq, Hq, D), np.float64)
+        tmax = np.zeros((Hq, Tq), np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if k_cache is not None and k_new is not None:
@@ -254,11 +257,13 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
                            cache_dtype=cache_dtype, kv_scale=kv_scale, new_dtype=new_dtype)
         if e > s and prob8 is not None:
             r = _prob8.attend(q_codes[s:e], prob8["q_scale"], K, V, causal, scale, prob8["p_scale"],
-                              band=band)
+                              band=band, score_err=prob8.get("score_err", 0.0))
             out[s:e] = r[0]
             lse[:, s:e] = r[1]
             if band is not None:
                 bound[s:e] = r[2]
+                absum[s:e] = r[3]["absum"]
+                tmax[:, s:e] = r[3]["tmax"]
         elif e > s:
             o, l = attend(Q[s:e], K, V, causal, scale)
             out[s:e] = o
@@ -267,7 +272,7 @@ def run_call(*, q, cu_seqlens_q, k_new=None, v_new=None, cu_seqlens_knew=None, k
     if prob8 is not None:
         res["q_codes"] = q_codes
         if band is not None:
-            res["bound"] = bound
+            res.update(bound=bound, absum=absum, tmax=tmax)
     return res
 
 

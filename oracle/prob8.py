@@ -31,7 +31,14 @@ Where a kernel computes P in float32, the value P / p_scale can land on the
 other side of a rounding boundary than the float64 value does.  ``attend``
 therefore also reports, for a relative band around every boundary, the
 largest change of out that such flips can cause (``bound``): an element
-whose value lies within the band may take either neighbouring code.
+whose value lies within the band may take either neighbouring code.  The
+band of element (i, j) is ``band + score_err * (T_ij + max_j' T_ij')`` with
+T_ij = scale * sum_d |q_id k_jd|: a product unit whose sums carry an error
+of up to score_err * sum |terms| moves S_ij by at most score_err * T_ij and
+the LSE by at most score_err * max_j T_ij, and P by the exponential of
+their difference.  For the same reason ``attend`` reports T's row maximum
+(``tmax``, to bound the LSE) and p_scale * sum_j |pcode_ij| |v_jd|
+(``absum``, to bound the error of the second product's sums).
 
 Pinned by tests/test_oracle_prob8.py: the float64 encoder against brute force
 over the code table; rows whose probabilities are exact e4m3 values (one
@@ -52,10 +59,11 @@ from .formats import _POS, e4m3fn_decode, e4m3fn_encode_f64
 DEFAULT_BAND = 2.0 ** -12
 
 
-def flip_bound(y: np.ndarray, band: float):
-    """For values y >= 0 (P / p_scale): which lie within a relative ``band`` of
-    a rounding boundary between two neighbouring e4m3fn values, and the gap
-    between those two values (0 where no flip is possible)."""
+def flip_bound(y: np.ndarray, band):
+    """For values y >= 0 (P / p_scale): which lie within a relative ``band``
+    (a number, or an array shaped like y) of a rounding boundary between two
+    neighbouring e4m3fn values, and the gap between those two values (0 where
+    no flip is possible)."""
     y = np.asarray(y, np.float64)
     hi = np.searchsorted(_POS, y, side="left")
     hi_c = np.clip(hi, 1, 0x7E)
@@ -68,14 +76,16 @@ def flip_bound(y: np.ndarray, band: float):
 
 def attend(Qc: np.ndarray, q_scale: float, K: np.ndarray, V: np.ndarray, causal: bool, scale: float,
            p_scale: float, rows: Optional[Sequence[int]] = None, band: Optional[float] = None,
-           return_codes: bool = False):
+           return_codes: bool = False, score_err: float = 0.0):
     """QKV-Prob attention of one sequence.
 
     Qc [Lq, Hq, D] uint8 query codes; K, V [Lk, Hkv, D] float64, dequantised
     (scales applied).  ``rows`` selects query indices.  Returns out
     [R, Hq, D] and lse [Hq, R]; with ``band`` also bound [R, Hq, D], the
-    largest change of out that flips of codes within the band can cause; with
-    ``return_codes`` also pcodes [Hq, R, Lk] (uint8; 0 for masked keys).
+    largest change of out that flips of codes within the band (widened by
+    ``score_err`` as the module text says) can cause, and a dict with tmax
+    [Hq, R] and absum [R, Hq, D]; with ``return_codes`` also pcodes
+    [Hq, R, Lk] (uint8; 0 for masked keys).
     """
     Q = e4m3fn_decode(Qc) * np.float64(np.float32(q_scale))
     Lq, Hq, D = Q.shape
@@ -89,6 +99,8 @@ def attend(Qc: np.ndarray, q_scale: float, K: np.ndarray, V: np.ndarray, causal:
     out = np.zeros((R, Hq, D), np.float64)
     lse = np.full((Hq, R), -np.inf, np.float64)
     bound = np.zeros((R, Hq, D), np.float64) if band is not None else None
+    tmax = np.zeros((Hq, R), np.float64) if band is not None else None
+    absum = np.zeros((R, Hq, D), np.float64) if band is not None else None
     codes_all = np.zeros((Hq, R, Lk), np.uint8) if return_codes else None
     j = np.arange(Lk)
     visible = np.ones((R, Lk), bool)
@@ -110,13 +122,19 @@ def attend(Qc: np.ndarray, q_scale: float, K: np.ndarray, V: np.ndarray, causal:
         out[live, h, :] = w @ V[:, kvh, :]                              # step 6
         lse[h, live] = L
         if band is not None:
-            _, gap = flip_bound(y, band)
+            T = scale * (np.abs(Q[rows[live], h, :]) @ np.abs(K[:, kvh, :]).T)
+            T = np.where(visible[live], T, 0.0)
+            tm = T.max(axis=1)
+            _, gap = flip_bound(y, band + score_err * (T + tm[:, None]))
             bound[live, h, :] = (gap * ps) @ np.abs(V[:, kvh, :])
+            tmax[h, live] = tm
+            absum[live, h, :] = np.abs(w) @ np.abs(V[:, kvh, :])
         if return_codes:
             codes_all[h, live] = pc
     res = [out, lse]
     if band is not None:
         res.append(bound)
+        res.append(dict(tmax=tmax, absum=absum))
     if return_codes:
         res.append(codes_all)
     return tuple(res)

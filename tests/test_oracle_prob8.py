@@ -105,7 +105,8 @@ def test_against_plain_attention(causal, p_scale):
     Lq, Lk, Hq, Hkv, D, q_scale, scale = 24, 40, 4, 2, 32, 0.015, 0.4
     Qc, K, V = _case(3, Lq, Lk, Hq, Hkv, D, q_scale, causal)
     band = 2.0 ** -12
-    out, lse, bound, pc = P8.attend(Qc, q_scale, K, V, causal, scale, p_scale, band=band, return_codes=True)
+    out, lse, bound, aux, pc = P8.attend(Qc, q_scale, K, V, causal, scale, p_scale, band=band,
+                                         return_codes=True)
     Qd = e4m3fn_decode(Qc) * np.float64(np.float32(q_scale))
     ref_out, ref_lse, probs = oracle.attend(Qd, K, V, causal, scale, return_probs=True)
     np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
@@ -124,8 +125,30 @@ def test_against_plain_attention(causal, p_scale):
         assert (np.abs(out[:, h, :] - ref_out[:, h, :]) <= lim + 1e-15).all()
     # P was quantised: the output is not the plain attention
     assert np.abs(out - ref_out).max() > 1e-6
-    # the bound covers flips of the codes inside the band
+    # the bound covers flips of the codes inside the band: each flip moves one
+    # weight by one step of e4m3 at that value
     assert (bound >= 0).all()
+    # the two neighbours of a value near a midpoint: c (below it) and c + 1
+    c = np.where(e4m3fn_decode(want) <= y, want.astype(int), want.astype(int) - 1).clip(0, 0x7D)
+    step = (e4m3fn_decode((c + 1).astype(np.uint8)) - e4m3fn_decode(c.astype(np.uint8))) * ps
+    for h in range(Hq):
+        fl = np.where(near[h], step[h], 0.0) @ np.abs(V[:, h // g, :])
+        np.testing.assert_allclose(bound[:, h, :], fl, rtol=1e-12, atol=1e-300)
+    # absum is sum_j |w_j| |v_j|, with w the dequantised weights
+    for h in range(Hq):
+        wv = (e4m3fn_decode(pc[h]) * ps) @ np.abs(V[:, h // g, :])
+        np.testing.assert_allclose(aux["absum"][:, h, :], wv, rtol=1e-12)
+
+
+def test_score_error_widens_the_band():
+    Lq, Lk, Hq, Hkv, D, q_scale, scale = 16, 32, 2, 1, 32, 0.015, 0.4
+    Qc, K, V = _case(4, Lq, Lk, Hq, Hkv, D, q_scale, False)
+    b0 = P8.attend(Qc, q_scale, K, V, False, scale, 1 / 448, band=2.0 ** -12)[2]
+    b1, aux = P8.attend(Qc, q_scale, K, V, False, scale, 1 / 448, band=2.0 ** -12, score_err=2.0 ** -10)[2:4]
+    assert (b1 >= b0).all() and b1.sum() > b0.sum()
+    Qd = e4m3fn_decode(Qc) * np.float64(np.float32(q_scale))
+    T = scale * np.einsum("qd,kd->qk", np.abs(Qd[:, 0]), np.abs(K[:, 0]))
+    np.testing.assert_allclose(aux["tmax"][0], T.max(axis=1), rtol=1e-12)
 
 
 def test_bound_counts_only_codes_near_a_boundary():
