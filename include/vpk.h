@@ -260,6 +260,52 @@ int32_t attn_varlen_paged_rope_fwd(const vpk_dims* dims,
                                    const vpk_host_index* host, void* stream);
 
 /*
+ * attn_varlen_paged_qkv_prob_fwd -- attn_varlen_paged_fwd (or, with `rope`,
+ * attn_varlen_paged_rope_fwd) with the attention in fp8 "QKV-Prob" form: the
+ * query rows, the keys and values and the softmax output are all fp8 e4m3fn,
+ * and both products run on fp8 matrix cores.  The vLLM Triton FAv2 PR page
+ * ("[Kernel][Triton][FP8] Adding fp8 and variable length sequence support to
+ * Triton FAv2 kernel", feature list item 7 and the paragraph before its
+ * LM EVAL tables) names such models: softmax(QK^T) is quantised to fp8
+ * before the second product.  The page fixes no scales or rounding; here:
+ *   query codes  qc = e4m3fn(fp32(q) * fp32(1 / q_scale)), the cache's rule
+ *                (after rotary embedding when `rope` is given);
+ *   scores       s_ij = scale * q_scale * k_scale * sum_d qc_id kc_jd, masked
+ *                as in attn_varlen_paged_fwd;
+ *   softmax      P_ij = exp(s_ij - lse_i), lse_i = ln sum_j exp(s_ij): the
+ *                row's exact softmax over all its visible keys;
+ *   P codes      pc_ij = e4m3fn(P_ij / p_scale), nearest, ties to even;
+ *   output       out_i = p_scale * v_scale * sum_j pc_ij vc_j (bf16, round to
+ *                nearest even), not renormalised; lse as above.
+ * The kernel reads each row's keys twice (once for the row maximum and sum,
+ * once for P and the second product) and never splits a key range.
+ *   kv_scale  host float[2] {k_scale, v_scale}, required (fp8 cache only).
+ *   qp_scale  host float[2] {q_scale, p_scale}: q_scale finite and > 0;
+ *             p_scale finite and >= 1/452 (P <= 1, so P / p_scale stays
+ *             within the range the conversion rounds without saturating;
+ *             1/448 maps P = 1 to the largest finite code).
+ *   rope      vpk_rope as for attn_varlen_paged_rope_fwd, or NULL.
+ * fp8 matrix-core sums are not exact float32 sums: on gfx950 they deviate by
+ * up to about 2^-13 of the sum of the magnitudes of their terms, so a P code
+ * whose value lies that close to a rounding boundary may take either
+ * neighbour.
+ * Extra errors: VPK_ERROR_INVALID_VALUE for a bf16 cache, no cache, or
+ * scales that break the rules above; VPK_ERROR_NOT_SUPPORTED when a
+ * sequence's keys span more than 1023 pages.  Otherwise as
+ * attn_varlen_paged_fwd.
+ */
+int32_t attn_varlen_paged_qkv_prob_fwd(const vpk_dims* dims,
+                                       const void* q, const int32_t* cu_seqlens_q,
+                                       const void* k_new, const void* v_new,
+                                       const int32_t* cu_seqlens_knew,
+                                       void* k_cache, void* v_cache,
+                                       const int32_t* block_table, const int32_t* cache_seqlens,
+                                       int32_t page_size, int32_t causal, float scale,
+                                       const float* kv_scale, const float* qp_scale, const vpk_rope* rope,
+                                       void* out, float* lse,
+                                       const vpk_host_index* host, void* stream);
+
+/*
  * The page-list form of the same call.  The POD page's batch API describes
  * sequences by a page list in CSR form (an offsets array into one array of
  * page ids) and lets the query rows of a sequence sit anywhere in q/out (its
@@ -460,7 +506,8 @@ int32_t vpk_set_option(const char* name, int64_t value);
  *           3 = LSE merge of split parts,
  *           4 = rotary embedding of the rows turned into copies before attention,
  *           5 = mixed attention grid (prefill-mode and decode-mode items of one
- *               call in one launch, option "mixed_grid").
+ *               call in one launch, option "mixed_grid"),
+ *           6 = fp8 QKV-Prob attention grid (attn_varlen_paged_qkv_prob_fwd).
  */
 int32_t vpk_timing_enable(int32_t enable);
 int32_t vpk_timing_reset(void);

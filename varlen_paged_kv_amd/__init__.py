@@ -25,14 +25,16 @@ from ._lib import VpkDims, VpkHostIndex, VpkHostPages
 __all__ = ["attn_varlen_paged_fwd_noalloc", "set_workspace", "workspace_bytes_upper_bound", "library_memory", "attn_varlen_paged_fwd", "attn_varlen_paged_list_fwd", "kv_cache_append", "VpkError", "set_option", "abi_version",
            "timing_enable", "timing_reset", "timing_read", "device_error", "plan_debug", "Plan",
            "KERNEL_ATTENTION", "KERNEL_APPEND", "KERNEL_ATTENTION_DECODE", "KERNEL_MERGE", "KERNEL_ROPE",
-           "KERNEL_ATTENTION_MIXED",
-           "attn_varlen_paged_rope_fwd"]
+           "KERNEL_ATTENTION_MIXED", "KERNEL_ATTENTION_PROB8",
+           "attn_varlen_paged_rope_fwd", "attn_varlen_paged_qkv_prob_fwd"]
 
 # kernel ids of the timing API: the prefill-mode attention grid, the standalone
 # append, the decode-mode attention grid, the split merge, the rotary copies,
-# the mixed attention grid (both kinds of items in one launch)
+# the mixed attention grid (both kinds of items in one launch), the fp8
+# QKV-Prob attention grid
 KERNEL_ATTENTION, KERNEL_APPEND, KERNEL_ATTENTION_DECODE, KERNEL_MERGE, KERNEL_ROPE, KERNEL_ATTENTION_MIXED = \
     0, 1, 2, 3, 4, 5
+KERNEL_ATTENTION_PROB8 = 6
 
 
 class VpkError(RuntimeError):
@@ -238,8 +240,17 @@ def attn_varlen_paged_rope_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     rotary_dim defaults to twice their width.  q and k_new are not modified;
     the cache stores the turned keys.
     """
+    return _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                       cache_seqlens, page_size, causal, scale, kv_scale, out, lse, return_lse, host_index,
+                       stream, _rope_args(rope_cos, rope_sin, rotary_dim, interleaved))
+
+
+def _rope_args(rope_cos, rope_sin, rotary_dim, interleaved):
+    """(VpkRope, cos, sin): the C struct and the tensors it points into."""
     rope_cos = _dev(rope_cos, "rope_cos", (torch.float32,))
     rope_sin = _dev(rope_sin, "rope_sin", (torch.float32,))
+    if rope_cos is None or rope_sin is None:
+        raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "rope_cos and rope_sin must both be given")
     if rope_cos.dim() != 2 or tuple(rope_sin.shape) != tuple(rope_cos.shape):
         raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "rope_cos / rope_sin must both be [max_positions, rotary_dim / 2]")
     if rotary_dim is None:
@@ -247,13 +258,40 @@ def attn_varlen_paged_rope_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
     if 2 * rope_cos.shape[1] != rotary_dim:
         raise VpkError(_lib.VPK_ERROR_INVALID_VALUE, "rope tables must have rotary_dim / 2 columns")
     rope = _lib.VpkRope(_ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], int(rotary_dim), int(bool(interleaved)))
+    return rope, rope_cos, rope_sin
+
+
+def attn_varlen_paged_qkv_prob_fwd(q: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                   k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                                   cu_seqlens_knew: Optional[torch.Tensor] = None,
+                                   k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
+                                   block_table: Optional[torch.Tensor] = None,
+                                   cache_seqlens: Optional[torch.Tensor] = None,
+                                   page_size: int = 0, causal: bool = True, scale: Optional[float] = None,
+                                   kv_scale: Optional[Sequence[float]] = None, *,
+                                   q_scale: float, p_scale: float = 1.0 / 448.0,
+                                   rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+                                   rotary_dim: Optional[int] = None, interleaved: bool = False,
+                                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                   return_lse: bool = True, host_index: Optional[dict] = None,
+                                   stream=None):
+    """attn_varlen_paged_fwd in fp8 "QKV-Prob" form (fp8 cache only): the query
+    rows are quantised to e4m3fn with ``q_scale``, the softmax output to
+    e4m3fn with ``p_scale`` before the second product, and both products run
+    on fp8 matrix cores.  ``rope_cos`` / ``rope_sin`` (optional) turn the
+    query rows and new key rows first, as attn_varlen_paged_rope_fwd does.
+    Returns (out, lse)."""
+    rope = None
+    if rope_cos is not None or rope_sin is not None:
+        rope = _rope_args(rope_cos, rope_sin, rotary_dim, interleaved)
     return _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
                        cache_seqlens, page_size, causal, scale, kv_scale, out, lse, return_lse, host_index,
-                       stream, (rope, rope_cos, rope_sin))
+                       stream, rope, prob8=(float(q_scale), float(p_scale)))
 
 
 def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table, cache_seqlens,
-                page_size, causal, scale, kv_scale, out, lse, return_lse, host_index, stream, rope, noalloc=False):
+                page_size, causal, scale, kv_scale, out, lse, return_lse, host_index, stream, rope, noalloc=False,
+                prob8=None):
     lib = _lib.load()
     q = _dev(q, "q", _BF16)
     cu_seqlens_q = _dev(cu_seqlens_q, "cu_seqlens_q", _I32)
@@ -322,7 +360,10 @@ def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache
         _check(st)
         return out, lse
     _ensure_workspace(dims, q.device, sh, rope is not None)
-    if rope is None:
+    if prob8 is not None:
+        qp = (ctypes.c_float * 2)(*prob8)
+        st = lib.attn_varlen_paged_qkv_prob_fwd(*args, qp, None if rope is None else ctypes.byref(rope[0]), *tail)
+    elif rope is None:
         st = lib.attn_varlen_paged_fwd(*args, *tail)
     else:
         st = lib.attn_varlen_paged_rope_fwd(*args, ctypes.byref(rope[0]), *tail)

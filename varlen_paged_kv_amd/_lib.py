@@ -29,7 +29,7 @@ EXPORTS = (
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
     "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
     "vpk_plan_run_device_scale", "vpk_set_workspace", "vpk_workspace_bytes_upper_bound", "vpk_library_memory",
-    "attn_varlen_paged_fwd_noalloc",
+    "attn_varlen_paged_fwd_noalloc", "attn_varlen_paged_qkv_prob_fwd",
 )
 
 
@@ -109,6 +109,9 @@ def load() -> ctypes.CDLL:
     lib.attn_varlen_paged_rope_fwd.restype = i32
     lib.attn_varlen_paged_rope_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32,
                                                P(f32), P(VpkRope), vp, vp, P(VpkHostIndex), vp]
+    lib.attn_varlen_paged_qkv_prob_fwd.restype = i32
+    lib.attn_varlen_paged_qkv_prob_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, f32,
+                                                   P(f32), P(f32), P(VpkRope), vp, vp, P(VpkHostIndex), vp]
     lib.attn_varlen_paged_list_fwd.restype = i32
     lib.attn_varlen_paged_list_fwd.argtypes = [P(VpkDims), vp, vp, vp, vp, vp, vp, i32, i32, f32, P(f32), vp, vp,
                                                P(VpkHostPages), vp]

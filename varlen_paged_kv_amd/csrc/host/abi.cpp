@@ -61,10 +61,10 @@ std::mutex g_tmu;
 std::atomic<bool> g_timing{false};
 std::vector<TimingRec> g_tpending;
 std::vector<hipEvent_t> g_tfree;
-constexpr int kTimedKernels = 6;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge,
-                                   // 4 rotary embedding, 5 mixed attention grid
-double g_tms[kTimedKernels] = {0, 0, 0, 0, 0, 0};
-int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0, 0, 0};
+constexpr int kTimedKernels = 7;   // 0 prefill-mode attention grid, 1 append, 2 decode-mode attention grid, 3 merge,
+                                   // 4 rotary embedding, 5 mixed attention grid, 6 fp8 QKV-Prob attention grid
+double g_tms[kTimedKernels] = {0, 0, 0, 0, 0, 0, 0};
+int64_t g_tcount[kTimedKernels] = {0, 0, 0, 0, 0, 0, 0};
 
 hipEvent_t take_event() {
   if (!g_tfree.empty()) {
@@ -306,6 +306,7 @@ struct Call {
   int32_t page_size;
   const float* kv_scale;                  // host {k_scale, v_scale} (fp8)
   const float* kv_scale_dev = nullptr;    // or the same in device memory, read by the kernels
+  const float* qp_scale = nullptr;        // fp8 QKV-Prob attention: host {q_scale, p_scale}
 };
 
 int32_t check_cu(const int32_t* cu, int32_t B, int32_t total, const char* name) {
@@ -687,7 +688,7 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
   // fp8 cache, or keys turned by the append: attention must see the stored
   // bytes, so the append runs first.
   const bool new_direct = do_append && !c.fp8 && rk.dim == 0;
-  const bool run_pre = plan.prefill.grid > 0;
+  const bool run_pre = plan.prefill.grid > 0 || (c.qp_scale && plan.mixed.grid > 0);
   const bool run_dec = plan.decode.grid > 0;
   // both kinds of items: one launch when asked to, or (default) when the two
   // grids would otherwise run one after the other (no side stream: prepared
@@ -741,6 +742,36 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
     p.rope = rq;
     p.app = ap;
     const int fmt = c.fp8 ? vpk::kKvFp8 : vpk::kKvBf16;
+    if (c.qp_scale) {
+      // fp8 QKV-Prob: every unit in the one grid (the plan has no splits);
+      // scores carry q_scale too, the output p_scale * v_scale
+      const vpk::Launch& Lc = plan.mixed;
+      if (Lc.grid <= 0) return VPK_SUCCESS;
+      AttnParams a = p;
+      a.num_pre_units = plan.num_pre_units;
+      a.items = reinterpret_cast<const WorkItem*>(R + L.items) + Lc.first;
+      a.queue_start = reinterpret_cast<const int32_t*>(R + L.queues) + Lc.queue_first;
+      a.queue_work = reinterpret_cast<const int32_t*>(R + L.work) + Lc.work_first;
+      a.persistent = Lc.persistent ? 1 : 0;
+      a.num_items = Lc.count;
+      a.attn_blocks = Lc.grid;
+      a.qk_scale_log2 = static_cast<float>(p.scale_log2e * static_cast<double>(kv_scale[0]) *
+                                           static_cast<double>(c.qp_scale[0]));
+      a.v_scale = static_cast<float>(static_cast<double>(c.qp_scale[1]) * static_cast<double>(kv_scale[1]));
+      a.kv_scale_dev = nullptr;
+      a.q_inv_scale = 1.0f / c.qp_scale[0];
+      a.p_log2 = static_cast<float>(std::log2(static_cast<double>(c.qp_scale[1])));
+      a.rope = vpk::RopeArgs{};
+      int rc;
+      if (timed) {
+        KernelTimer tm(6, stream);
+        rc = vpk::launch_attention_prob8(a, Lc.grid, dims->head_dim, stream);
+      } else {
+        rc = vpk::launch_attention_prob8(a, Lc.grid, dims->head_dim, stream);
+      }
+      if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "attention launch (QKV-Prob)");
+      return VPK_SUCCESS;
+    }
     // `with_append`: this grid also runs one workgroup per new token
     auto launch = [&](const vpk::Launch& Lc, int mode, hipStream_t s, bool with_append) -> int32_t {
       const bool dec = mode == vpk::kGridDecode;
@@ -853,6 +884,11 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   int32_t st;
   PlanInput in;
   fill_plan_input(c, m, causal, 0, in);
+  if (c.qp_scale) {
+    // QKV-Prob: one grid, whole key ranges (P needs each row's full sum)
+    in.force_splits = 1;
+    in.one_grid = true;
+  }
   if (rope && (st = check_rope_positions(in, rope))) return st;
   if ((st = refuse_capture(stream))) return st;
   Workspace* w = nullptr;
@@ -871,6 +907,9 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   } catch (const std::bad_alloc&) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
+  if (c.qp_scale && !plan.groups.empty())
+    return fail(VPK_ERROR_NOT_SUPPORTED, "QKV-Prob attention: a sequence's keys span more than " +
+                                             std::to_string(vpk::kMaxItemPages - 1) + " pages");
   // Rotary embedding: the attention kernels turn the query rows as they load
   // them (interleaved pairs, or half-split pairs whose two chunks one lane
   // holds: rotary_dim a multiple of 32); with an fp8 cache the append, which
@@ -887,7 +926,8 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   if (rope) {
     rc.positions = true;
     const vpk::RopeArgs ra{rope->cos, rope->sin, rope->rotary_dim, rope->interleaved};
-    const bool fused_q = rope->interleaved != 0 || rope->rotary_dim % 32 == 0;
+    // (the QKV-Prob grid reads turned copies of every query row)
+    const bool fused_q = !c.qp_scale && (rope->interleaved != 0 || rope->rotary_dim % 32 == 0);
     q_dec_copy = fused_q && plan.decode.grid > 0 && !(plan.mixed.grid > 0 && g_opt.mixed_grid.load() == 1);
     rc.q = (!fused_q || q_dec_copy) && dims->total_q > 0;
     if (fused_q) rq = ra;
@@ -1010,7 +1050,8 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
                   void* k_cache, void* v_cache, const int32_t* block_table,
                   const int32_t* cache_seqlens, int32_t page_size, int32_t causal, float scale,
                   const float* kv_scale, void* out, float* lse, const vpk_host_index* host,
-                  void* stream_v, const vpk_rope* rope = nullptr, bool noalloc = false) {
+                  void* stream_v, const vpk_rope* rope = nullptr, bool noalloc = false,
+                  const float* qp_scale = nullptr, bool prob8 = false) {
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   if (!dims) return fail(VPK_ERROR_INVALID_VALUE, "dims is NULL");
   // new tokens are present when any of their arrays is given; with total_knew == 0
@@ -1018,8 +1059,18 @@ int32_t attn_impl(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens
   Call c{dims, k_new != nullptr || v_new != nullptr || cu_seqlens_knew != nullptr,
          k_cache != nullptr || v_cache != nullptr,
          dims->kv_cache_dtype == VPK_DTYPE_FP8_E4M3FN && (k_cache || v_cache), page_size, kv_scale};
+  c.qp_scale = prob8 ? qp_scale : nullptr;
   int32_t st = check_dims(c);
   if (st != VPK_SUCCESS) return st;
+  if (prob8) {
+    if (!c.fp8 || !c.has_cache)
+      return fail(VPK_ERROR_INVALID_VALUE, "QKV-Prob attention needs an fp8 (e4m3fn) cache");
+    if (!qp_scale) return fail(VPK_ERROR_INVALID_VALUE, "qp_scale is NULL");
+    if (!std::isfinite(qp_scale[0]) || !(qp_scale[0] > 0.f))
+      return fail(VPK_ERROR_INVALID_VALUE, "q_scale must be finite and > 0");
+    if (!std::isfinite(qp_scale[1]) || !(static_cast<double>(qp_scale[1]) >= 1.0 / 452.0))
+      return fail(VPK_ERROR_INVALID_VALUE, "p_scale must be finite and >= 1/452");
+  }
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_new and v_new must both be given or both be NULL");
   if ((k_cache == nullptr) != (v_cache == nullptr)) return fail(VPK_ERROR_INVALID_VALUE, "k_cache and v_cache must both be given or both be NULL");
   if (!c.has_new && !c.has_cache) return fail(VPK_ERROR_INVALID_VALUE, "no keys: give k_new/v_new, a cache, or both");
@@ -1415,6 +1466,24 @@ int32_t attn_varlen_paged_rope_fwd(const vpk_dims* dims, const void* q, const in
   }
 }
 
+int32_t attn_varlen_paged_qkv_prob_fwd(const vpk_dims* dims, const void* q, const int32_t* cu_seqlens_q,
+                                       const void* k_new, const void* v_new, const int32_t* cu_seqlens_knew,
+                                       void* k_cache, void* v_cache, const int32_t* block_table,
+                                       const int32_t* cache_seqlens, int32_t page_size, int32_t causal, float scale,
+                                       const float* kv_scale, const float* qp_scale, const vpk_rope* rope, void* out,
+                                       float* lse, const vpk_host_index* host, void* stream) {
+  try {
+    g_err.clear();
+    return attn_impl(dims, q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache, block_table,
+                     cache_seqlens, page_size, causal, scale, kv_scale, out, lse, host, stream, rope, false, qp_scale,
+                     true);
+  } catch (const std::bad_alloc&) {
+    return fail(VPK_ERROR_OUT_OF_MEMORY, "host allocation failed");
+  } catch (...) {
+    return fail(VPK_ERROR_INVALID_VALUE, "unexpected host exception");
+  }
+}
+
 int32_t attn_varlen_paged_list_fwd(const vpk_dims* dims, const void* q, const void* k_new, const void* v_new,
                                    void* k_cache, void* v_cache, const int32_t* kv_indices, int32_t page_size,
                                    int32_t causal, float scale, const float* kv_scale, void* out, float* lse,
@@ -1552,7 +1621,7 @@ int32_t vpk_timing_reset(void) {
 }
 
 int32_t vpk_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
-  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..5");
+  if (kernel < 0 || kernel >= kTimedKernels) return fail(VPK_ERROR_INVALID_VALUE, "kernel id must be 0..6");
   std::lock_guard<std::mutex> lk(g_tmu);
   for (const TimingRec& r : g_tpending) {
     hipError_t e = hipEventSynchronize(r.b);

@@ -302,7 +302,8 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.decode.first = n_prefill_units;
   out.decode.count = static_cast<int32_t>(out.items.size()) - n_prefill_units;
   out.num_pre_units = n_prefill_units;
-  const bool with_mixed = in.mixed && out.prefill.count > 0 && out.decode.count > 0;
+  const bool with_mixed =
+      (in.mixed && out.prefill.count > 0 && out.decode.count > 0) || (in.one_grid && !out.items.empty());
   if (with_mixed) {
     out.mixed.first = 0;
     out.mixed.count = static_cast<int32_t>(out.items.size());
@@ -323,6 +324,10 @@ void build_plan(const PlanInput& in, Plan& out) {
   out.persistent = false;
   for (Launch* L : {&out.prefill, &out.decode, &out.mixed}) {
     if (L == &out.mixed && !with_mixed) continue;
+    if (in.one_grid && L != &out.mixed) {
+      L->grid = 0;
+      continue;
+    }
     const int64_t nwork = static_cast<int64_t>(L->count) * in.hkv;
     const int64_t lslots = static_cast<int64_t>(std::max(1, in.num_cus)) *
                            std::max(1, L == &out.decode ? in.wg_per_cu : in.pre_wg_per_cu);
@@ -356,7 +361,7 @@ void build_plan(const PlanInput& in, Plan& out) {
     // in the mixed grid a decode-mode unit runs on all eight waves of a
     // workgroup that holds the whole CU: half the slot time of its cost,
     // which counts a four-wave workgroup sharing the CU with another
-    const bool halve_dec = L == &out.mixed;
+    const bool halve_dec = L == &out.mixed && !in.one_grid;
     auto cost_of = [&](int32_t u) {
       const double c = un[ord[u]].cost;
       return halve_dec && L->first + u >= n_prefill_units ? 0.5 * c : c;

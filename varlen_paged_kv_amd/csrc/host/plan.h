@@ -33,6 +33,7 @@ struct PlanInput {
   int32_t force_splits = 0;             // 0: planner decides
   int32_t persistent = -1;              // -1 planner, 0 off, 1 on
   bool mixed = false;                   // a batch with both kinds of items also gets the one-launch grid
+  bool one_grid = false;                // every unit in the one-launch grid only (Plan::mixed), whatever its kinds
   int32_t mixed_dec_parts = 1;          // with both kinds: decode-mode parts of total / (num_cus * this)
   int32_t split_min_keys = 256;
   // largest number of split-partial rows the workspace holds (< 0: no limit);

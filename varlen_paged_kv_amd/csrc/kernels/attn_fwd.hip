@@ -59,6 +59,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -1600,6 +1601,316 @@ struct Mixed {
   }
 };
 
+// ---------------------------------------------------------------- fp8 QKV-Prob
+// Attention with the query, key and value rows and the softmax output P all in
+// fp8: the "QKV-Prob" models of the vLLM Triton FAv2 PR page ("[Kernel][Triton]
+// [FP8] Adding fp8 and variable length sequence support to Triton FAv2
+// kernel", feature list item 7, and the paragraph before its LM EVAL tables:
+// softmax(QK^T) is quantised to fp8 before the second product).  Both
+// products run on gfx950's v_mfma_f32_32x32x64_f8f6f4 with e4m3 operands:
+// K and V stay raw cache codes in LDS (nothing is widened), and the query rows
+// are quantised as they are loaded, by the cache's rule with q_scale.  P is
+// the row's exact softmax: a first pass over the item's keys computes only
+// the scores and each row's maximum m and sum l; a second pass recomputes the
+// scores, rounds P / p_scale = 2^(s c - m c - log2 l - log2 p_scale) to e4m3
+// with the hardware conversion (nearest, ties to even) and adds P V.  The
+// output is O * p_scale * v_scale, not renormalised after the quantisation.
+//
+// MFMA operands (32 rows x 64 k values, 32 bytes per lane): both operands of
+// the instruction map (lane half, byte) to k the same way, so any assignment
+// of the 64 k values that both share gives the same sums.  Scores: lane half
+// lg holds head-dim values 64 s + 32 lg + (0..31) at step s.  P V: byte
+// 16 h + i of the P operand is element i of score accumulator h (key
+// 32 h + 8 (i / 4) + 4 lg + i % 4), and four transposed LDS reads gather the
+// V^T operand for the same keys.  Items are never split: the host plans this
+// grid without key-range parts.
+template <int D>
+struct Prob8 : Src<D, kKvFp8, true> {
+  using B = Src<D, kKvFp8, true>;
+  using C = Cfg<D>;
+  using Item = typename B::Item;
+  static constexpr int NW = kPrefillWaves;
+  static constexpr int NT = NW * 64;
+  static constexpr int ROW = D;                   // bytes of a code row
+  static constexpr int CPR = ROW / 16;            // 16-byte chunks of a row
+  static constexpr int TILE = kBlockN * ROW;      // bytes of a 64-key tile
+  static constexpr int STAGE = 2 * TILE;          // K tile, then V tile
+  static constexpr int NS = 3;                    // ring stages
+  static constexpr int KS = D / 64;               // MFMA steps over the head dim
+  static constexpr int DBLK = D / 32;             // 32-wide output blocks
+  static constexpr int RPW = 1024 / ROW;          // rows one wave copies with one instruction
+  static constexpr int WPT = kBlockN / RPW;       // waves that copy one tile
+
+  // Chunk c of code row r sits at c ^ sw(r).  Score reads (16 consecutive
+  // rows, one chunk each) and the transposed V reads (rows {0..3, 8..11} +
+  // 4 lg + 16 j, chunks c and c ^ 1 in the two lane groups of a half wave)
+  // then touch distinct banks.
+  __device__ static __forceinline__ int sw(int r) {
+    if constexpr (D == 128) return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
+    else return (r >> 2) & 3;
+  }
+
+  // query row codes: head-dim values 64 s + 32 lg + (0..31) of this lane's row
+  __device__ static __forceinline__ void load_q8(const AttnParams& p, const SeqInfo& sq, int kvh, int prow,
+                                                 bool row_ok, int lg, i32x8 (&qf)[KS], int& token, int& qh) {
+    using append_detail::enc2;
+    token = prow / p.g;
+    qh = kvh * p.g + (prow - token * p.g);
+    const uint16_t* qrow = p.q + (static_cast<int64_t>(sq.q_start + token) * p.hq + qh) * D;
+    u32x4 x[KS][4];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * lg + 8 * t4);
+        x[s][t4] = v;
+      }
+    const float inv = p.q_inv_scale;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        qf[s][2 * t4] = static_cast<int>(enc2(x[s][t4][0], inv) | (enc2(x[s][t4][1], inv) << 16));
+        qf[s][2 * t4 + 1] = static_cast<int>(enc2(x[s][t4][2], inv) | (enc2(x[s][t4][3], inv) << 16));
+      }
+  }
+
+  // copies of the tile rows of keys [kbase, kbase + 64) into stage `st`: K
+  // (and V when WITH_V); rows past the item's end or on an unusable page
+  // read zeros.  Returns the copies this wave issued.
+  template <bool WITH_V>
+  __device__ static __forceinline__ int stage(const AttnParams& p, const Item& it, uint8_t* st, int kbase,
+                                              int wave, int lane) {
+    const char* zeros = static_cast<const char*>(p.zeros);
+    const int part = wave % WPT;
+    const int r = part * RPW + lane / CPR;
+    const int c = (lane % CPR) ^ sw(r);
+    const char *kp, *vp;
+    const bool ok = B::template row_src<true>(p, it, kbase + r, kp, vp);
+    uint8_t* const dst = st + part * RPW * ROW;
+    if constexpr (WPT == NW) {
+      dma16<true>(ok ? kp + c * 16 : zeros, reinterpret_cast<uint16_t*>(dst));
+      if constexpr (WITH_V) dma16<true>(ok ? vp + c * 16 : zeros, reinterpret_cast<uint16_t*>(dst + TILE));
+      return WITH_V ? 2 : 1;
+    } else {
+      // half of the waves copy K, the other half V
+      const bool is_v = wave >= WPT;
+      if (is_v && !WITH_V) return 0;
+      dma16<true>(ok ? (is_v ? vp : kp) + c * 16 : zeros, reinterpret_cast<uint16_t*>(dst + (is_v ? TILE : 0)));
+      return 1;
+    }
+  }
+
+  // S^T of this wave's 32 query rows against the tile's 64 keys
+  __device__ static __forceinline__ void qk(const uint8_t* kt, const i32x8 (&qf)[KS], f32x16 (&acc)[2], int lr,
+                                            int lg) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+    i32x8 kf[KS][2];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 32 * h + lr;
+        const int c0 = 4 * s + 2 * lg;
+        const u32x4 x0 = B::template lds_read<u32x4>(
+            B::lds_addr(reinterpret_cast<const uint16_t*>(kt + r * ROW + ((c0 ^ sw(r)) << 4))));
+        const u32x4 x1 = B::template lds_read<u32x4>(
+            B::lds_addr(reinterpret_cast<const uint16_t*>(kt + r * ROW + (((c0 + 1) ^ sw(r)) << 4))));
+        kf[s][h] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][h], qf[s], acc[h], 0, 0, 0, 0, 0, 0);
+  }
+
+  // first pass: running row maximum and sum; `rel` is the last visible key
+  // relative to this lane's first key of the block (MASK)
+  template <bool MASK>
+  __device__ static __forceinline__ void stats(f32x16 (&acc)[2], float& m_run, float& l_run, int rel, float c) {
+    if constexpr (MASK) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (h * 32 + (i >> 2) * 8 + (i & 3) > rel) acc[h][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[h][i]);
+    mx = wave_pair_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float neg = m_new == -INFINITY ? 0.f : -m_new * c;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][i], c, neg));
+    // (m_run = -inf: the old sum is 0 and exp2(-inf) = 0)
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    l_run = l_run * alpha + s;
+    m_run = m_new;
+  }
+
+  // second pass: the P operand, e4m3 codes of 2^(s c + neg2) = P / p_scale
+  template <bool MASK>
+  __device__ static __forceinline__ i32x8 probs(const f32x16 (&acc)[2], int rel, float c, float neg2) {
+    i32x8 pb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          y[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][i], c, neg2));
+          if (MASK && h * 32 + q4 * 8 + e > rel) y[e] = 0.f;
+        }
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w, true);
+        pb[4 * h + q4] = w;
+      }
+    return pb;
+  }
+
+  // V^T operand of output block d: bytes 8 j + (0..7) hold keys 16 j + 4 lg +
+  // (0..3) and 16 j + 8 + 4 lg + (0..3) of head-dim value 32 d + lr, the key
+  // order of the P operand.  A 16-lane group addresses 8 code rows (lanes 2q
+  // and 2q + 1 the two halves of row q's chunk); ds_read_b64_tr_b8 gives lane
+  // i byte i of each of the 8 rows, in row order.
+  __device__ static __forceinline__ i32x8 vread(const uint8_t* vt, int d, int lr, int lg) {
+    const int i = lr & 15;
+    const int q = i >> 1;
+    const int chunk = 2 * d + (lr >> 4);
+    i32x8 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * j + 4 * lg + (q & 3) + 8 * (q >> 2);
+      const uint8_t* a = vt + row * ROW + ((chunk ^ sw(row)) << 4) + 8 * (i & 1);
+      const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2*>(
+          static_cast<uintptr_t>(B::lds_addr(reinterpret_cast<const uint16_t*>(a)))));
+      v[2 * j] = x[0];
+      v[2 * j + 1] = x[1];
+    }
+    return v;
+  }
+
+  __device__ static __forceinline__ void item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq,
+                                              const Item& it, uint8_t* ring, int* lims, float c, float out_scale,
+                                              int wave, int lr, int lg, int t) {
+    const int lane = t & 63;
+    const int kbeg = item.key_begin;
+    const int nblk = it.kend > kbeg ? (it.kend - kbeg + kBlockN - 1) / kBlockN : 0;
+    const int q_start = __builtin_amdgcn_readfirstlane(sq.q_start);
+    const int wrow = wave * kWaveRows + lr;
+    const bool row_ok = wrow < item.nrows;
+    i32x8 qf[KS];
+    int token, qh;
+    load_q8(p, sq, it.kvh, item.row0 + wrow, row_ok, lg, qf, token, qh);
+
+    // per-row and per-wave key bounds (as in the prefill-mode kernel)
+    const int shift = sq.kv_len - sq.q_len;
+    {
+      int lim = it.kend - 1;
+      if (p.causal) lim = min(lim, token + shift);
+      lims[t] = lim - lg * 4;
+    }
+    const int wr0 = wave * kWaveRows;
+    const int wr1 = min(item.nrows, wr0 + kWaveRows) - 1;
+    int wlo = it.kend - 1, whi = it.kend - 1;
+    if (p.causal) {
+      wlo = min(wlo, (item.row0 + wr0) / p.g + shift);
+      whi = min(whi, (item.row0 + wr1) / p.g + shift);
+    }
+    const int nb_w = (wr1 < wr0 || whi < kbeg) ? 0 : min(nblk, (whi - kbeg) / kBlockN + 1);
+    const int n_full = min(nb_w, max(0, (wlo - kbeg + 1) / kBlockN));
+
+    // one pass over the item's blocks: block n + 2 is copied while block n
+    // is computed (three stages; barrier n frees the stage of block n - 1)
+    auto stage_of = [&](int j) {
+      return ring + (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j)) % 3u) * STAGE;
+    };
+    auto pass = [&](auto v_tag, auto&& body) {
+      constexpr bool WITH_V = decltype(v_tag)::value;
+      int cpb = 0;
+      if (nblk > 0) cpb = stage<WITH_V>(p, it, stage_of(0), kbeg, wave, lane);
+      if (nblk > 1) stage<WITH_V>(p, it, stage_of(1), kbeg + kBlockN, wave, lane);
+      for (int n = 0; n < nblk; ++n) {
+        wait_vmem_upto(n + 1 < nblk ? cpb : 0);
+        __syncthreads();
+        if (n + 2 < nblk) stage<WITH_V>(p, it, stage_of(n + 2), kbeg + (n + 2) * kBlockN, wave, lane);
+        if (n < nb_w) body(n, stage_of(n));
+      }
+      __syncthreads();   // every wave is done with the ring
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    pass(std::false_type{}, [&](int n, const uint8_t* st) {
+      f32x16 acc[2];
+      qk(st, qf, acc, lr, lg);
+      if (n < n_full) stats<false>(acc, m_run, l_run, 0, c);
+      else stats<true>(acc, m_run, l_run, lims[t] - (kbeg + n * kBlockN), c);
+    });
+    const float l_tot = wave_pair_sum(l_run);
+    const bool live = l_tot > 0.f;
+    const float neg2 = live ? -(m_run * c + __log2f(l_tot) + p.p_log2) : 0.f;
+
+    f32x16 o[DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+    pass(std::true_type{}, [&](int n, const uint8_t* st) {
+      f32x16 acc[2];
+      qk(st, qf, acc, lr, lg);
+      const i32x8 pb = n < n_full ? probs<false>(acc, 0, c, neg2)
+                                  : probs<true>(acc, lims[t] - (kbeg + n * kBlockN), c, neg2);
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+        o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread(st + TILE, d, lr, lg), pb, o[d], 0, 0, 0, 0,
+                                                               0, 0);
+    });
+
+    if (wr1 >= wr0) {
+      const float inv = live ? out_scale : 0.f;
+      const float lse_v = live ? m_run * c * kLn2 + __logf(l_tot) : -INFINITY;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) B::store_out_block(p, q_start, token, qh, d, o[d], inv, lg, row_ok);
+      if (row_ok && lg == 0 && p.lse) p.lse[static_cast<int64_t>(qh) * p.total_q + q_start + token] = lse_v;
+    }
+  }
+
+  __device__ static __forceinline__ void run(const AttnParams& p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+    __shared__ int32_t pids[kMaxItemPages];
+    __shared__ int lims[NT];
+    __shared__ typename B::QEntry qbuf[B::kQueueChunk];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int lr = lane & 31;
+    const int lg = lane >> 5;
+    const float c = p.qk_scale_log2;
+    const float out_scale = p.v_scale;
+    B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      item(p, e.item, e.item.s, it, ring, lims, c, out_scale, wave, lr, lg, t);
+    });
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_prob8_kernel(const AttnParams p) {
+  Prob8<D>::run(p);
+}
+
 // ROPE: the query rows are turned by rotary embedding as they are loaded
 // (separate instantiations, so that the other kernels' register allocation
 // does not carry the rotation code)
@@ -1637,6 +1948,17 @@ int launch_d(const AttnParams& p, int grid, int kv_format, bool paged, int mode,
 }
 
 }  // namespace
+
+int launch_attention_prob8(const AttnParams& p, int grid, int head_dim, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_prob8_kernel<128>, dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
+  else if (head_dim == 64)
+    hipLaunchKernelGGL(attn_prob8_kernel<64>, dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);
+  else
+    return static_cast<int>(hipErrorInvalidValue);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
                      int mode, void* stream) {

@@ -138,6 +138,10 @@ struct AttnParams {
   double scale_log2e;         // scale * log2(e) in double, for the device-scale product
   RopeArgs rope;              // query rows turned as they are loaded (dim 0: none)
   AppendParams app;           // the append, when it runs inside this grid
+  // fp8 "QKV-Prob" grid only (qk_scale_log2 then also holds q_scale, v_scale
+  // the product p_scale * v_scale)
+  float q_inv_scale;          // fp32(1 / q_scale): the query rows' quantiser
+  float p_log2;               // log2(p_scale)
 };
 
 
@@ -187,6 +191,8 @@ enum GridMode : int { kGridPrefill = 0, kGridDecode = 1, kGridMixed = 2 };
 // Kernel launchers (defined in the .hip files); they return hipError_t as int.
 int launch_attention(const AttnParams& p, int grid, int head_dim, int kv_format, bool paged,
                      int mode, void* stream);
+// fp8 "QKV-Prob" attention over every unit of the launch (fp8 cache, no splits)
+int launch_attention_prob8(const AttnParams& p, int grid, int head_dim, void* stream);
 int launch_append(const AppendParams& p, void* stream);
 int launch_merge(const MergeParams& p, void* stream);
 int launch_rope(const RopeParams& p, int head_dim, void* stream);
