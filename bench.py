@@ -9,8 +9,9 @@ without a cache (16 sequences, lengths U[256, 2048], 32 query / 8 kv heads,
 head_dim 128, bf16, causal): prefill TFLOP/s.  The line also carries
 `decode` (paged decode, KV GB/s against HBM), `chunked_prefill` (TFLOP/s) and
 `mixed_fp8` (the mixed prefill + decode batch over an fp8 cache: the step,
-the prefill rows alone, the decode rows alone, the fused / serial ratio and
-the combined roofline fraction), each with its own roofline and CPU baseline.
+the prefill rows alone, the decode rows alone, the fused / serial ratio, the
+combined roofline fraction, and the same batch through the fp8 QKV-Prob call
+against the fp8 MFMA peak), each with its own roofline and CPU baseline.
 With --workload NAME only that workload is measured and it is the headline
 (names: varlen_prefill, paged_decode, chunked_prefill, mixed_fp8, tiny).
 
@@ -47,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill attn TFLOP/s + decode KV GB/s (% of MI355X peak), varlen paged"
 PEAK_BF16_TFLOPS = 2500.0     # dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # HBM3E
 KERNEL_SOURCES = ["varlen_paged_kv_amd/csrc/kernels/attn_fwd.hip", "varlen_paged_kv_amd/csrc/kernels/append_dev.h",
                   "varlen_paged_kv_amd/csrc/vpk_internal.h"]
@@ -163,12 +165,14 @@ def cpu_baseline(wl, budget_s):
 class Runner:
     """Device copies of one workload's inputs and the timing passes over them."""
 
-    def __init__(self, wl, dev, rotate, rope=False, mode="direct"):
+    def __init__(self, wl, dev, rotate, rope=False, mode="direct", qp_scale=None):
         import torch
         import varlen_paged_kv_amd as vpk
         self.torch, self.vpk, self.wl = torch, vpk, wl
         self.fp8 = wl.cache_dtype == "fp8"
         self.mode = mode
+        # (q_scale, p_scale): each step is the fp8 QKV-Prob call (direct calls only)
+        self.qp_scale = qp_scale
 
         def bf16(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -242,7 +246,11 @@ class Runner:
         wl, c = self.wl, self.copies[i % len(self.copies)]
         args = (c["q"], c["cu_q"], c["k_new"], c["v_new"], c["cu_kn"], c["kc"], c["vc"], c["bt"], c["cl"],
                 wl.page_size, wl.causal, wl.scale, wl.kv_scale if self.fp8 else None)
-        if self.rope_kw is None:
+        if self.qp_scale is not None:
+            self.vpk.attn_varlen_paged_qkv_prob_fwd(*args, q_scale=self.qp_scale[0], p_scale=self.qp_scale[1],
+                                                    out=c["out"], lse=c["lse"], host_index=self.host,
+                                                    **(self.rope_kw or {}))
+        elif self.rope_kw is None:
             self.vpk.attn_varlen_paged_fwd(*args, out=c["out"], lse=c["lse"], host_index=self.host)
         else:
             self.vpk.attn_varlen_paged_rope_fwd(*args, **self.rope_kw, out=c["out"], lse=c["lse"],
@@ -285,7 +293,8 @@ class Runner:
         kern = {}
         for key, kid in (("prefill_grid", vpk.KERNEL_ATTENTION), ("decode_grid", vpk.KERNEL_ATTENTION_DECODE),
                          ("mixed_grid", vpk.KERNEL_ATTENTION_MIXED), ("append", vpk.KERNEL_APPEND),
-                         ("merge", vpk.KERNEL_MERGE), ("rope", vpk.KERNEL_ROPE)):
+                         ("merge", vpk.KERNEL_MERGE), ("rope", vpk.KERNEL_ROPE),
+                         ("prob8_grid", vpk.KERNEL_ATTENTION_PROB8)):
             ms, n = vpk.timing_read(kid)
             kern[key] = (ms * 1e3 / n if n else 0.0, n)
         gpu_ms, wall = self.timed(steps, False)
@@ -386,6 +395,8 @@ def measure_workload(name, args, dev, cpu_budget):
             del rs
         obj["parts_alone_ms"] = parts
         obj["fused_over_serial"] = m["ms_per_step"] / (parts["prefill_rows"] + parts["decode_rows"])
+        if not args.no_qkv_prob:
+            obj["qkv_prob"] = measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops)
     else:
         obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
@@ -402,6 +413,49 @@ def measure_workload(name, args, dev, cpu_budget):
         log(f"{name}: timing the CPU oracle on a bounded sample")
         obj["cpu_baseline"] = cpu_baseline(wl, cpu_budget)
     return obj
+
+
+def measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops):
+    """The same batch through the fp8 QKV-Prob call (query rows and P in e4m3 too, both products
+    on the fp8 MFMA; q_scale = amax(q) / 448, p_scale = 1 / 448): step throughput and the roofline
+    of its one attention grid against the fp8 MFMA peak."""
+    q32 = (wl.q.astype(np.uint32) << 16).view(np.float32)
+    qp = (float(np.float32(np.abs(q32).max() / 448.0)), 1.0 / 448.0)
+    r = Runner(wl, dev, args.rotate, rope=args.rope, qp_scale=qp)
+    m = r.measure(args.steps, args.warmup, args.settle)
+    log(summary(f"{wl.name} QKV-Prob", m))
+    del r
+    us = m["kernels"]["prob8_grid"][0]
+    elapsed = m["ms_per_step"] / 1e3
+    ach = pre_flops / (us / 1e6) / 1e12 if us > 0 else 0.0
+    roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_FP8_TFLOPS, "traffic": None,
+            "kernel": "attention (fp8 QKV-Prob grid: every item of the batch in one launch)",
+            "kernel_avg_us": us, "kernel_timing": kernel_note(m, args.steps),
+            "note": "achieved counts the algorithmic 4 * D FLOPs per visible (query, key) pair of the "
+                    "prefill rows; the kernel also computes every score twice (a first pass for the "
+                    "row maximum and sum), 6 * D executed FLOPs per pair",
+            "decode_part": {"bytes": dec_bytes, "gbs_over_kernel": dec_bytes / (us / 1e6) / 1e9 if us > 0 else 0.0},
+            "combined_frac_kernel": (pre_flops / (PEAK_FP8_TFLOPS * 1e12) + dec_bytes / (PEAK_HBM_GBS * 1e9))
+            / (us / 1e6) if us > 0 else 0.0}
+    res = {"call": "attn_varlen_paged_qkv_prob_fwd", "dtype": "fp8 e4m3 (Q, K, V and P)",
+           "q_scale": qp[0], "p_scale": qp[1], "ms_per_step": m["ms_per_step"],
+           "value": step_flops / elapsed / 1e12, "unit": "TFLOP/s", "roofline": roof}
+    if not args.no_parts:
+        from synth import subset
+        dec = decode_rows(wl)
+        parts = {}
+        for label, seqs in (("prefill_rows", np.nonzero(~dec)[0]), ("decode_rows", np.nonzero(dec)[0])):
+            rs = Runner(subset(wl, seqs), dev, args.rotate, rope=args.rope, qp_scale=qp)
+            ms = rs.measure(args.steps, args.warmup, args.settle)
+            log(summary(f"{wl.name} QKV-Prob {label} alone", ms))
+            parts[label] = {"ms_per_step": ms["ms_per_step"], "grid_us": ms["kernels"]["prob8_grid"][0]}
+            del rs
+        res["parts_alone"] = parts
+        pus = parts["prefill_rows"]["grid_us"]
+        if pus > 0:
+            res["prefill_rows_grid_frac_fp8"] = pre_flops / (pus / 1e6) / 1e12 / PEAK_FP8_TFLOPS
+    return res
 
 
 def main():
@@ -427,6 +481,8 @@ def main():
     ap.add_argument("--mixed-grid", type=int, default=-2, help="library option mixed_grid (-1, 0 or 1; default: the library's)")
     ap.add_argument("--mixed-dec-parts", type=int, default=0, help="library option mixed_dec_parts (0: the library's)")
     ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
+    ap.add_argument("--no-qkv-prob", action="store_true",
+                    help="mixed batch: do not also time it through the fp8 QKV-Prob call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -469,8 +525,9 @@ def main():
         "config": head["config"], "pct_of_peak": head["pct_of_peak"], "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
-    if "rope_kernel" in head:
-        line["rope_kernel"] = head["rope_kernel"]
+    for key in ("rope_kernel", "qkv_prob", "parts_alone_ms", "fused_over_serial"):
+        if key in head:
+            line[key] = head[key]
     for name in names[1:]:
         line["decode" if name == "paged_decode" else name] = objs[name]
     print(json.dumps(line), flush=True)

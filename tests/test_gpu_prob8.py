@@ -126,6 +126,8 @@ SMALL = [
     ("rows_without_keys", [9, 4], [2, 4], [0, 0], 4, 2, 128, 8, True),
     ("empty_sequences", [0, 70, 0, 1], [0, 70, 0, 1], [10, 0, 0, 5], 8, 1, 128, 16, True),
     ("many_tiles_g1", [600], [600], [100], 2, 2, 128, 64, True),
+    ("decode_long_32_rows", [4, 1, 2], [4, 1, 2], [8000, 3000, 33], 16, 2, 128, 16, True),
+    ("decode_D64_S7", [1, 2, 1], [1, 2, 1], [2000, 77, 5], 8, 4, 64, 7, True),
 ]
 
 

@@ -361,7 +361,7 @@ void build_plan(const PlanInput& in, Plan& out) {
     // in the mixed grid a decode-mode unit runs on all eight waves of a
     // workgroup that holds the whole CU: half the slot time of its cost,
     // which counts a four-wave workgroup sharing the CU with another
-    const bool halve_dec = L == &out.mixed && !in.one_grid;
+    const bool halve_dec = L == &out.mixed;
     auto cost_of = [&](int32_t u) {
       const double c = un[ord[u]].cost;
       return halve_dec && L->first + u >= n_prefill_units ? 0.5 * c : c;

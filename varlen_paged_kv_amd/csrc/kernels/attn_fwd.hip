@@ -115,15 +115,19 @@ __device__ __forceinline__ float wave_pair_sum(float x) {
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// wait until at most n (0..4) vector-memory instructions of this wave are in
-// flight; larger n waits for at most 4
+// wait until at most n (0..8) vector-memory instructions of this wave are in
+// flight; larger n waits for at most 8
 __device__ __forceinline__ void wait_vmem_upto(int n) {
   switch (n) {
     case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
     case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
     case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
   }
 }
 
@@ -1623,7 +1627,9 @@ struct Mixed {
 // 16 h + i of the P operand is element i of score accumulator h (key
 // 32 h + 8 (i / 4) + 4 lg + i % 4), and four transposed LDS reads gather the
 // V^T operand for the same keys.  Items are never split: the host plans this
-// grid without key-range parts.
+// grid without key-range parts.  Prefill-mode items (more than 32 rows) run
+// eight waves of 32 rows over shared 64-key tiles; decode-mode items (at most
+// 32 rows) split their keys over the eight waves.
 template <int D>
 struct Prob8 : Src<D, kKvFp8, true> {
   using B = Src<D, kKvFp8, true>;
@@ -1702,18 +1708,19 @@ struct Prob8 : Src<D, kKvFp8, true> {
     }
   }
 
-  // S^T of this wave's 32 query rows against the tile's 64 keys
-  __device__ static __forceinline__ void qk(const uint8_t* kt, const i32x8 (&qf)[KS], f32x16 (&acc)[2], int lr,
+  // S^T of this wave's 32 query rows against the tile's first 32 NH keys
+  template <int NH>
+  __device__ static __forceinline__ void qk(const uint8_t* kt, const i32x8 (&qf)[KS], f32x16 (&acc)[NH], int lr,
                                             int lg) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
-    i32x8 kf[KS][2];
+    i32x8 kf[KS][NH];
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < NH; ++h) {
         const int r = 32 * h + lr;
         const int c0 = 4 * s + 2 * lg;
         const u32x4 x0 = B::template lds_read<u32x4>(
@@ -1725,24 +1732,24 @@ struct Prob8 : Src<D, kKvFp8, true> {
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
         acc[h] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][h], qf[s], acc[h], 0, 0, 0, 0, 0, 0);
   }
 
   // first pass: running row maximum and sum; `rel` is the last visible key
   // relative to this lane's first key of the block (MASK)
-  template <bool MASK>
-  __device__ static __forceinline__ void stats(f32x16 (&acc)[2], float& m_run, float& l_run, int rel, float c) {
+  template <int NH, bool MASK>
+  __device__ static __forceinline__ void stats(f32x16 (&acc)[NH], float& m_run, float& l_run, int rel, float c) {
     if constexpr (MASK) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (h * 32 + (i >> 2) * 8 + (i & 3) > rel) acc[h][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[h][i]);
     mx = wave_pair_max(mx);
@@ -1750,7 +1757,7 @@ struct Prob8 : Src<D, kKvFp8, true> {
     const float neg = m_new == -INFINITY ? 0.f : -m_new * c;
     float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[h][i], c, neg));
     // (m_run = -inf: the old sum is 0 and exp2(-inf) = 0)
@@ -1760,11 +1767,12 @@ struct Prob8 : Src<D, kKvFp8, true> {
   }
 
   // second pass: the P operand, e4m3 codes of 2^(s c + neg2) = P / p_scale
-  template <bool MASK>
-  __device__ static __forceinline__ i32x8 probs(const f32x16 (&acc)[2], int rel, float c, float neg2) {
-    i32x8 pb;
+  // (bytes of keys past the block's 32 NH are zero)
+  template <int NH, bool MASK>
+  __device__ static __forceinline__ i32x8 probs(const f32x16 (&acc)[NH], int rel, float c, float neg2) {
+    i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         float y[4];
@@ -1785,14 +1793,16 @@ struct Prob8 : Src<D, kKvFp8, true> {
   // (0..3) and 16 j + 8 + 4 lg + (0..3) of head-dim value 32 d + lr, the key
   // order of the P operand.  A 16-lane group addresses 8 code rows (lanes 2q
   // and 2q + 1 the two halves of row q's chunk); ds_read_b64_tr_b8 gives lane
-  // i byte i of each of the 8 rows, in row order.
+  // i byte i of each of the 8 rows, in row order.  Keys past the tile's
+  // 32 NH rows read as zero.
+  template <int NH>
   __device__ static __forceinline__ i32x8 vread(const uint8_t* vt, int d, int lr, int lg) {
     const int i = lr & 15;
     const int q = i >> 1;
     const int chunk = 2 * d + (lr >> 4);
-    i32x8 v;
+    i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2 * NH; ++j) {
       const int row = 16 * j + 4 * lg + (q & 3) + 8 * (q >> 2);
       const uint8_t* a = vt + row * ROW + ((chunk ^ sw(row)) << 4) + 8 * (i & 1);
       const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<lds_i32x2*>(
@@ -1855,9 +1865,9 @@ struct Prob8 : Src<D, kKvFp8, true> {
     float m_run = -INFINITY, l_run = 0.f;
     pass(std::false_type{}, [&](int n, const uint8_t* st) {
       f32x16 acc[2];
-      qk(st, qf, acc, lr, lg);
-      if (n < n_full) stats<false>(acc, m_run, l_run, 0, c);
-      else stats<true>(acc, m_run, l_run, lims[t] - (kbeg + n * kBlockN), c);
+      qk<2>(st, qf, acc, lr, lg);
+      if (n < n_full) stats<2, false>(acc, m_run, l_run, 0, c);
+      else stats<2, true>(acc, m_run, l_run, lims[t] - (kbeg + n * kBlockN), c);
     });
     const float l_tot = wave_pair_sum(l_run);
     const bool live = l_tot > 0.f;
@@ -1870,13 +1880,13 @@ struct Prob8 : Src<D, kKvFp8, true> {
       for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
     pass(std::true_type{}, [&](int n, const uint8_t* st) {
       f32x16 acc[2];
-      qk(st, qf, acc, lr, lg);
-      const i32x8 pb = n < n_full ? probs<false>(acc, 0, c, neg2)
-                                  : probs<true>(acc, lims[t] - (kbeg + n * kBlockN), c, neg2);
+      qk<2>(st, qf, acc, lr, lg);
+      const i32x8 pb = n < n_full ? probs<2, false>(acc, 0, c, neg2)
+                                  : probs<2, true>(acc, lims[t] - (kbeg + n * kBlockN), c, neg2);
 #pragma unroll
       for (int d = 0; d < DBLK; ++d)
-        o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread(st + TILE, d, lr, lg), pb, o[d], 0, 0, 0, 0,
-                                                               0, 0);
+        o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread<2>(st + TILE, d, lr, lg), pb, o[d], 0, 0, 0,
+                                                               0, 0, 0);
     });
 
     if (wr1 >= wr0) {
@@ -1888,10 +1898,167 @@ struct Prob8 : Src<D, kKvFp8, true> {
     }
   }
 
+  // ---- decode-mode items (at most 32 packed rows): the eight waves split the
+  //      item's 32-key blocks (wave w takes blocks w, w + 8, ...), each with
+  //      its own two-stage ring of K and V tiles, and no barrier inside the
+  //      loops.  The waves' row maxima and sums (first pass) and their
+  //      partial outputs (second pass) are combined through LDS in a fixed
+  //      order, so the result does not depend on timing.
+  static constexpr int DK = 32;                          // keys per decode-mode block
+  static constexpr int DTILE = DK * ROW;                 // bytes of a K (or V) tile
+  static constexpr int DSTAGE = 2 * DTILE;
+  static constexpr int DCOPIES = DTILE / 1024;           // copies per tile and wave
+  static constexpr int kDecBytes = NW * 2 * DSTAGE;      // the eight waves' rings
+  static constexpr int kCombStride = D + 4;              // fp32 row stride of the output combine
+  static constexpr int kCombBytes = (NW / 2) * kWaveRows * kCombStride * 4;
+  static constexpr int kRingBytes = NS * STAGE > kDecBytes ? (NS * STAGE > kCombBytes ? NS * STAGE : kCombBytes)
+                                                           : (kDecBytes > kCombBytes ? kDecBytes : kCombBytes);
+
+  // copies of the K (and V) rows of keys [kbase, kbase + 32) into a wave's stage
+  template <bool WITH_V>
+  __device__ static __forceinline__ int dstage(const AttnParams& p, const Item& it, uint8_t* st, int kbase,
+                                               int lane) {
+    const char* zeros = static_cast<const char*>(p.zeros);
+#pragma unroll
+    for (int i = 0; i < DCOPIES; ++i) {
+      const int r = i * RPW + lane / CPR;
+      const int c = (lane % CPR) ^ sw(r);
+      const char *kp, *vp;
+      const bool ok = B::template row_src<true>(p, it, kbase + r, kp, vp);
+      dma16<true>(ok ? kp + c * 16 : zeros, reinterpret_cast<uint16_t*>(st + i * RPW * ROW));
+      if constexpr (WITH_V)
+        dma16<true>(ok ? vp + c * 16 : zeros, reinterpret_cast<uint16_t*>(st + DTILE + i * RPW * ROW));
+    }
+    return WITH_V ? 2 * DCOPIES : DCOPIES;
+  }
+
+  __device__ static __forceinline__ void dec_item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq,
+                                                  const Item& it, uint8_t* ring, float* ml, int* lims, float c,
+                                                  float out_scale, int wave, int lr, int lg, int t) {
+    const int lane = t & 63;
+    const int kbeg = item.key_begin;
+    const int q_start = __builtin_amdgcn_readfirstlane(sq.q_start);
+    const bool row_ok = lr < item.nrows;
+    i32x8 qf[KS];
+    int token, qh;
+    load_q8(p, sq, it.kvh, item.row0 + lr, row_ok, lg, qf, token, qh);
+    const int shift = sq.kv_len - sq.q_len;
+    {
+      int lim = it.kend - 1;
+      if (p.causal) lim = min(lim, token + shift);
+      lims[t] = lim - lg * 4;
+    }
+    // keys some row sees: [kbeg, whi]; keys every row sees: [kbeg, wlo]
+    int wlo = it.kend - 1, whi = it.kend - 1;
+    if (p.causal) {
+      wlo = min(wlo, item.row0 / p.g + shift);
+      whi = min(whi, (item.row0 + item.nrows - 1) / p.g + shift);
+    }
+    const int nb = whi < kbeg ? 0 : (whi - kbeg) / DK + 1;
+    const int n_full = max(0, (wlo - kbeg + 1) / DK);
+    uint8_t* const mine = ring + wave * 2 * DSTAGE;
+    // this wave's blocks: the next one is copied while the current one is
+    // computed (its stage was read by the block before, already consumed)
+    auto pass = [&](auto v_tag, auto&& body) {
+      constexpr bool WITH_V = decltype(v_tag)::value;
+      int j = wave;
+      if (j >= nb) return;
+      const int cpb = dstage<WITH_V>(p, it, mine, kbeg + j * DK, lane);
+      for (int i = 0; j < nb; ++i, j += NW) {
+        const bool more = j + NW < nb;
+        if (more) dstage<WITH_V>(p, it, mine + ((i + 1) & 1) * DSTAGE, kbeg + (j + NW) * DK, lane);
+        wait_vmem_upto(more ? cpb : 0);
+        body(j, mine + (i & 1) * DSTAGE);
+      }
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    pass(std::false_type{}, [&](int j, const uint8_t* st) {
+      f32x16 acc[1];
+      qk<1>(st, qf, acc, lr, lg);
+      if (j < n_full) stats<1, false>(acc, m_run, l_run, 0, c);
+      else stats<1, true>(acc, m_run, l_run, lims[t] - (kbeg + j * DK), c);
+    });
+    // the row's maximum and sum over the eight waves (in wave order)
+    const float l_w = wave_pair_sum(l_run);
+    if (lg == 0) {
+      ml[wave * kWaveRows + lr] = m_run;
+      ml[(NW + wave) * kWaveRows + lr] = l_w;
+    }
+    __syncthreads();
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, ml[w * kWaveRows + lr]);
+    float l = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = ml[w * kWaveRows + lr];
+        if (mw != -INFINITY) l += ml[(NW + w) * kWaveRows + lr] * __builtin_amdgcn_exp2f((mw - m) * c);
+      }
+    }
+    const bool live = l > 0.f;
+    const float neg2 = live ? -(m * c + __log2f(l) + p.p_log2) : 0.f;
+
+    f32x16 o[DBLK];
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+    pass(std::true_type{}, [&](int j, const uint8_t* st) {
+      f32x16 acc[1];
+      qk<1>(st, qf, acc, lr, lg);
+      const i32x8 pb = j < n_full ? probs<1, false>(acc, 0, c, neg2)
+                                  : probs<1, true>(acc, lims[t] - (kbeg + j * DK), c, neg2);
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+        o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread<1>(st + DTILE, d, lr, lg), pb, o[d], 0, 0, 0,
+                                                               0, 0, 0);
+    });
+    // partial outputs summed over the waves in a fixed tree: wave w + half
+    // hands its sums to wave w, half = 4, 2, 1
+    float* const so = reinterpret_cast<float*>(ring);
+#pragma unroll
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+      __syncthreads();   // rings, or the previous round's slots, are free
+      if (wave >= half && wave < 2 * half) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            *reinterpret_cast<float4*>(so + ((wave - half) * kWaveRows + lr) * kCombStride + d * 32 + i4 * 8 +
+                                       lg * 4) =
+                make_float4(o[d][i4 * 4], o[d][i4 * 4 + 1], o[d][i4 * 4 + 2], o[d][i4 * 4 + 3]);
+      }
+      __syncthreads();
+      if (wave < half) {
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const float4 f = *reinterpret_cast<const float4*>(so + (wave * kWaveRows + lr) * kCombStride +
+                                                              d * 32 + i4 * 8 + lg * 4);
+            o[d][i4 * 4] += f.x;
+            o[d][i4 * 4 + 1] += f.y;
+            o[d][i4 * 4 + 2] += f.z;
+            o[d][i4 * 4 + 3] += f.w;
+          }
+      }
+    }
+    if (wave == 0) {
+      const float inv = live ? out_scale : 0.f;
+      const float lse_v = live ? m * c * kLn2 + __logf(l) : -INFINITY;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d) B::store_out_block(p, q_start, token, qh, d, o[d], inv, lg, row_ok);
+      if (row_ok && lg == 0 && p.lse) p.lse[static_cast<int64_t>(qh) * p.total_q + q_start + token] = lse_v;
+    }
+  }
+
   __device__ static __forceinline__ void run(const AttnParams& p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRingBytes];
     __shared__ int32_t pids[kMaxItemPages];
     __shared__ int lims[NT];
+    __shared__ float ml[2 * NW * kWaveRows];
     __shared__ typename B::QEntry qbuf[B::kQueueChunk];
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -1900,8 +2067,13 @@ struct Prob8 : Src<D, kKvFp8, true> {
     const int lg = lane >> 5;
     const float c = p.qk_scale_log2;
     const float out_scale = p.v_scale;
-    B::for_each_item(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+    // prefill-mode items first, then decode-mode ones (each body in a pass of
+    // its own keeps the register allocation of the other out of it)
+    B::template for_each_item<0>(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
       item(p, e.item, e.item.s, it, ring, lims, c, out_scale, wave, lr, lg, t);
+    });
+    B::template for_each_item<1>(p, qbuf, pids, t, NT, [&](const typename B::QEntry& e, const Item& it) {
+      dec_item(p, e.item, e.item.s, it, ring, ml, lims, c, out_scale, wave, lr, lg, t);
     });
   }
 };
