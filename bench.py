@@ -382,6 +382,8 @@ def measure_workload(name, args, dev, cpu_budget):
         roof["combined_frac"] = (pre_flops / (PEAK_BF16_TFLOPS * 1e12) + dec_bytes / (PEAK_HBM_GBS * 1e9)) / elapsed
         obj["roofline"] = roof
         del r
+        if not args.no_qkv_prob:
+            obj["qkv_prob"] = measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops)
         if args.no_parts:
             obj["cpu_baseline"] = cpu_baseline(wl, cpu_budget) if cpu_budget > 0 else None
             return obj
@@ -395,8 +397,6 @@ def measure_workload(name, args, dev, cpu_budget):
             del rs
         obj["parts_alone_ms"] = parts
         obj["fused_over_serial"] = m["ms_per_step"] / (parts["prefill_rows"] + parts["decode_rows"])
-        if not args.no_qkv_prob:
-            obj["qkv_prob"] = measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops)
     else:
         obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
