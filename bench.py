@@ -429,7 +429,7 @@ def measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops):
     elapsed = m["ms_per_step"] / 1e3
     ach = pre_flops / (us / 1e6) / 1e12 if us > 0 else 0.0
     roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / PEAK_FP8_TFLOPS, "traffic": None,
+            "frac": ach / PEAK_FP8_TFLOPS, "traffic": load_traffic(f"{wl.name}_qkv_prob"),
             "kernel": "attention (fp8 QKV-Prob grid: every item of the batch in one launch)",
             "kernel_avg_us": us, "kernel_timing": kernel_note(m, args.steps),
             "note": "achieved counts the algorithmic 4 * D FLOPs per visible (query, key) pair of the "
