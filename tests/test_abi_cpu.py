@@ -275,3 +275,28 @@ def test_workspace_bound_host_only():
     assert st == 1 and b"aligned" in lib.vpk_last_error()
     st = lib.vpk_set_workspace(None, ctypes.c_void_p(FAKE), 1024)
     assert st == 1 and b"at least" in lib.vpk_last_error()
+
+
+def test_qkv_prob_errors_before_the_device():
+    lib = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(dims, qp, kv=(0.02, 0.01), cache=FAKE):
+        ks = (ctypes.c_float * 2)(*kv)
+        qps = None if qp is None else (ctypes.c_float * 2)(*qp)
+        st = lib.attn_varlen_paged_qkv_prob_fwd(ctypes.byref(dims), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                                vp(cache), vp(cache), vp(FAKE), vp(FAKE), 16, 1, 0.1, ks, qps, None,
+                                                vp(FAKE), vp(FAKE), ctypes.byref(hi), None)
+        return st, lib.vpk_last_error().decode()
+
+    hi, keep = _host([0, 2, 4], [0, 2, 4], [3, 5])
+    fp8 = _dims(kv_cache_dtype=2)
+    st, msg = call(_dims(kv_cache_dtype=1), (0.01, 1 / 448))
+    assert st == 1 and "fp8" in msg, msg
+    st, msg = call(fp8, (0.01, 1 / 448), cache=None)
+    assert st == 1 and "fp8" in msg, msg
+    assert call(fp8, None) == (1, "qp_scale is NULL")
+    for qp, frag in (((0.0, 1 / 448), "q_scale"), ((float("nan"), 1 / 448), "q_scale"),
+                     ((0.01, 1 / 500), "p_scale"), ((0.01, float("inf")), "p_scale")):
+        st, msg = call(fp8, qp)
+        assert st == 1 and frag in msg, (qp, msg)
