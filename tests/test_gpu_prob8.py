@@ -254,3 +254,33 @@ def test_close_to_plain_fp8_attention():
     err = np.abs(to_np_out(out) - plain["out"])
     say(f"[ok] QKV-Prob against plain fp8-KV attention: max {err.max():.3e} mean {err.mean():.3e}")
     assert err.max() < 0.1 and err.mean() < 1e-2
+
+
+N_FUZZ = 24
+
+
+def _fuzz_spec(i):
+    """Fuzz case i of the dense tier, over an fp8 cache (the QKV-Prob call needs one)."""
+    from test_gpu_fuzz import fuzz_case
+    spec = dict(fuzz_case(i), cache_dtype="fp8", seed=9500 + i)
+    if spec["page_size"] == 0:
+        spec["page_size"] = 16
+    return spec
+
+
+def test_fuzz_specs_reach_the_boundaries():
+    specs = [_fuzz_spec(i) for i in range(N_FUZZ)]
+    assert {s["D"] for s in specs} == {64, 128}
+    assert {s["Hq"] // s["Hkv"] for s in specs} == {1, 4, 8}
+    assert {s["causal"] for s in specs} == {True, False}
+    rows = [q * (s["Hq"] // s["Hkv"]) for s in specs for q in s["q_lens"]]
+    assert 32 in rows and 0 in rows and any(r > 256 for r in rows)
+
+
+@pytest.mark.parametrize("i", range(N_FUZZ))
+def test_fuzz(i):
+    spec = _fuzz_spec(i)
+    wl = make_custom(**spec)
+    p_scale = 1.0 / 448.0 if i % 2 == 0 else 2.0 ** -6
+    _case(wl, f"QKV-Prob fuzz {i} q={spec['q_lens']} new={spec['new_lens']} cache={spec['cache_lens']}",
+          _q_scale(wl), p_scale, with_new=spec["new_lens"] is not None)
