@@ -363,6 +363,10 @@ def measure_workload(name, args, dev, cpu_budget):
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_HBM_GBS
         obj["roofline"] = hbm_roof(dec_bytes, k["decode_grid"][0], load_traffic(name), note)
         obj["roofline"]["merge_avg_us"] = k["merge"][0]
+        # the same kernel against a read bandwidth measured on this GPU in this run
+        ceil = read_ceiling(dev)
+        if ceil:
+            obj["read_ceiling"] = dict(ceil, kernel_frac=obj["roofline"]["achieved"] / ceil["value"])
     elif name == "mixed_fp8":
         obj.update(value=step_flops / elapsed / 1e12, unit="TFLOP/s")
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_BF16_TFLOPS
@@ -458,6 +462,46 @@ def measure_qkv_prob(wl, args, dev, pre_flops, dec_bytes, step_flops):
     return res
 
 
+def read_ceiling(dev, gib=4.0, reps=5):
+    """A read bandwidth measured on this GPU in this run, for the decode figure: a streaming
+    read of a contiguous `gib` GiB buffer (16 times the 256 MB MALL) by the helper library
+    libvpk_measure.so, over several launch shapes, best of `reps` passes each; GB/s of bytes
+    read.  None when the helper is not built."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "varlen_paged_kv_amd", "lib", "libvpk_measure.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.vpk_measure_stream_read.restype = ctypes.c_int
+    lib.vpk_measure_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = int(gib * (1 << 30))
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    shapes = [(2048, 1), (4096, 4), (8192, 4), (16384, 8)]
+    out = torch.empty(max(g for g, _ in shapes) * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best, best_shape = 0.0, None
+    for grid, unroll in shapes:
+        for rep in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = lib.vpk_measure_stream_read(buf.data_ptr(), nbytes, grid, unroll, out.data_ptr(), stream)
+            b.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"stream read launch failed ({rc})")
+            gbs = nbytes / (a.elapsed_time(b) / 1e3) / 1e9
+            if rep > 0 and gbs > best:
+                best, best_shape = gbs, (grid, unroll)
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"value": best, "unit": "GB/s",
+            "how": f"streaming read of a contiguous {gib:g} GiB buffer, 16-byte loads in a grid-stride "
+                   f"loop; best launch shape {best_shape[0]} x 256 threads, {best_shape[1]} loads in flight "
+                   f"per thread, best of {reps}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,7 +569,7 @@ def main():
         "config": head["config"], "pct_of_peak": head["pct_of_peak"], "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
-    for key in ("rope_kernel", "qkv_prob", "parts_alone_ms", "fused_over_serial"):
+    for key in ("rope_kernel", "qkv_prob", "parts_alone_ms", "fused_over_serial", "read_ceiling"):
         if key in head:
             line[key] = head[key]
     for name in names[1:]:

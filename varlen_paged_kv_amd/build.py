@@ -4,7 +4,8 @@
 
 Every source is compiled with hipcc for --offload-arch=gfx950; packed fp32
 instructions are disabled in device code (-packed-fp32-ops).  The library is
-written to varlen_paged_kv_amd/lib/libvpk.so.
+written to varlen_paged_kv_amd/lib/libvpk.so; the benchmark's read-bandwidth
+helper to varlen_paged_kv_amd/lib/libvpk_measure.so.
 """
 from __future__ import annotations
 
@@ -20,6 +21,10 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "lib")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(OUT_DIR, "libvpk.so")
+# a separate helper library for the benchmark's read-bandwidth reference (not
+# part of the attention path; only bench.py loads it)
+MEASURE_LIB = os.path.join(OUT_DIR, "libvpk_measure.so")
+MEASURE_SOURCES = ["measure/read_bw.hip"]
 
 SOURCES = [
     "kernels/attn_fwd.hip",
@@ -63,20 +68,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(OUT_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + MEASURE_SOURCES
+    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], MEASURE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", MEASURE_LIB)
     return LIB
 
 
