@@ -162,6 +162,42 @@ def cpu_baseline(wl, budget_s):
                       f"numpy float64, plus the batch's append pro rata; {elapsed:.1f} s"}
 
 
+class GpuSampler:
+    """Clock and power of the GPU sampled every 5 ms on a host thread while the timed pass
+    runs (torch.cuda.clock_rate / power_draw, which query amd-smi); best effort: None
+    where the query is not available."""
+
+    def __init__(self, torch):
+        self.torch, self.samples, self.stop = torch, [], False
+
+    def _run(self):
+        while not self.stop:
+            try:
+                self.samples.append((self.torch.cuda.clock_rate(), self.torch.cuda.power_draw()))
+            except Exception:
+                return
+            time.sleep(0.005)
+
+    def __enter__(self):
+        import threading
+        self.t = threading.Thread(target=self._run, daemon=True)
+        self.t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        self.t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        clk = sorted(c for c, _ in self.samples)
+        pw = sorted(p for _, p in self.samples)
+        return {"samples": len(self.samples), "sclk_mhz_median": clk[len(clk) // 2], "sclk_mhz_min": clk[0],
+                "power_median": pw[len(pw) // 2], "power_max": pw[-1],
+                "note": "torch.cuda.clock_rate (MHz) and torch.cuda.power_draw (as the driver reports it)"}
+
+
 class Runner:
     """Device copies of one workload's inputs and the timing passes over them."""
 
@@ -297,9 +333,11 @@ class Runner:
                          ("prob8_grid", vpk.KERNEL_ATTENTION_PROB8)):
             ms, n = vpk.timing_read(kid)
             kern[key] = (ms * 1e3 / n if n else 0.0, n)
-        gpu_ms, wall = self.timed(steps, False)
+        with GpuSampler(self.torch) as gs:
+            gpu_ms, wall = self.timed(steps, False)
         return dict(ms_per_step=gpu_ms / steps, host_us_per_step=wall * 1e6 / steps,
-                    inst_us_per_step=inst_ms * 1e3 / steps, kernels=kern, settle_steps=self.settle_steps)
+                    inst_us_per_step=inst_ms * 1e3 / steps, kernels=kern, settle_steps=self.settle_steps,
+                    gpu=gs.summary())
 
 
 def kernel_note(m, steps):
@@ -357,7 +395,8 @@ def measure_workload(name, args, dev, cpu_budget):
     note = kernel_note(m, args.steps)
     elapsed = m["ms_per_step"] / 1e3
     obj = {"workload": name, "ms_per_step": m["ms_per_step"], "config": config_of(wl, step_flops, step_bytes,
-                                                                                      args.rope)}
+                                                                                      args.rope),
+           "gpu_during_timed_pass": m.get("gpu")}
     if name == "paged_decode":
         obj.update(value=step_bytes / elapsed / 1e9, unit="GB/s")
         obj["pct_of_peak"] = 100.0 * obj["value"] / PEAK_HBM_GBS
@@ -569,7 +608,8 @@ def main():
         "config": head["config"], "pct_of_peak": head["pct_of_peak"], "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
-    for key in ("rope_kernel", "qkv_prob", "parts_alone_ms", "fused_over_serial", "read_ceiling"):
+    for key in ("rope_kernel", "qkv_prob", "parts_alone_ms", "fused_over_serial", "read_ceiling",
+                "gpu_during_timed_pass"):
         if key in head:
             line[key] = head[key]
     for name in names[1:]:
