@@ -1862,13 +1862,48 @@ struct Prob8 : Src<D, kKvFp8, true> {
       __syncthreads();   // every wave is done with the ring
     };
 
+    // First pass: K tiles of BK1 = 128 keys (half as many barriers as 64-key
+    // blocks; the pass computes little per key and no output is live yet),
+    // three stages, each wave copying 16 rows of every tile.
+    constexpr int BK1 = 2 * kBlockN;
+    constexpr int TILE1 = BK1 * ROW;
+    constexpr int CP1 = (BK1 / NW) / RPW;                 // copies per wave and tile
+    static_assert(3 * TILE1 <= kRingBytes, "first-pass ring fits");
+    const int nblk1 = it.kend > kbeg ? (it.kend - kbeg + BK1 - 1) / BK1 : 0;
+    const int nb_w1 = (wr1 < wr0 || whi < kbeg) ? 0 : min(nblk1, (whi - kbeg) / BK1 + 1);
+    const int n_full1 = min(nb_w1, max(0, (wlo - kbeg + 1) / BK1));
+    auto st1_of = [&](int j) {
+      return ring + (__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j)) % 3u) * TILE1;
+    };
+    auto stage1 = [&](int j) {
+      const char* zeros = static_cast<const char*>(p.zeros);
+      const int kbase = kbeg + j * BK1;
+      uint8_t* const st = st1_of(j);
+#pragma unroll
+      for (int i = 0; i < CP1; ++i) {
+        const int r0 = (wave * CP1 + i) * RPW;             // first row of this copy
+        const int r = r0 + lane / CPR;
+        const int cc = (lane % CPR) ^ sw(r);
+        const char *kp, *vp;
+        const bool ok = B::template row_src<true>(p, it, kbase + r, kp, vp);
+        dma16<true>(ok ? kp + cc * 16 : zeros, reinterpret_cast<uint16_t*>(st + r0 * ROW));
+      }
+    };
     float m_run = -INFINITY, l_run = 0.f;
-    pass(std::false_type{}, [&](int n, const uint8_t* st) {
-      f32x16 acc[2];
-      qk<2>(st, qf, acc, lr, lg);
-      if (n < n_full) stats<2, false>(acc, m_run, l_run, 0, c);
-      else stats<2, true>(acc, m_run, l_run, lims[t] - (kbeg + n * kBlockN), c);
-    });
+    if (nblk1 > 0) stage1(0);
+    if (nblk1 > 1) stage1(1);
+    for (int n = 0; n < nblk1; ++n) {
+      wait_vmem_upto(n + 1 < nblk1 ? CP1 : 0);
+      __syncthreads();
+      if (n + 2 < nblk1) stage1(n + 2);
+      if (n < nb_w1) {
+        f32x16 acc[4];
+        qk<4>(st1_of(n), qf, acc, lr, lg);
+        if (n < n_full1) stats<4, false>(acc, m_run, l_run, 0, c);
+        else stats<4, true>(acc, m_run, l_run, lims[t] - (kbeg + n * BK1), c);
+      }
+    }
+    __syncthreads();   // every wave is done with the ring
     const float l_tot = wave_pair_sum(l_run);
     const bool live = l_tot > 0.f;
     const float neg2 = live ? -(m_run * c + __log2f(l_tot) + p.p_log2) : 0.f;
