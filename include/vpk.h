@@ -489,6 +489,12 @@ int32_t vpk_abi_version(void);
  *   "plan_upload"      0 = the kernels read a direct call's work list from
  *                      pinned host memory (default); 1 = it is copied into the
  *                      workspace on the call's stream first.
+ *   "plan_log"         1 = print one line per planned call on stderr: units
+ *                      and workgroups of each launch ("q" marks persistent
+ *                      queues), split tiles, partial rows, bytes of plan
+ *                      records and device work memory; 0 = off; -1 (default)
+ *                      = on when the environment variable VPK_LOG is set to
+ *                      a value other than 0 (read at the first call).
  * Returns VPK_ERROR_INVALID_VALUE for an unknown name or value.
  */
 int32_t vpk_set_option(const char* name, int64_t value);

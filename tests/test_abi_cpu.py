@@ -176,6 +176,34 @@ def test_plan_create_errors_before_the_device():
     assert lib.vpk_plan_destroy(None) == 0
 
 
+def test_plan_log(capfd):
+    """Option "plan_log" prints one line per planned call on stderr (the plan is
+    built before any device call, so the line appears here without a GPU)."""
+    lib = _lib.load()
+    assert lib.vpk_set_option(b"plan_log", 2) == 1
+    hi, keep = _host([0, 2, 4], [0, 2, 4], [3, 5])
+    try:
+        assert lib.vpk_set_option(b"plan_log", 1) == 0
+        assert lib.vpk_set_option(b"num_cus", 256) == 0
+        st, msg, h = _plan_create(_dims(), hi)
+        if st == 0:
+            lib.vpk_plan_destroy(h)
+    finally:
+        lib.vpk_set_option(b"plan_log", -1)
+        lib.vpk_set_option(b"num_cus", 0)
+    err = capfd.readouterr().err
+    assert "vpk: plan_create batch=2 q_rows=4 new_rows=4 hq=8 hkv=2 D=128" in err
+    assert "units pre=0 dec=2" in err        # two sequences of 2 tokens x 4 heads per kv head: decode mode
+    assert lib.vpk_set_option(b"plan_log", 0) == 0
+    try:
+        st, msg, h = _plan_create(_dims(), hi)
+        if st == 0:
+            lib.vpk_plan_destroy(h)
+    finally:
+        lib.vpk_set_option(b"plan_log", -1)
+    assert "vpk:" not in capfd.readouterr().err
+
+
 def _list_call(dims, hp, *, q=FAKE, k_new=FAKE, v_new=FAKE, kc=FAKE, vc=FAKE, kvi=FAKE, page_size=16,
                causal=1, scale=0.1, out=FAKE, lse=FAKE):
     lib = _lib.load()

@@ -7,6 +7,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -49,6 +51,7 @@ struct Options {
   std::atomic<int64_t> plan_upload{0};
   std::atomic<int64_t> mixed_grid{-1};
   std::atomic<int64_t> mixed_dec_parts{1};
+  std::atomic<int64_t> plan_log{-1};   // -1: VPK_LOG from the environment
 } g_opt;
 
 // ------------------------------------------------------------------ timing
@@ -500,6 +503,35 @@ struct RopeCopies {
   bool k = false;
 };
 
+// Plan log: one line per planned call on stderr with the plan's shape --
+// units and workgroups of each launch, split tiles, partial rows and the
+// bytes of plan records and device work memory -- to see what the planner
+// made of a batch without a profiler.  On with VPK_LOG=1 in the environment
+// (read at the first call) or option "plan_log" = 1; option 0 turns it off.
+bool plan_log_on() {
+  static const bool env_on = [] {
+    const char* v = std::getenv("VPK_LOG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+  }();
+  const int64_t o = g_opt.plan_log.load();
+  return o < 0 ? env_on : o != 0;
+}
+
+void log_plan(const char* entry, const Plan& p, const vpk_dims* d, size_t plan_bytes, size_t work_bytes) {
+  if (!plan_log_on()) return;
+  auto mode = [](const vpk::Launch& L) { return L.persistent ? "q" : ""; };
+  std::fprintf(stderr,
+               "vpk: %s batch=%d q_rows=%d new_rows=%d hq=%d hkv=%d D=%d | units pre=%d dec=%d | "
+               "workgroups pre=%d%s dec=%d%s one=%d%s (q: persistent queues) | split tiles=%zu part_rows=%lld | "
+               "plan_bytes=%zu device_work_bytes=%zu\n",
+               entry, d->batch, d->total_q, d->total_knew, d->num_q_heads, d->num_kv_heads, d->head_dim,
+               p.prefill.count, p.decode.count, p.prefill.grid, mode(p.prefill), p.decode.grid, mode(p.decode),
+               p.mixed.grid, mode(p.mixed),
+               p.groups.size() / std::max<size_t>(1, static_cast<size_t>(d->num_kv_heads)),
+               static_cast<long long>(p.part_rows), plan_bytes, work_bytes);
+  std::fflush(stderr);
+}
+
 Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dims* rope = nullptr,
                   RopeCopies rc = RopeCopies{}) {
   Layout L;
@@ -938,6 +970,7 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
     }
   }
   const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr, rc);
+  log_plan(c.qp_scale ? "qkv_prob" : "attention", plan, dims, L.plan_end, L.part_end);
   if ((st = get_workspace(stream, L.part_end + (upload ? L.plan_end : 0), &w))) return st;
   int region = 0;
   if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
@@ -1030,6 +1063,7 @@ int32_t plan_and_enqueue_noalloc(const Call& c, const Mirrors& m, int32_t causal
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
   const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim);
+  log_plan("attention_noalloc", plan, dims, L.plan_end, L.part_end);
   const size_t need = kFlagBytes + L.plan_end + L.part_end;
   if (need > vpk::kScratchBytes)
     return fail(VPK_ERROR_CAPACITY, "the call needs " + std::to_string(need) + " bytes of scratch, the "
@@ -1306,6 +1340,7 @@ int32_t plan_create_impl(const vpk_dims* dims, const vpk_host_index* host, int32
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host memory for the plan");
   }
   pl->L = layout_for(pl->plan, B, dims->total_knew, dims->head_dim);
+  log_plan("plan_create", pl->plan, dims, pl->L.plan_end, pl->L.part_end);
   hipError_t e = hipGetDevice(&pl->device);
   if (e != hipSuccess) {
     delete pl;
@@ -1591,6 +1626,9 @@ int32_t vpk_set_option(const char* name, int64_t value) {
   } else if (n == "mixed_grid") {
     if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "mixed_grid must be -1, 0 or 1");
     g_opt.mixed_grid = value;
+  } else if (n == "plan_log") {
+    if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "plan_log must be -1, 0 or 1");
+    g_opt.plan_log = value;
   } else if (n == "num_cus") {
     if (value < 0 || value > 4096) return fail(VPK_ERROR_INVALID_VALUE, "num_cus out of range");
     g_opt.num_cus = value;
