@@ -563,6 +563,8 @@ def main():
     ap.add_argument("--plan-upload", type=int, default=0, help="library option plan_upload (0 or 1)")
     ap.add_argument("--mixed-grid", type=int, default=-2, help="library option mixed_grid (-1, 0 or 1; default: the library's)")
     ap.add_argument("--mixed-dec-parts", type=int, default=0, help="library option mixed_dec_parts (0: the library's)")
+    ap.add_argument("--keep-scores", type=int, default=1,
+                    help="library option keep_scores for the QKV-Prob call (0 or 1)")
     ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
     ap.add_argument("--no-qkv-prob", action="store_true",
                     help="mixed batch: do not also time it through the fp8 QKV-Prob call")
@@ -584,6 +586,7 @@ def main():
         vpk.set_option("mixed_grid", args.mixed_grid)
     if args.mixed_dec_parts > 0:
         vpk.set_option("mixed_dec_parts", args.mixed_dec_parts)
+    vpk.set_option("keep_scores", args.keep_scores)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)

@@ -456,6 +456,20 @@ int32_t vpk_set_workspace(void* stream, void* ptr, size_t bytes);
  */
 size_t vpk_workspace_bytes_upper_bound(const vpk_dims* dims, int32_t num_cus, int32_t rope);
 
+/*
+ * vpk_qkv_prob_score_bytes -- device bytes, beyond the bound above, with which
+ * attn_varlen_paged_qkv_prob_fwd keeps the first-pass scores of its
+ * decode-mode rows in the workspace (sequences of at most 8 packed rows,
+ * q_len * num_q_heads / num_kv_heads, with head_dim 128): 128 bytes per row
+ * and 32 keys of each kv head, a quarter or less of re-reading the K codes in
+ * the second pass.  A workspace without this room gives the same results
+ * (the second pass reads K again).  From the host arrays cu_seqlens_q,
+ * cu_seqlens_knew and cache_seqlens of `host` (the latter two may be NULL:
+ * no new tokens / no cache).  Host only; returns 0 for invalid arguments or
+ * when no row qualifies.
+ */
+size_t vpk_qkv_prob_score_bytes(const vpk_dims* dims, const vpk_host_index* host);
+
 /* Memory the library holds on its own: device bytes of its fallback
  * workspaces (streams without vpk_set_workspace) and pinned host bytes of its
  * plan buffers.  Prepared plans are not counted (each owns its buffer). */
@@ -489,6 +503,10 @@ int32_t vpk_abi_version(void);
  *   "plan_upload"      0 = the kernels read a direct call's work list from
  *                      pinned host memory (default); 1 = it is copied into the
  *                      workspace on the call's stream first.
+ *   "keep_scores"      QKV-Prob calls: 1 (default) = decode-mode rows keep
+ *                      their first-pass scores in the workspace when it has
+ *                      room (vpk_qkv_prob_score_bytes); 0 = the second pass
+ *                      reads K again.  Same results either way.
  *   "plan_log"         1 = print one line per planned call on stderr: units
  *                      and workgroups of each launch ("q" marks persistent
  *                      queues), split tiles, partial rows, bytes of plan

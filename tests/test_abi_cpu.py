@@ -176,6 +176,25 @@ def test_plan_create_errors_before_the_device():
     assert lib.vpk_plan_destroy(None) == 0
 
 
+def test_qkv_prob_score_bytes():
+    """Room for kept QKV-Prob scores: 128 bytes per (row, 32 keys, kv head) of each sequence of at most 8
+    packed rows (head_dim 128 only), plus 256 bytes of alignment; 0 when nothing qualifies."""
+    lib = _lib.load()
+    d = _dims(batch=4, total_q=12, total_knew=12, num_q_heads=8, num_kv_heads=2)          # g = 4
+    hi, keep = _host([0, 1, 3, 11, 12], [0, 1, 3, 11, 12], [100, 31, 0, 5000])
+    # rows 4, 8, 32 (too many), 4; keys 101, 33, -, 5001 -> blocks 4, 2, -, 157
+    want = (4 * 4 + 8 * 2 + 4 * 157) * 2 * 128 + 256
+    assert lib.vpk_qkv_prob_score_bytes(ctypes.byref(d), ctypes.byref(hi)) == want
+    only_new, k2 = _host([0, 1, 3, 11, 12], [0, 1, 3, 11, 12])                            # no cache
+    assert lib.vpk_qkv_prob_score_bytes(ctypes.byref(d), ctypes.byref(only_new)) == (4 + 8 + 4) * 2 * 128 + 256
+    assert lib.vpk_qkv_prob_score_bytes(ctypes.byref(_dims(batch=4, total_q=12, total_knew=12, num_q_heads=8,
+                                                           num_kv_heads=2, head_dim=64)), ctypes.byref(hi)) == 0
+    assert lib.vpk_qkv_prob_score_bytes(ctypes.byref(d), None) == 0
+    assert lib.vpk_set_option(b"keep_scores", 0) == 0
+    assert lib.vpk_set_option(b"keep_scores", 1) == 0
+    assert lib.vpk_set_option(b"keep_scores", 2) == 1
+
+
 def test_plan_log(capfd):
     """Option "plan_log" prints one line per planned call on stderr (the plan is
     built before any device call, so the line appears here without a GPU)."""

@@ -201,6 +201,54 @@ def test_persistent_and_one_workgroup_per_item(persistent):
         vpk.set_option("persistent", -1)
 
 
+def test_kept_scores_equal_a_second_read_of_k():
+    """Decode-mode rows of at most 8 packed rows keep their first-pass scores in the workspace, where the
+    second pass reads them back instead of the K codes; without room (or with option keep_scores 0) the
+    second pass reads K again.  Both recompute nothing differently: the bits must be equal."""
+    wl = make_custom(q_lens=[1, 2, 1, 8, 1, 0], new_lens=[1, 2, 1, 8, 1, 0], cache_lens=[3000, 700, 0, 64, 5000, 9],
+                     Hq=8, Hkv=2, D=128, page_size=16, causal=True, cache_dtype="fp8", seed=4242)
+    q_scale, p_scale = _q_scale(wl), 1.0 / 448.0
+    say(f"[case] kept scores vs K read again: rows 4, 8, 4, 32, 4 per kv head, seed {wl.seed}")
+    runs = {}
+    try:
+        dc = DeviceCall(wl)
+        out, lse = _run(dc, q_scale, p_scale)                 # the binding's workspace holds the scores
+        torch.cuda.synchronize()
+        runs["kept"] = (out.clone(), lse.clone(), dc.cache_host())
+        vpk.set_option("keep_scores", 0)
+        dc = DeviceCall(wl)
+        out, lse = _run(dc, q_scale, p_scale)
+        torch.cuda.synchronize()
+        runs["option off"] = (out.clone(), lse.clone(), dc.cache_host())
+        vpk.set_option("keep_scores", 1)
+        vpk.AUTO_WORKSPACE = False
+        s = torch.cuda.Stream()
+        buf = torch.empty(64 * 1024, dtype=torch.uint8, device="cuda")   # no room for the 300 KB of scores
+        vpk.set_workspace(buf, stream=s)
+        dc = DeviceCall(wl)
+        with torch.cuda.stream(s):
+            out, lse = vpk.attn_varlen_paged_qkv_prob_fwd(
+                dc.q, dc.cu_q, dc.k_new, dc.v_new, dc.cu_kn, dc.k_cache, dc.v_cache, dc.bt, dc.cl, wl.page_size,
+                wl.causal, wl.scale, wl.kv_scale, q_scale=q_scale, p_scale=p_scale, host_index=dc.host, stream=s)
+        s.synchronize()
+        runs["small workspace"] = (out.clone(), lse.clone(), dc.cache_host())
+        vpk.set_workspace(None, stream=s)
+        s.synchronize()
+    finally:
+        vpk.set_option("keep_scores", 1)
+        vpk.AUTO_WORKSPACE = True
+    o0, l0, (k0, v0) = runs["kept"]
+    for name in ("option off", "small workspace"):
+        o, l, (k, v) = runs[name]
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), f"{name}: out differs from kept scores"
+        assert torch.equal(l.view(torch.int32), l0.view(torch.int32)), f"{name}: lse differs from kept scores"
+        assert np.array_equal(k, k0) and np.array_equal(v, v0), f"{name}: cache bytes differ"
+    ref = _oracle(wl, q_scale, p_scale)
+    assert np.array_equal(k0, ref["k_cache"]) and np.array_equal(v0, ref["v_cache"]), "cache bytes"
+    mx, le, fl = check_prob8(to_np_out(o0), l0.cpu().numpy().astype(np.float64), ref, "kept scores")
+    say(f"[ok] kept scores: bitwise equal to K read again (option and small workspace); max err {mx:.2e}")
+
+
 def test_saturating_query_codes():
     """A q_scale below amax / 448: the largest query values saturate at +-448 on both sides."""
     wl = make_custom(q_lens=[50, 1], new_lens=[50, 1], cache_lens=[20, 300], Hq=4, Hkv=2, D=128, page_size=16,

@@ -146,12 +146,13 @@ def library_memory():
     return d.value, h.value
 
 
-def _ensure_workspace(dims: VpkDims, device, stream_handle, rope: bool = False):
-    """Register a torch-allocated workspace of at least the bound for this call's sizes on its stream
-    (grown by replacing it: the old tensor goes back to torch's allocator in the stream's order)."""
+def _ensure_workspace(dims: VpkDims, device, stream_handle, rope: bool = False, extra: int = 0):
+    """Register a torch-allocated workspace of at least the bound for this call's sizes (plus ``extra``
+    bytes) on its stream (grown by replacing it: the old tensor goes back to torch's allocator in the
+    stream's order)."""
     if not AUTO_WORKSPACE:
         return
-    need = workspace_bytes_upper_bound(dims, rope)
+    need = workspace_bytes_upper_bound(dims, rope) + int(extra)
     key = (device.index, stream_handle.value)
     cur = _WORKSPACES.get(key)
     if cur is not None and cur.numel() >= need:
@@ -359,7 +360,16 @@ def _attn_dense(q, cu_seqlens_q, k_new, v_new, cu_seqlens_knew, k_cache, v_cache
         del keep
         _check(st)
         return out, lse
-    _ensure_workspace(dims, q.device, sh, rope is not None)
+    extra = 0
+    if prob8 is not None and AUTO_WORKSPACE:
+        # room for the decode-mode rows' kept scores (from the host lengths)
+        sq = hi
+        if keep[0] is None or (cu_seqlens_knew is not None and keep[1] is None) or \
+                (cache_seqlens is not None and keep[2] is None):
+            lens = [None if t is None else _host_i32(t) for t in (cu_seqlens_q, cu_seqlens_knew, cache_seqlens)]
+            sq = VpkHostIndex(*[None if a is None else a.ctypes.data for a in lens], None)
+        extra = int(lib.vpk_qkv_prob_score_bytes(ctypes.byref(dims), ctypes.byref(sq)))
+    _ensure_workspace(dims, q.device, sh, rope is not None, extra)
     if prob8 is not None:
         qp = (ctypes.c_float * 2)(*prob8)
         st = lib.attn_varlen_paged_qkv_prob_fwd(*args, qp, None if rope is None else ctypes.byref(rope[0]), *tail)

@@ -29,7 +29,7 @@ EXPORTS = (
     "vpk_device_error", "vpk_plan_debug", "vpk_plan_create", "vpk_plan_run", "vpk_plan_device_error",
     "vpk_plan_destroy", "attn_varlen_paged_list_fwd", "attn_varlen_paged_rope_fwd",
     "vpk_plan_run_device_scale", "vpk_set_workspace", "vpk_workspace_bytes_upper_bound", "vpk_library_memory",
-    "attn_varlen_paged_fwd_noalloc", "attn_varlen_paged_qkv_prob_fwd",
+    "attn_varlen_paged_fwd_noalloc", "attn_varlen_paged_qkv_prob_fwd", "vpk_qkv_prob_score_bytes",
 )
 
 
@@ -129,6 +129,8 @@ def load() -> ctypes.CDLL:
     lib.vpk_set_workspace.argtypes = [vp, vp, ctypes.c_size_t]
     lib.vpk_workspace_bytes_upper_bound.restype = ctypes.c_size_t
     lib.vpk_workspace_bytes_upper_bound.argtypes = [P(VpkDims), i32, i32]
+    lib.vpk_qkv_prob_score_bytes.restype = ctypes.c_size_t
+    lib.vpk_qkv_prob_score_bytes.argtypes = [P(VpkDims), P(VpkHostIndex)]
     lib.vpk_library_memory.restype = i32
     lib.vpk_library_memory.argtypes = [P(ctypes.c_size_t), P(ctypes.c_size_t)]
     _lib = lib

@@ -52,6 +52,7 @@ struct Options {
   std::atomic<int64_t> mixed_grid{-1};
   std::atomic<int64_t> mixed_dec_parts{1};
   std::atomic<int64_t> plan_log{-1};   // -1: VPK_LOG from the environment
+  std::atomic<int64_t> keep_scores{1};
 } g_opt;
 
 // ------------------------------------------------------------------ timing
@@ -490,7 +491,8 @@ int64_t part_rows_fitting(size_t bytes, const vpk_dims* d, int32_t num_cus, bool
 //   [seqs][new tokens: sequence, position][units][merge groups][queue starts][queue work]
 // Partials area (device memory): [part_o fp32 rows x D][part_lse fp32 rows]
 struct Layout {
-  size_t seqs, tok, items, groups, queues, work, qpos, kpos, plan_end, part_o, part_lse, rot_q, rot_k, part_end;
+  size_t seqs, tok, items, groups, queues, work, qpos, kpos, plan_end, part_o, part_lse, rot_q, rot_k, scores,
+      part_end;
 };
 
 // Rotary embedding (`rope` set): the positions of the query rows and new
@@ -502,6 +504,11 @@ struct RopeCopies {
   bool q = false;
   bool k = false;
 };
+
+// QKV-Prob decode-mode units of at most this many rows keep their scores
+// between the two passes (above it, storing and reloading them moves more
+// bytes than reading the K codes again)
+constexpr int32_t kKeepScoreRows = 8;
 
 // Plan log: one line per planned call on stderr with the plan's shape --
 // units and workgroups of each launch, split tiles, partial rows and the
@@ -533,7 +540,7 @@ void log_plan(const char* entry, const Plan& p, const vpk_dims* d, size_t plan_b
 }
 
 Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dims* rope = nullptr,
-                  RopeCopies rc = RopeCopies{}) {
+                  RopeCopies rc = RopeCopies{}, size_t score_bytes = 0) {
   Layout L;
   L.seqs = 0;
   L.tok = align_up(L.seqs + sizeof(SeqInfo) * B, 64);
@@ -550,7 +557,8 @@ Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dim
   L.rot_q = align_up(L.part_lse + sizeof(float) * static_cast<size_t>(p.part_rows), 256);
   const size_t hq = rope ? static_cast<size_t>(rope->num_q_heads) : 0, hkv = rope ? static_cast<size_t>(rope->num_kv_heads) : 0;
   L.rot_k = align_up(L.rot_q + (rc.q ? 2 * tq * hq * D : 0), 256);
-  L.part_end = align_up(L.rot_k + (rc.k ? 2 * tn * hkv * D : 0), 256);
+  L.scores = align_up(L.rot_k + (rc.k ? 2 * tn * hkv * D : 0), 256);
+  L.part_end = align_up(L.scores + score_bytes, 256);
   return L;
 }
 
@@ -792,6 +800,7 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       a.v_scale = static_cast<float>(static_cast<double>(c.qp_scale[1]) * static_cast<double>(kv_scale[1]));
       a.kv_scale_dev = nullptr;
       a.q_inv_scale = 1.0f / c.qp_scale[0];
+      a.scores = reinterpret_cast<float*>(PA + L.scores);
       a.p_log2 = static_cast<float>(std::log2(static_cast<double>(c.qp_scale[1])));
       a.rope = vpk::RopeArgs{};
       int rc;
@@ -942,6 +951,25 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   if (c.qp_scale && !plan.groups.empty())
     return fail(VPK_ERROR_NOT_SUPPORTED, "QKV-Prob attention: a sequence's keys span more than " +
                                              std::to_string(vpk::kMaxItemPages - 1) + " pages");
+  // QKV-Prob: decode-mode units of at most kKeepScoreRows rows keep their
+  // first-pass scores in the work memory (8 * rows bytes per key over both
+  // passes, against re-reading 128-byte K rows); `part` / `part_stride` give
+  // each (unit, kv head) its place in 128-byte units (one row of a 32-key block)
+  size_t score_bytes = 0;
+  if (c.qp_scale && dims->head_dim == 128 && g_opt.keep_scores.load() != 0) {
+    int64_t units = 0;
+    for (size_t i = static_cast<size_t>(plan.num_pre_units); i < plan.items.size(); ++i) {
+      WorkItem& it = plan.items[i];
+      if (it.nrows > kKeepScoreRows) continue;
+      const int64_t nb = it.key_end > it.key_begin ? (it.key_end - it.key_begin + 31) / 32 : 0;
+      const int64_t per_head = nb * it.nrows;
+      if (units + per_head * dims->num_kv_heads > INT32_MAX) break;
+      it.part = static_cast<int32_t>(units);
+      it.part_stride = static_cast<int32_t>(per_head);
+      units += per_head * dims->num_kv_heads;
+    }
+    score_bytes = static_cast<size_t>(units) * 128;
+  }
   // Rotary embedding: the attention kernels turn the query rows as they load
   // them (interleaved pairs, or half-split pairs whose two chunks one lane
   // holds: rotary_dim a multiple of 32); with an fp8 cache the append, which
@@ -969,7 +997,13 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
       rc.k = k_new != nullptr && dims->total_knew > 0;
     }
   }
-  const Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr, rc);
+  Layout L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr, rc, score_bytes);
+  if (score_bytes && w->user && kFlagBytes + L.part_end + (upload ? L.plan_end : 0) > w->user_bytes) {
+    // the caller's workspace does not hold the scores: read K again instead
+    for (size_t i = static_cast<size_t>(plan.num_pre_units); i < plan.items.size(); ++i) plan.items[i].part = -1;
+    score_bytes = 0;
+    L = layout_for(plan, B, dims->total_knew, dims->head_dim, rope ? dims : nullptr, rc, 0);
+  }
   log_plan(c.qp_scale ? "qkv_prob" : "attention", plan, dims, L.plan_end, L.part_end);
   if ((st = get_workspace(stream, L.part_end + (upload ? L.plan_end : 0), &w))) return st;
   int region = 0;
@@ -1592,6 +1626,24 @@ int32_t vpk_library_memory(size_t* device_bytes, size_t* pinned_bytes) {
   return VPK_SUCCESS;
 }
 
+size_t vpk_qkv_prob_score_bytes(const vpk_dims* dims, const vpk_host_index* host) {
+  if (!dims || !host || !host->cu_seqlens_q || dims->batch < 0 || dims->num_kv_heads <= 0 ||
+      dims->num_q_heads <= 0 || dims->num_q_heads % dims->num_kv_heads != 0 || dims->head_dim != 128)
+    return 0;
+  const int64_t g = dims->num_q_heads / dims->num_kv_heads;
+  int64_t units = 0;
+  for (int32_t b = 0; b < dims->batch; ++b) {
+    const int64_t rows = (static_cast<int64_t>(host->cu_seqlens_q[b + 1]) - host->cu_seqlens_q[b]) * g;
+    if (rows <= 0 || rows > kKeepScoreRows) continue;
+    int64_t kv = host->cache_seqlens ? std::max<int32_t>(host->cache_seqlens[b], 0) : 0;
+    if (host->cu_seqlens_knew) kv += std::max<int64_t>(0, static_cast<int64_t>(host->cu_seqlens_knew[b + 1]) -
+                                                            host->cu_seqlens_knew[b]);
+    units += (kv + 31) / 32 * rows;
+  }
+  if (units == 0) return 0;
+  return static_cast<size_t>(units) * dims->num_kv_heads * 128 + 256;
+}
+
 size_t vpk_workspace_bytes_upper_bound(const vpk_dims* dims, int32_t num_cus, int32_t rope) {
   if (!dims || dims->batch < 0 || dims->total_q < 0 || dims->total_knew < 0 || dims->num_kv_heads <= 0 ||
       dims->num_q_heads <= 0 || dims->head_dim <= 0 || dims->num_q_heads % dims->num_kv_heads != 0)
@@ -1626,6 +1678,9 @@ int32_t vpk_set_option(const char* name, int64_t value) {
   } else if (n == "mixed_grid") {
     if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "mixed_grid must be -1, 0 or 1");
     g_opt.mixed_grid = value;
+  } else if (n == "keep_scores") {
+    if (value < 0 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "keep_scores must be 0 or 1");
+    g_opt.keep_scores = value;
   } else if (n == "plan_log") {
     if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "plan_log must be -1, 0 or 1");
     g_opt.plan_log = value;

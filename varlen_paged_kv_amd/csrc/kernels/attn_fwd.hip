@@ -1967,6 +1967,39 @@ struct Prob8 : Src<D, kKvFp8, true> {
     return WITH_V ? 2 * DCOPIES : DCOPIES;
   }
 
+  // Decode-mode items of few rows keep their first-pass scores (fp32, in the
+  // device work memory) instead of reading K again in the second pass.  The
+  // item's block j (32 keys) holds nrows * 32 floats from float j * nrows * 32
+  // on; a lane (lr, lg) of a valid row stores its 16 accumulator values there
+  // as four 16-byte pieces, piece i4 at float 4 * (2 nrows i4 + nrows lg + lr),
+  // so each store instruction writes one contiguous run.  The two passes then
+  // move 8 * nrows bytes per key instead of the 128 bytes of a K code row.
+  static constexpr int kScoreCopies = 4;                 // 16-byte pieces per lane and block
+  __device__ static __forceinline__ float* score_at(float* sbase, int j, int nrows, int i4, int lr, int lg) {
+    return sbase + static_cast<int64_t>(j) * nrows * 32 + (i4 * 2 * nrows + lg * nrows + lr) * 4;
+  }
+  // second pass with kept scores: this wave's scores of block j into the K
+  // half of the stage (lane l's piece i4 at 1024 i4 + 16 l: only the lane
+  // that stored it reads it back), the V rows into the V half
+  __device__ static __forceinline__ int sstage(const AttnParams& p, const Item& it, uint8_t* st, float* sbase,
+                                               int j, int nrows, bool row_ok, int kbase, int lane) {
+    const char* zeros = static_cast<const char*>(p.zeros);
+    const int lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+    for (int i4 = 0; i4 < kScoreCopies; ++i4)
+      dma16<true>(row_ok ? static_cast<const void*>(score_at(sbase, j, nrows, i4, lr, lg)) : zeros,
+                  reinterpret_cast<uint16_t*>(st + i4 * 1024));
+#pragma unroll
+    for (int i = 0; i < DCOPIES; ++i) {
+      const int r = i * RPW + lane / CPR;
+      const int c = (lane % CPR) ^ sw(r);
+      const char *kp, *vp;
+      const bool ok = B::template row_src<true>(p, it, kbase + r, kp, vp);
+      dma16<true>(ok ? vp + c * 16 : zeros, reinterpret_cast<uint16_t*>(st + DTILE + i * RPW * ROW));
+    }
+    return kScoreCopies + DCOPIES;
+  }
+
   __device__ static __forceinline__ void dec_item(const AttnParams& p, const WorkItem& item, const SeqInfo& sq,
                                                   const Item& it, uint8_t* ring, float* ml, int* lims, float c,
                                                   float out_scale, int wave, int lr, int lg, int t) {
@@ -1992,25 +2025,42 @@ struct Prob8 : Src<D, kKvFp8, true> {
     const int nb = whi < kbeg ? 0 : (whi - kbeg) / DK + 1;
     const int n_full = max(0, (wlo - kbeg + 1) / DK);
     uint8_t* const mine = ring + wave * 2 * DSTAGE;
+    // scores kept between the passes (the host gives such items a place)
+    const int nrows = __builtin_amdgcn_readfirstlane(item.nrows);
+    const int spart = __builtin_amdgcn_readfirstlane(item.part);
+    const bool keep = D == 128 && spart >= 0;
+    float* const sbase = p.scores + static_cast<int64_t>(spart < 0 ? 0 : spart) * 32;
     // this wave's blocks: the next one is copied while the current one is
-    // computed (its stage was read by the block before, already consumed)
-    auto pass = [&](auto v_tag, auto&& body) {
-      constexpr bool WITH_V = decltype(v_tag)::value;
+    // computed (its stage was read by the block before, already consumed).
+    // `stage_fn` issues a block's copies and returns their count; `extra` is
+    // the number of stores each body issues (in flight behind the next
+    // block's copies, which complete in issue order after them)
+    auto pass = [&](auto&& stage_fn, int extra, auto&& body) {
       int j = wave;
       if (j >= nb) return;
-      const int cpb = dstage<WITH_V>(p, it, mine, kbeg + j * DK, lane);
+      const int cpb = stage_fn(mine, j);
       for (int i = 0; j < nb; ++i, j += NW) {
         const bool more = j + NW < nb;
-        if (more) dstage<WITH_V>(p, it, mine + ((i + 1) & 1) * DSTAGE, kbeg + (j + NW) * DK, lane);
-        wait_vmem_upto(more ? cpb : 0);
+        if (more) stage_fn(mine + ((i + 1) & 1) * DSTAGE, j + NW);
+        wait_vmem_upto((more ? cpb : 0) + (i > 0 ? extra : 0));
         body(j, mine + (i & 1) * DSTAGE);
       }
     };
+    auto stage_k = [&](uint8_t* st, int j) { return dstage<false>(p, it, st, kbeg + j * DK, lane); };
+    auto stage_kv = [&](uint8_t* st, int j) { return dstage<true>(p, it, st, kbeg + j * DK, lane); };
 
     float m_run = -INFINITY, l_run = 0.f;
-    pass(std::false_type{}, [&](int j, const uint8_t* st) {
+    pass(stage_k, keep ? kScoreCopies : 0, [&](int j, const uint8_t* st) {
       f32x16 acc[1];
       qk<1>(st, qf, acc, lr, lg);
+      if constexpr (D == 128) {
+        if (keep && row_ok) {
+#pragma unroll
+          for (int i4 = 0; i4 < kScoreCopies; ++i4)
+            *reinterpret_cast<float4*>(score_at(sbase, j, nrows, i4, lr, lg)) =
+                make_float4(acc[0][4 * i4], acc[0][4 * i4 + 1], acc[0][4 * i4 + 2], acc[0][4 * i4 + 3]);
+        }
+      }
       if (j < n_full) stats<1, false>(acc, m_run, l_run, 0, c);
       else stats<1, true>(acc, m_run, l_run, lims[t] - (kbeg + j * DK), c);
     });
@@ -2040,16 +2090,42 @@ struct Prob8 : Src<D, kKvFp8, true> {
     for (int d = 0; d < DBLK; ++d)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    pass(std::true_type{}, [&](int j, const uint8_t* st) {
-      f32x16 acc[1];
-      qk<1>(st, qf, acc, lr, lg);
+    auto pv = [&](int j, const uint8_t* st, const f32x16 (&acc)[1]) {
       const i32x8 pb = j < n_full ? probs<1, false>(acc, 0, c, neg2)
                                   : probs<1, true>(acc, lims[t] - (kbeg + j * DK), c, neg2);
 #pragma unroll
       for (int d = 0; d < DBLK; ++d)
         o[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vread<1>(st + DTILE, d, lr, lg), pb, o[d], 0, 0, 0,
                                                                0, 0, 0);
-    });
+    };
+    bool kept = false;
+    if constexpr (D == 128) {
+      if (keep) {
+        kept = true;
+        wait_vmem();   // this lane's score stores are complete before it copies them back
+        auto stage_sv = [&](uint8_t* st, int j) {
+          return sstage(p, it, st, sbase, j, nrows, row_ok, kbeg + j * DK, lane);
+        };
+        pass(stage_sv, 0, [&](int j, const uint8_t* st) {
+          f32x16 acc[1];
+#pragma unroll
+          for (int i4 = 0; i4 < kScoreCopies; ++i4) {
+            const u32x4 x = B::template lds_read<u32x4>(
+                B::lds_addr(reinterpret_cast<const uint16_t*>(st + i4 * 1024 + lane * 16)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[0][4 * i4 + e] = __uint_as_float(x[e]);
+          }
+          pv(j, st, acc);
+        });
+      }
+    }
+    if (!kept) {
+      pass(stage_kv, 0, [&](int j, const uint8_t* st) {
+        f32x16 acc[1];
+        qk<1>(st, qf, acc, lr, lg);
+        pv(j, st, acc);
+      });
+    }
     // partial outputs summed over the waves in a fixed tree: wave w + half
     // hands its sums to wave w, half = 4, 2, 1
     float* const so = reinterpret_cast<float*>(ring);

@@ -142,6 +142,10 @@ struct AttnParams {
   // the product p_scale * v_scale)
   float q_inv_scale;          // fp32(1 / q_scale): the query rows' quantiser
   float p_log2;               // log2(p_scale)
+  // decode-mode items whose `part` is >= 0 keep their first-pass fp32 scores
+  // here, from float 32 * (part + kv head * part_stride) on (32 per block
+  // of 32 keys and row)
+  float* scores;
 };
 
 
