@@ -563,6 +563,8 @@ def main():
     ap.add_argument("--plan-upload", type=int, default=0, help="library option plan_upload (0 or 1)")
     ap.add_argument("--mixed-grid", type=int, default=-2, help="library option mixed_grid (-1, 0 or 1; default: the library's)")
     ap.add_argument("--mixed-dec-parts", type=int, default=0, help="library option mixed_dec_parts (0: the library's)")
+    ap.add_argument("--force-splits", type=int, default=0,
+                    help="library option force_splits: every tile's key range in this many parts (0: the planner's)")
     ap.add_argument("--keep-scores", type=int, default=1,
                     help="library option keep_scores for the QKV-Prob call (0 or 1)")
     ap.add_argument("--rope", action="store_true", help="rotary embedding of q and k_new in every step")
@@ -587,6 +589,7 @@ def main():
     if args.mixed_dec_parts > 0:
         vpk.set_option("mixed_dec_parts", args.mixed_dec_parts)
     vpk.set_option("keep_scores", args.keep_scores)
+    vpk.set_option("force_splits", args.force_splits)
 
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
