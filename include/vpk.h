@@ -277,8 +277,12 @@ int32_t attn_varlen_paged_rope_fwd(const vpk_dims* dims,
  *   P codes      pc_ij = e4m3fn(P_ij / p_scale), nearest, ties to even;
  *   output       out_i = p_scale * v_scale * sum_j pc_ij vc_j (bf16, round to
  *                nearest even), not renormalised; lse as above.
- * The kernel reads each row's keys twice (once for the row maximum and sum,
- * once for P and the second product) and never splits a key range.
+ * Each row's scores are formed twice (once for the row maximum and sum,
+ * once for P and the second product) and no key range is split.  Sequences
+ * of at most 8 packed rows (head_dim 128) keep their first-pass scores in
+ * the workspace when it has room (vpk_qkv_prob_score_bytes; option
+ * "keep_scores"), so their second pass reads the scores instead of the K
+ * codes; the results are the same either way.
  *   kv_scale  host float[2] {k_scale, v_scale}, required (fp8 cache only).
  *   qp_scale  host float[2] {q_scale, p_scale}: q_scale finite and > 0;
  *             p_scale finite and >= 1/452 (P <= 1, so P / p_scale stays
