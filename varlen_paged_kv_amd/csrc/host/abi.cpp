@@ -417,6 +417,14 @@ int32_t device_cus() {
   return n;
 }
 
+// fp8 cache, head_dim 128, new tokens, keys not turned: the decode-mode items
+// may form and store their sequences' new token codes themselves (the group
+// size g is returned; 0: the standalone append stores every new token)
+int32_t dec_append_g(const Call& c, bool key_rope) {
+  if (!c.fp8 || !c.has_cache || !c.has_new || c.qp_scale || key_rope || c.d->head_dim != 128) return 0;
+  return c.d->num_q_heads / c.d->num_kv_heads;
+}
+
 void fill_plan_input(const Call& c, const Mirrors& m, int32_t causal, int32_t num_cus, PlanInput& in) {
   in.batch = c.d->batch;
   in.hq = c.d->num_q_heads;
@@ -567,6 +575,26 @@ Layout layout_for(const Plan& p, int32_t B, int32_t Tn, int32_t D, const vpk_dim
 // index of that position's page id (the sequence's first index + pos / S)
 // and the slot pos % S, so an append workgroup finds its tokens' slots with
 // one read each.
+// A decode-mode sequence (0 < q_len * g <= 32 packed rows) of a call whose
+// decode-mode items store their own new tokens (dec_g > 0: the group size).
+bool dec_stores_own(const SeqInfo& s, int32_t dec_g) {
+  return dec_g > 0 && s.q_len > 0 && static_cast<int64_t>(s.q_len) * dec_g <= vpk::kWaveRows;
+}
+
+// The group size for a plan of decode-mode units only in which every
+// sequence with new tokens is such a decode-mode sequence, else 0: the
+// decode-mode items then store all new tokens and the standalone append is
+// not launched (so its records need no change).  (Forming the codes in the item that reads them puts a
+// dependent read of the new rows into that item's last block; on the mixed
+// fp8 batch, whose prefill-mode tokens still need the append first, that
+// cost more than it saved.)
+int32_t dec_own_g(const Plan& p, int32_t dec_g) {
+  if (dec_g <= 0 || p.num_pre_units > 0) return 0;
+  for (const SeqInfo& s : p.seqs)
+    if (s.new_len > 0 && !dec_stores_own(s, dec_g)) return 0;
+  return dec_g;
+}
+
 void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B, int32_t page_size,
                     char* base) {
   if (B) std::memcpy(base + L.seqs, p.seqs.data(), sizeof(SeqInfo) * B);
@@ -718,7 +746,13 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
   char* const R = bs.R;
   char* const PA = bs.PA;
   int32_t st;
-  const bool do_append = c.has_cache && c.has_new && dims->total_knew > 0;
+  const int32_t dec_g = dec_own_g(plan, dec_append_g(c, rk.dim > 0));
+  // tokens left to the standalone append (decode-mode items store their own)
+  int64_t append_tokens = 0;
+  if (c.has_cache && c.has_new)
+    for (const SeqInfo& sq : plan.seqs)
+      if (!dec_stores_own(sq, dec_g)) append_tokens += sq.new_len;
+  const bool do_append = append_tokens > 0;
   AppendParams ap = append_params(c, bs.head, R, L, k_new, v_new, k_cache, v_cache, block_table);
   ap.rope = rk;
   ap.kpos = reinterpret_cast<const int32_t*>(R + L.kpos);
@@ -752,6 +786,7 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
     p.k_new = k_new;
     p.v_new = v_new;
     p.new_direct = new_direct ? 1 : 0;
+    p.dec_append = dec_g > 0 ? 1 : 0;
     p.block_table = block_table;
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;

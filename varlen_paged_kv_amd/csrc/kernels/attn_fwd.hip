@@ -850,6 +850,54 @@ struct Src {
       dma16<true>(ok ? (V_ROWS ? vp : kp) + c * 16 : zeros, reinterpret_cast<uint16_t*>(region + i * 8 * F8ROW));
     }
   }
+  // New tokens among keys [kbase, kbase + 64) of an fp8 decode-mode block
+  // (AttnParams::dec_append): after the block's copies have landed, each lane
+  // replaces the 16 codes its copy brought for such a row (the slot the
+  // append would fill, not yet written) by the codes of k_new / v_new under
+  // the append's encoder, in LDS and in the cache.  Rows on an unusable page
+  // keep the zeros their copy read, as with the standalone append.
+  __device__ static __forceinline__ void dec_new8(const AttnParams& p, const Item& it, uint8_t* rk, uint8_t* rv,
+                                                  int kbase, int lane) {
+    using append_detail::enc2;
+    if (kbase + 64 <= it.cache_len) return;
+    float k_inv = p.app.k_inv_scale, v_inv = p.app.v_inv_scale;
+    if (p.app.kv_scale_dev) {
+      k_inv = 1.0f / p.app.kv_scale_dev[0];
+      v_inv = 1.0f / p.app.kv_scale_dev[1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 8 + (lane >> 3);
+      const int key = kbase + r;
+      if (key < it.cache_len || key >= it.kend) continue;
+      const int c = (lane & 7) ^ f8swz(r);
+      const uint32_t pi = static_cast<uint32_t>(key) / static_cast<uint32_t>(p.page_size);
+      const int page = it.pids[pi - it.first_page];
+      if (page < 0) continue;
+      const int64_t tok = it.kn_start + key - it.cache_len;
+      const char* ks = it.knb + tok * it.new_row_bytes + c * 32;
+      const char* vs = it.vnb + tok * it.new_row_bytes + c * 32;
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(ks), k1 = *reinterpret_cast<const u32x4*>(ks + 16);
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(vs), v1 = *reinterpret_cast<const u32x4*>(vs + 16);
+      u32x4 kc, vc;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        kc[e] = enc2(k0[2 * e], k_inv) | (enc2(k0[2 * e + 1], k_inv) << 16);
+        kc[2 + e] = enc2(k1[2 * e], k_inv) | (enc2(k1[2 * e + 1], k_inv) << 16);
+        vc[e] = enc2(v0[2 * e], v_inv) | (enc2(v0[2 * e + 1], v_inv) << 16);
+        vc[2 + e] = enc2(v1[2 * e], v_inv) | (enc2(v1[2 * e + 1], v_inv) << 16);
+      }
+      // the LDS slot this lane's copy of row r filled
+      *reinterpret_cast<u32x4*>(rk + i * 8 * F8ROW + lane * 16) = kc;
+      *reinterpret_cast<u32x4*>(rv + i * 8 * F8ROW + lane * 16) = vc;
+      const uint32_t slot = static_cast<uint32_t>(key) - pi * static_cast<uint32_t>(p.page_size);
+      const int64_t off = (static_cast<int64_t>(page) * p.page_size + slot) * p.app.row_elems +
+                          static_cast<int64_t>(it.kvh) * D + c * 16;
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.app.k_cache) + off) = kc;
+      *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.app.v_cache) + off) = vc;
+    }
+    wait_lds();   // the rows' codes are in LDS before the block is read
+  }
   __device__ static __forceinline__ bf16x8 widen8(uint32_t c0, uint32_t c1) {
     u32x4 w;
     uint32_t a, b, x, y;
@@ -1002,7 +1050,9 @@ __device__ __forceinline__ void scales(const AttnParams& p, float& qk, float& vs
 
 // NWV: waves of the workgroup (4 in the decode-mode grid; 8 when a decode-mode
 // item runs in the 512-thread workgroup of the mixed grid)
-template <int D, int FMT, bool PAGED, bool ROPE, int NWV = kWaves>
+// DECAPP: the item forms and stores the new tokens its fp8 blocks hold
+// (AttnParams::dec_append; head_dim 128, keys not turned)
+template <int D, int FMT, bool PAGED, bool ROPE, int NWV = kWaves, bool DECAPP = false>
 struct Decode : Src<D, FMT, PAGED> {
   using B = Src<D, FMT, PAGED>;
   using C = Cfg<D>;
@@ -1113,6 +1163,7 @@ struct Decode : Src<D, FMT, PAGED> {
         B::template dma_raw8<false>(p, it, rk, kbase, lane);
         B::template dma_raw8<true>(p, it, rv, kbase, lane);
         wait_vmem();
+        if constexpr (DECAPP && !ROPE) B::dec_new8(p, it, rk, rv, kbase, lane);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int j32 = 2 * jb + hh;
@@ -2197,9 +2248,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_prob8_kernel(const
 // ROPE: the query rows are turned by rotary embedding as they are loaded
 // (separate instantiations, so that the other kernels' register allocation
 // does not carry the rotation code)
-template <int D, int FMT, bool PAGED, bool ROPE>
+template <int D, int FMT, bool PAGED, bool ROPE, bool DECAPP = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(const AttnParams p) {
-  Decode<D, FMT, PAGED, ROPE>::run(p);
+  Decode<D, FMT, PAGED, ROPE, kWaves, DECAPP>::run(p);
 }
 
 template <int D, int FMT, bool PAGED, bool ROPE>
@@ -2214,7 +2265,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 1) void attn_mixed_kernel(const
 
 template <int D, int FMT, bool PAGED, bool ROPE>
 int launch_t(const AttnParams& p, int grid, int mode, hipStream_t s) {
-  if (mode == kGridDecode)
+  if (mode == kGridDecode && p.dec_append) {
+    // (the host sets dec_append only for fp8 caches with head_dim 128 and unturned keys)
+    if constexpr (FMT == kKvFp8 && PAGED && D == 128 && !ROPE)
+      hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED, ROPE, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else
+      return static_cast<int>(hipErrorInvalidValue);
+  } else if (mode == kGridDecode)
     hipLaunchKernelGGL((attn_decode_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kThreads), 0, s, p);
   else if (mode == kGridMixed)
     hipLaunchKernelGGL((attn_mixed_kernel<D, FMT, PAGED, ROPE>), dim3(grid), dim3(kPrefillWaves * 64), 0, s, p);

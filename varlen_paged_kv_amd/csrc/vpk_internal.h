@@ -122,6 +122,10 @@ struct AttnParams {
   int32_t num_pre_units;      // units of this launch below this index run in prefill mode
   int32_t persistent;
   int32_t new_direct;         // keys >= cache_len come from k_new / v_new (bf16 cache)
+  // fp8 cache, decode-mode items (head_dim 128): the new tokens' codes are
+  // formed from k_new / v_new by the item that reads them, which also stores
+  // them into the cache (the standalone append skips those tokens)
+  int32_t dec_append;
   int32_t attn_blocks;        // workgroups past this index run the append instead
   int32_t max_pages;
   int32_t num_pages;
