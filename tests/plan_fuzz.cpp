@@ -1,4 +1,4 @@
-// Host-only fuzz driver for the work planner (csrc/host/plan.cpp), built with
+// Host-only fuzz harness for the work planner (csrc/host/plan.cpp), built with
 // AddressSanitizer and UndefinedBehaviorSanitizer by tests/test_plan_sanitize.py
 // (g++, no GPU code).  Seeded random batches, edge lengths included, every
 // planner knob; after each plan it checks, from the inputs alone:
