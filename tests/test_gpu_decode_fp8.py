@@ -117,3 +117,28 @@ def test_decode_page_guard():
     check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref_out, ref_lse, "fp8",
                     label="fp8 decode page guard")
     say("[ok] fp8 decode page guard: flagged, dropped, read as zero")
+
+
+def test_device_scales():
+    """A prepared run with the scales in device memory: bitwise the direct call with the same scales on
+    the host (the decode-mode items form the reciprocals of the device scales as the append does)."""
+    wl = _wl(CASES[1], seed=401)
+    ks = (np.asarray(wl.kv_scale, np.float32) * np.float32(1.25)).astype(np.float32)
+    dd = DeviceCall(wl)
+    out, lse = vpk.attn_varlen_paged_fwd(dd.q, dd.cu_q, dd.k_new, dd.v_new, dd.cu_kn, dd.k_cache, dd.v_cache,
+                                         dd.bt, dd.cl, wl.page_size, wl.causal, wl.scale,
+                                         (float(ks[0]), float(ks[1])), host_index=dd.host)
+    torch.cuda.synchronize()
+    dp = DeviceCall(wl)
+    plan = vpk.Plan(wl.cu_seqlens_q, wl.Hq, wl.Hkv, wl.D, cu_seqlens_knew=wl.cu_seqlens_knew,
+                    cache_seqlens=wl.cache_seqlens, block_table=wl.block_table, page_size=wl.page_size,
+                    num_pages=wl.k_cache.shape[0], max_pages_per_seq=wl.block_table.shape[1],
+                    cache_dtype="fp8", causal=wl.causal)
+    o2, l2 = plan.run(dp.q, dp.k_new, dp.v_new, dp.k_cache, dp.v_cache, dp.bt, scale=wl.scale,
+                      kv_scale=torch.from_numpy(ks.copy()).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(o2), _bits(out)) and np.array_equal(_bits(l2), _bits(lse)), "out / lse differ"
+    k1, v1 = dd.cache_host()
+    k2, v2 = dp.cache_host()
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2), "cache bytes differ"
+    say("[ok] fp8 decode, device scales: bitwise the direct call")
