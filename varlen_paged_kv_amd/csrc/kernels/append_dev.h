@@ -28,27 +28,23 @@ namespace append_detail {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// float32 magnitude -> e4m3fn code: nearest, ties to even, satfinite.  The
-// sign bit comes from the unscaled input (1/scale > 0, so it is the product's
-// sign for every non-NaN input, and it keeps a NaN's sign deterministic).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x, uint32_t sign) {
-  const uint32_t a = __float_as_uint(x) & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |x| >= 448 (and inf): saturate
-  if (a >= 0x3C800000u) {                            // |x| >= 2^-6: normal code
-    // keep 3 mantissa bits with round-to-nearest-even, then rebias 127 -> 7
-    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));
-  }
-  // subnormal code m * 2^-9, m = round-to-nearest-even(|x| * 2^9) in 0..8
-  const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);
-  return sign | static_cast<uint32_t>(m);
-}
-
+// Two bf16 values (low half first) -> two e4m3fn codes (low byte first) of
+// fp32(x) * inv: nearest, ties to even, satfinite.  A NaN's code takes the
+// sign of the unscaled input (1/scale > 0, so it is the product's sign for
+// every other input, and it keeps a NaN's sign deterministic).
 __device__ __forceinline__ uint32_t enc2(uint32_t two_bf16, float inv) {
   const float lo = __uint_as_float(two_bf16 << 16) * inv;
   const float hi = __uint_as_float(two_bf16 & 0xFFFF0000u) * inv;
-  return f32_to_e4m3(lo, (two_bf16 >> 8) & 0x80u) | (f32_to_e4m3(hi, (two_bf16 >> 24) & 0x80u) << 8);
+  // magnitudes from 448 up (infinities included) saturate; the hardware
+  // conversion rounds the rest to nearest, ties to even, subnormal codes
+  // included, and keeps the sign of zero
+  uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(
+                   __builtin_amdgcn_fmed3f(lo, -448.0f, 448.0f), __builtin_amdgcn_fmed3f(hi, -448.0f, 448.0f), 0,
+                   false)) & 0xFFFFu;
+  // a NaN gives the NaN code with the input's sign
+  if (__builtin_isnan(lo)) w = (w & 0xFF00u) | ((two_bf16 >> 8) & 0x80u) | 0x7Fu;
+  if (__builtin_isnan(hi)) w = (w & 0x00FFu) | ((((two_bf16 >> 24) & 0x80u) | 0x7Fu) << 8);
+  return w;
 }
 
 }  // namespace append_detail
@@ -68,6 +64,30 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
   using namespace append_detail;
   const int t0 = wg * p.tokens_per_wg;
   const int nt = min(p.tokens_per_wg, p.total_knew - t0);
+  const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
+  const int per_tok = 2 * chunks;       // K chunks then V chunks
+  const int total = nt * per_tok;
+  // four chunks per thread at a time: their loads are issued together, then
+  // they are encoded and stored
+  constexpr int kBatch = 4;
+  auto load_batch = [&](int f0, u32x4 (&x)[kBatch]) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int f = f0 + k * nthreads;
+      if (f < total) {
+        const int i = f / per_tok;
+        const int c = f - i * per_tok;
+        const bool is_v = c >= chunks;
+        const int cc = is_v ? c - chunks : c;
+        x[k] = *reinterpret_cast<const u32x4*>((is_v ? p.v_new : p.k_new) +
+                                                 static_cast<int64_t>(t0 + i) * p.row_elems + cc * 8);
+      }
+    }
+  };
+  // the first batch's sources do not depend on the destinations: their loads
+  // are issued before the destination lookups, so both round trips overlap
+  u32x4 x[kBatch];
+  load_batch(tid, x);
   int32_t* const tpos = reinterpret_cast<int32_t*>(dst + kAppendTokensMax);
   if (p.rope.dim > 0)
     for (int i = tid; i < nt; i += nthreads) tpos[i] = p.kpos[t0 + i];
@@ -84,7 +104,6 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
       dst[i] = (static_cast<int64_t>(page) * p.page_size + slot) * p.row_elems;
     }
   }
-  __syncthreads();
   // fp8: the reciprocals of the scales (fp32 division, rounded once, as the
   // host computes them when the scales are passed by value)
   float k_inv = p.k_inv_scale, v_inv = p.v_inv_scale;
@@ -92,26 +111,9 @@ __device__ __forceinline__ void append_tokens(const AppendParams& p, int wg, int
     k_inv = 1.0f / p.kv_scale_dev[0];
     v_inv = 1.0f / p.kv_scale_dev[1];
   }
-  const int chunks = p.row_elems / 8;   // 8 bf16 source elements per chunk
-  const int per_tok = 2 * chunks;       // K chunks then V chunks
-  const int total = nt * per_tok;
-  // four chunks per thread at a time: their loads are issued together, then
-  // they are encoded and stored
-  constexpr int kBatch = 4;
+  __syncthreads();
   for (int f0 = tid; f0 < total; f0 += kBatch * nthreads) {
-    u32x4 x[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int f = f0 + k * nthreads;
-      if (f < total) {
-        const int i = f / per_tok;
-        const int c = f - i * per_tok;
-        const bool is_v = c >= chunks;
-        const int cc = is_v ? c - chunks : c;
-        x[k] = *reinterpret_cast<const u32x4*>((is_v ? p.v_new : p.k_new) +
-                                                 static_cast<int64_t>(t0 + i) * p.row_elems + cc * 8);
-      }
-    }
+    if (f0 != tid) load_batch(f0, x);
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int f = f0 + k * nthreads;
