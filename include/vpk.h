@@ -57,7 +57,8 @@
  * tensor, so that PyTorch owns the device memory); a stream without one gets a
  * library-allocated workspace that grows as needed (the fallback).  The work
  * list of a direct call is written into a small ring of pinned host buffers
- * that the kernels read directly.  Two calls that overlap in time on one
+ * that the kernels read directly, or from a copy at the end of a caller's
+ * workspace when it repeats the previous call's (option "plan_reuse").  Two calls that overlap in time on one
  * device must use the same stream or different streams, never the same stream
  * from two host threads at once.
  *
@@ -507,6 +508,16 @@ int32_t vpk_abi_version(void);
  *   "plan_upload"      0 = the kernels read a direct call's work list from
  *                      pinned host memory (default); 1 = it is copied into the
  *                      workspace on the call's stream first.
+ *   "plan_reuse"       1 (default) = a direct call with a caller's workspace
+ *                      whose work list has the same bytes as the previous
+ *                      call's on its stream (same lengths, options and
+ *                      workspace, as in every layer of a model step) has it
+ *                      copied once, on the stream, to the end of that
+ *                      workspace, and the calls after it read the copy
+ *                      instead of pinned host memory; the copy is dropped
+ *                      when a call brings another work list, when a call's
+ *                      partials reach it, or when the workspace is replaced.
+ *                      0 = always the pinned buffer.  Same results either way.
  *   "keep_scores"      QKV-Prob calls: 1 (default) = decode-mode rows keep
  *                      their first-pass scores in the workspace when it has
  *                      room (vpk_qkv_prob_score_bytes); 0 = the second pass

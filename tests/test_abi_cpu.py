@@ -193,6 +193,9 @@ def test_qkv_prob_score_bytes():
     assert lib.vpk_set_option(b"keep_scores", 0) == 0
     assert lib.vpk_set_option(b"keep_scores", 1) == 0
     assert lib.vpk_set_option(b"keep_scores", 2) == 1
+    assert lib.vpk_set_option(b"plan_reuse", 0) == 0
+    assert lib.vpk_set_option(b"plan_reuse", 1) == 0
+    assert lib.vpk_set_option(b"plan_reuse", 2) == 1
 
 
 def test_plan_log(capfd):

@@ -25,6 +25,7 @@ def _restore():
     vpk.AUTO_WORKSPACE = True
     vpk.set_option("force_splits", 0)
     vpk.set_option("plan_upload", 0)
+    vpk.set_option("plan_reuse", 1)
 
 
 def _mixed(cache="bf16", seed=71):
@@ -119,3 +120,44 @@ def test_small_workspace_splits_less_and_too_small_is_refused():
     vpk.set_workspace(None, stream=s)
     s.synchronize()
     say(f"[ok] small workspaces within tolerance; too small refused: {ei.value.msg}")
+
+
+def test_repeated_calls_read_the_reused_work_list():
+    """Direct calls on one stream with a caller's workspace: from the second call in a row with the same work
+    list on, the kernels read its copy at the end of the workspace.  A call with other lengths between, and
+    calls whose partials reach the copy (a workspace of exactly the bound, every tile cut into 7 parts), must
+    not disturb it: every call gives the bits of the same call with reuse off, in the same workspace."""
+    wa = _mixed("bf16", seed=74)
+    wb = make_custom(q_lens=[3, 1, 64], new_lens=[3, 1, 64], cache_lens=[100, 2000, 30], Hq=8, Hkv=2, D=128,
+                     page_size=16, causal=True, cache_dtype="bf16", seed=75)
+    da, db = DeviceCall(wa), DeviceCall(wb)
+    vpk.AUTO_WORKSPACE = False
+    big = max(int(wl.B) for wl in (wa, wb))
+    dims = [_lib.VpkDims(wl.B, wl.Tq, wl.Tn, wl.Hq, wl.Hkv, wl.D, wl.num_pages, wl.block_table.shape[1],
+                         _lib.VPK_DTYPE_BF16) for wl in (wa, wb)]
+    size = max(vpk.workspace_bytes_upper_bound(d) for d in dims)
+    steps = [("a", 0), ("a", 0), ("a", 0), ("b", 0), ("a", 0), ("a", 0), ("a", 7), ("a", 7), ("a", 0), ("a", 0)]
+    results = {}
+    for reuse in (0, 1):
+        vpk.set_option("plan_reuse", reuse)
+        s = torch.cuda.Stream()
+        buf = torch.empty(size, dtype=torch.uint8, device="cuda")
+        vpk.set_workspace(buf, stream=s)
+        say(f"[case] plan reuse {reuse}: {len(steps)} calls in a row, workspace {size} bytes (batch {big})")
+        outs = []
+        with torch.cuda.stream(s):
+            for name, splits in steps:
+                vpk.set_option("force_splits", splits)
+                outs.append((da if name == "a" else db).run(stream=s))
+        s.synchronize()
+        vpk.set_workspace(None, stream=s)
+        results[reuse] = [(_bits(o), _bits(l)) for o, l in outs]
+        del buf
+    vpk.set_option("force_splits", 0)
+    for i, ((o0, l0), (o1, l1)) in enumerate(zip(results[0], results[1])):
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1), f"call {i} {steps[i]}: reuse changed the bits"
+    ref = oracle_full(wa)
+    o, l = outs[-1]
+    check_attention(to_np_out(o), l.cpu().numpy().astype(np.float64), ref["out"], ref["lse"], label="plan reuse")
+    say("[ok] plan reuse: every call bitwise equal to reuse off, within tolerance")
+

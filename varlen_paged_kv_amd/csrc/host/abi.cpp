@@ -53,6 +53,7 @@ struct Options {
   std::atomic<int64_t> mixed_dec_parts{1};
   std::atomic<int64_t> plan_log{-1};   // -1: VPK_LOG from the environment
   std::atomic<int64_t> keep_scores{1};
+  std::atomic<int64_t> plan_reuse{1};
 } g_opt;
 
 // ------------------------------------------------------------------ timing
@@ -143,6 +144,12 @@ struct Workspace {
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr;
   hipEvent_t ev_join = nullptr;
+  // Plan reuse: the work list of the last direct call on this stream (its
+  // bytes), and whether a copy of it sits at the end of the caller's
+  // workspace, at offset rec_off
+  std::vector<char> rec;
+  int rec_state = 0;         // 0 none, 1 seen once (not copied), 2 copied
+  size_t rec_off = 0;
   char* head() const { return user ? user : dev; }
   char* parts() const { return head() + kFlagBytes; }
 };
@@ -188,6 +195,8 @@ int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
   if (st) return st;
   *out = w;
   if (w->user) {
+    // a call whose partials reach the reused work list's copy overwrites it
+    if (w->rec_state == 2 && kFlagBytes + part_need > w->rec_off) w->rec_state = 0;
     if (kFlagBytes + part_need > w->user_bytes)
       return fail(VPK_ERROR_CAPACITY, "the workspace set with vpk_set_workspace holds " + std::to_string(w->user_bytes) +
                                           " bytes, this call needs " + std::to_string(kFlagBytes + part_need) +
@@ -246,6 +255,39 @@ int32_t take_plan_buffer(Workspace* w, size_t bytes, int* index) {
     pb.bytes = nb;
   }
   *index = k;
+  return VPK_SUCCESS;
+}
+
+// Plan reuse (option plan_reuse): the kernels of a direct call read its
+// work list (`bytes` bytes at R, in pinned host memory) over PCIe.  Every
+// layer of a model step calls with the same lengths and so writes the same
+// bytes: when they equal the previous call's on this stream, the list is
+// copied once, on `stream`, to the end of the caller's workspace, and the
+// calls after it read that copy (device memory) until a call brings other
+// bytes or its partials reach the copy.  The first call with new bytes reads
+// them from pinned memory as before, so calls whose lengths keep changing
+// pay only the comparison on the host.
+int32_t reuse_plan(Workspace* w, size_t bytes, size_t part_end, hipStream_t stream, char** R) {
+  if (g_opt.plan_reuse.load() == 0 || !w->user) return VPK_SUCCESS;
+  const size_t need = align_up(bytes, 256);
+  if (kFlagBytes + part_end + need > w->user_bytes) {
+    w->rec_state = 0;
+    return VPK_SUCCESS;
+  }
+  const size_t off = (w->user_bytes - need) / 256 * 256;
+  const bool same = w->rec_state > 0 && w->rec.size() == bytes && std::memcmp(w->rec.data(), *R, bytes) == 0;
+  if (!same) {
+    w->rec.assign(*R, *R + bytes);
+    w->rec_state = 1;
+    return VPK_SUCCESS;
+  }
+  if (w->rec_state == 1 || w->rec_off != off) {
+    const hipError_t e = hipMemcpyAsync(w->user + off, *R, bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (reused work list)");
+    w->rec_state = 2;
+    w->rec_off = off;
+  }
+  *R = w->user + off;
   return VPK_SUCCESS;
 }
 
@@ -1052,6 +1094,8 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
     const hipError_t e = hipMemcpyAsync(dR, R, L.plan_end, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan upload)");
     R = dR;
+  } else if ((st = reuse_plan(w, L.plan_end, L.part_end, stream, &R))) {
+    return st;
   }
   const Bases bases{R, w->parts(), w->head()};
   if (rc.q || rc.k) {
@@ -1639,6 +1683,7 @@ int32_t vpk_set_workspace(void* stream_v, void* ptr, size_t bytes) {
     std::lock_guard<std::mutex> lk(g_wmu);
     w->user = static_cast<char*>(ptr);
     w->user_bytes = ptr ? bytes : 0;
+    w->rec_state = 0;   // no copy of a work list in the new buffer
     return VPK_SUCCESS;
   } catch (...) {
     return fail(VPK_ERROR_OUT_OF_MEMORY, "host exception in vpk_set_workspace");
@@ -1713,6 +1758,9 @@ int32_t vpk_set_option(const char* name, int64_t value) {
   } else if (n == "mixed_grid") {
     if (value < -1 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "mixed_grid must be -1, 0 or 1");
     g_opt.mixed_grid = value;
+  } else if (n == "plan_reuse") {
+    if (value < 0 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "plan_reuse must be 0 or 1");
+    g_opt.plan_reuse = value;
   } else if (n == "keep_scores") {
     if (value < 0 || value > 1) return fail(VPK_ERROR_INVALID_VALUE, "keep_scores must be 0 or 1");
     g_opt.keep_scores = value;
