@@ -161,3 +161,31 @@ def test_repeated_calls_read_the_reused_work_list():
     check_attention(to_np_out(o), l.cpu().numpy().astype(np.float64), ref["out"], ref["lse"], label="plan reuse")
     say("[ok] plan reuse: every call bitwise equal to reuse off, within tolerance")
 
+
+
+def test_back_to_back_calls_through_the_plan_ring():
+    """Fourteen direct calls without a synchronisation, cycling over three batches with different lengths
+    (each call long on the GPU, so the host plans well ahead and wraps the ring of 8 plan buffers, whose
+    reuse waits on one event per 4 calls): each result must be bitwise the same call run alone."""
+    rng = np.random.default_rng(76)
+    wls = []
+    for i in range(3):
+        ql = rng.integers(128, 512, size=8)
+        wls.append(make_custom(q_lens=ql.tolist(), new_lens=ql.tolist(),
+                               cache_lens=rng.integers(2000, 6000, size=8).tolist(), Hq=32, Hkv=8, D=128,
+                               page_size=16, causal=True, cache_dtype="bf16", seed=77 + i))
+    dcs = [DeviceCall(wl) for wl in wls]
+    s = torch.cuda.Stream()
+    alone = []
+    for dc in dcs:
+        o, l = _run(dc, s)
+        alone.append((_bits(o), _bits(l)))
+    order = [i % 3 for i in range(14)]
+    say(f"[case] plan ring: {len(order)} calls back to back over 3 batches of 8 sequences")
+    with torch.cuda.stream(s):
+        outs = [dcs[i].run(stream=s) for i in order]
+    s.synchronize()
+    for n, (i, (o, l)) in enumerate(zip(order, outs)):
+        assert np.array_equal(_bits(o), alone[i][0]) and np.array_equal(_bits(l), alone[i][1]), \
+            f"call {n} (batch {i}) differs from the same call alone"
+    say("[ok] plan ring: every back-to-back call bitwise equal to the call alone")

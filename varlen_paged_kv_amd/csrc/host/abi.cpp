@@ -113,15 +113,21 @@ constexpr size_t kZerosOffset = 256;
 // Plans live in pinned host memory that the kernels read directly (each
 // workgroup reads its unit and sequence records once): no copy, no copy
 // stream, no cross-stream dependency on the critical path.  A ring of buffers
-// lets the host plan ahead of the GPU; a buffer is reused once the event
-// recorded behind the last kernel that read it has completed.
+// lets the host plan ahead of the GPU; a buffer is reused once an event
+// recorded behind the last kernel that read it has completed.  One event is
+// recorded per kPlanCover calls (each record costs the stream a few
+// microseconds): buffer k's use is covered by the event that the call with
+// buffer k | (kPlanCover - 1) records after it.
 constexpr int kPlanRing = 8;
+constexpr int kPlanCover = 4;
+static_assert(kPlanRing % kPlanCover == 0, "whole groups in the ring");
 
 struct PlanBuf {
   char* host = nullptr;      // pinned, device-accessible
   size_t bytes = 0;
-  hipEvent_t ev = nullptr;   // recorded after the kernels of the call that used it
-  bool pending = false;
+  hipEvent_t ev = nullptr;   // recorded after the kernels of the call that used this buffer (every kPlanCover-th)
+  bool used = false;         // read by enqueued work that no recorded event covers yet
+  int cover = -1;            // the buffer whose event covers this buffer's last use (-1: none pending)
 };
 
 // Split-partial rows one call may use at most, whatever its workspace (the
@@ -233,18 +239,25 @@ int32_t get_workspace(hipStream_t stream, size_t part_need, Workspace** out) {
 }
 
 // The next plan buffer with room for `bytes`, once the GPU is done with it.
-int32_t take_plan_buffer(Workspace* w, size_t bytes, int* index) {
+int32_t take_plan_buffer(Workspace* w, size_t bytes, hipStream_t stream, int* index) {
   const int k = w->next;
   w->next = (w->next + 1) % kPlanRing;
   PlanBuf& pb = w->plan[k];
   hipError_t e;
-  if (pb.pending) {
-    e = hipEventSynchronize(pb.ev);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (plan buffer)");
-    pb.pending = false;
-  }
   if (!pb.ev && (e = hipEventCreateWithFlags(&pb.ev, hipEventDisableTiming)) != hipSuccess)
     return hip_fail(e, "hipEventCreate (plan buffer)");
+  if (pb.used) {
+    // no event covers its last use (a call of its group failed before its
+    // release): one recorded now covers everything enqueued so far
+    if ((e = hipEventRecord(pb.ev, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (plan buffer)");
+    pb.used = false;
+    pb.cover = k;
+  }
+  if (pb.cover >= 0) {
+    e = hipEventSynchronize(w->plan[pb.cover].ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (plan buffer)");
+    pb.cover = -1;
+  }
   if (pb.bytes < bytes) {
     if (pb.host) (void)hipHostFree(pb.host);
     pb.host = nullptr;
@@ -291,11 +304,19 @@ int32_t reuse_plan(Workspace* w, size_t bytes, size_t part_end, hipStream_t stre
   return VPK_SUCCESS;
 }
 
-// Mark plan buffer k as read by everything enqueued on `stream` so far.
+// Mark plan buffer k as read by everything enqueued on `stream` so far; the
+// last buffer of each group of kPlanCover records the event that covers the
+// group's uses.
 int32_t release_plan_buffer(Workspace* w, hipStream_t stream, int k) {
-  hipError_t e = hipEventRecord(w->plan[k].ev, stream);
+  w->plan[k].used = true;
+  if (k % kPlanCover != kPlanCover - 1) return VPK_SUCCESS;
+  const hipError_t e = hipEventRecord(w->plan[k].ev, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord (plan buffer)");
-  w->plan[k].pending = true;
+  for (int j = k - (kPlanCover - 1); j <= k; ++j)
+    if (w->plan[j].used) {
+      w->plan[j].used = false;
+      w->plan[j].cover = k;
+    }
   return VPK_SUCCESS;
 }
 
@@ -660,8 +681,8 @@ void serialize_plan(const Plan& p, const Layout& L, const int32_t* cu_kn, int32_
 
 // Serialise the plan into the next pinned plan buffer; *index receives it.
 int32_t write_plan(Workspace* w, const Plan& p, const Layout& L, const int32_t* cu_kn, int32_t B,
-                   int32_t page_size, int* index) {
-  int32_t st = take_plan_buffer(w, L.plan_end, index);
+                   int32_t page_size, hipStream_t stream, int* index) {
+  int32_t st = take_plan_buffer(w, L.plan_end, stream, index);
   if (st) return st;
   serialize_plan(p, L, cu_kn, B, page_size, w->plan[*index].host);
   return VPK_SUCCESS;
@@ -1084,7 +1105,7 @@ int32_t plan_and_enqueue(const Call& c, const Mirrors& m, int32_t causal, const 
   log_plan(c.qp_scale ? "qkv_prob" : "attention", plan, dims, L.plan_end, L.part_end);
   if ((st = get_workspace(stream, L.part_end + (upload ? L.plan_end : 0), &w))) return st;
   int region = 0;
-  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, stream, &region))) return st;
   char* R = w->plan[region].host;
   if (rope)
     write_rope_positions(plan, L, B, dims->total_q, R,
@@ -1388,7 +1409,7 @@ int32_t append_impl(const vpk_dims* dims, const void* k_new, const void* v_new,
   Workspace* w = nullptr;
   if ((st = get_workspace(stream, 0, &w))) return st;
   int region = 0;
-  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, &region))) return st;
+  if ((st = write_plan(w, plan, L, m.cu_kn, B, c.page_size, stream, &region))) return st;
   if ((st = enqueue_append(append_params(c, w->head(), w->plan[region].host, L, k_new, v_new, k_cache,
                                          v_cache, block_table),
                            stream)))
