@@ -1,4 +1,4 @@
-"""Seeded fuzz tier: random small batches through the C ABI against the oracle.
+"""Seeded fuzz tier: 200 random small batches through the C ABI against the oracle.
 
 Each case draws its own shape from a seeded generator: batch 1..8, lengths
 0..300 (empty sequences, rows that see no key, q longer than kv), page sizes
@@ -15,7 +15,7 @@ from synth import make_custom
 
 from gpu_util import run_and_check
 
-N_CASES = 40
+N_CASES = 200
 
 
 def fuzz_case(i: int):
