@@ -304,7 +304,7 @@ def test_close_to_plain_fp8_attention():
     assert err.max() < 0.1 and err.mean() < 1e-2
 
 
-N_FUZZ = 24
+N_FUZZ = 100
 
 
 def _fuzz_spec(i):
