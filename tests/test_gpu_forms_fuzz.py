@@ -2,9 +2,10 @@
 
 With the option mixed_grid 1 (every batch that holds both kinds of items in
 one launch), the direct call is checked against the oracle (attention within
-the tolerances, appended cache bytes exact); the prepared call (vpk_plan_run)
-and the allocation-free call, each on fresh copies of the inputs, must then
-give the direct call's output, lse and cache bytes bit for bit.
+the tolerances, appended cache bytes exact); the prepared call (vpk_plan_run),
+the allocation-free call and the page-list form, each on fresh copies of the
+inputs, must then give the direct call's output, lse and cache bytes bit for
+bit.
 """
 import numpy as np
 import pytest
@@ -15,6 +16,7 @@ from synth import make_custom
 
 from gpu_util import DeviceCall, run_and_check, say
 from test_gpu_fuzz import fuzz_case
+from test_gpu_list import _list_call
 
 pytestmark = pytest.mark.gpu
 
@@ -61,11 +63,14 @@ def test_forms_agree(i):
     vpk.attn_varlen_paged_fwd_noalloc(dn.q, dn.cu_q, dn.k_new, dn.v_new, dn.cu_kn, dn.k_cache, dn.v_cache, dn.bt,
                                       dn.cl, wl.page_size, wl.causal, wl.scale, kv, out=o3, lse=l3,
                                       host_index=dn.host)
+    dl = DeviceCall(wl, with_new=dc.with_new)
+    cu = wl.cu_seqlens_q.astype(np.int64)
+    o4, l4 = _list_call(dl, dl.q, cu[:-1], np.diff(cu))
     torch.cuda.synchronize()
-    for name, o, l, d in (("prepared", o2, l2, dp), ("allocation-free", o3, l3, dn)):
+    for name, o, l, d in (("prepared", o2, l2, dp), ("allocation-free", o3, l3, dn), ("page-list", o4, l4, dl)):
         assert np.array_equal(_bits(o), _bits(out)), f"case {i} {name}: out differs from the direct call"
         assert np.array_equal(_bits(l), _bits(lse)), f"case {i} {name}: lse differs from the direct call"
         if caches[0] is not None:
             k2, v2 = d.cache_host()
             assert np.array_equal(k2, caches[0]) and np.array_equal(v2, caches[1]), f"case {i} {name}: cache bytes"
-    say(f"[ok] forms {i}: prepared and allocation-free bitwise equal to the direct call")
+    say(f"[ok] forms {i}: prepared, allocation-free and page-list calls bitwise equal to the direct call")
