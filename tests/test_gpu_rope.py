@@ -101,3 +101,59 @@ def test_rope_full_size_mixed_fp8():
                         label=f"rope mixed_fp8 seq {b}")
     say(f"[ok] rope full size mixed_fp8: all {wl.B} sequences; max {errs[0]:.2e} mean {errs[1]:.2e} "
         f"lse {errs[2]:.2e}")
+
+
+N_FUZZ = 80
+
+
+def _fuzz_rope(i):
+    """Fuzz case i of the dense tier with a rotary dim (a multiple of 16 up to the head dim) and a pairing."""
+    from test_gpu_fuzz import fuzz_case
+    spec = fuzz_case(i)
+    if i % 4:
+        # three draws in four made valid: no sequence with more query rows than keys
+        nl = spec["new_lens"]
+        for b, q in enumerate(spec["q_lens"]):
+            lk = spec["cache_lens"][b] + (nl[b] if nl else 0)
+            if q > lk:
+                if spec["cache_dtype"]:
+                    spec["cache_lens"][b] += q - lk
+                else:
+                    nl[b] = q
+    rng = np.random.default_rng(9700 + i)
+    R = 16 * int(rng.integers(1, spec["D"] // 16 + 1))
+    return spec, R, bool(rng.integers(0, 2))
+
+
+def test_rope_fuzz_draws_reach_both_pairings_and_dims():
+    draws = [_fuzz_rope(i) for i in range(N_FUZZ)]
+    assert {inter for _, _, inter in draws} == {True, False}
+    assert any(R == s["D"] for s, R, _ in draws) and any(R % 32 == 16 for _, R, _ in draws)
+
+
+@pytest.mark.parametrize("i", range(N_FUZZ))
+def test_rope_fuzz(i):
+    """The dense tier's draws with rotary embedding: against the oracle, or, where a sequence has more query
+    rows than keys (its first rows would have negative positions), refused before anything is enqueued."""
+    spec, R, inter = _fuzz_rope(i)
+    wl = make_custom(**spec)
+    with_new = wl.k_new is not None
+    cos, sin = rope_tables(int(wl.kv_lens().max()) + 3, R)
+    dc = DeviceCall(wl, with_new=with_new)
+    if np.any(wl.q_lens() > wl.kv_lens()):
+        kc0, vc0 = dc.cache_host()
+        with pytest.raises(vpk.VpkError) as ei:
+            _rope_call(dc, torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(), R, inter)
+        assert ei.value.status == 1, ei.value   # VPK_ERROR_INVALID_VALUE
+        kc1, vc1 = dc.cache_host()
+        if kc0 is not None:
+            assert np.array_equal(kc0, kc1) and np.array_equal(vc0, vc1), "a refused call wrote the cache"
+        return
+    out, lse = _rope_call(dc, torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda(), R, inter)
+    torch.cuda.synchronize()
+    ref = _oracle(wl, with_new, dict(cos=cos, sin=sin, rotary_dim=R, interleaved=inter))
+    check_attention(to_np_out(out), lse.cpu().numpy().astype(np.float64), ref["out"], ref["lse"],
+                    "fp8" if wl.cache_dtype == "fp8" else "bf16", label=f"rope fuzz {i} R={R} inter={inter}")
+    kc, vc = dc.cache_host()
+    if kc is not None:
+        assert np.array_equal(kc, ref["k_cache"]) and np.array_equal(vc, ref["v_cache"]), f"rope fuzz {i}: cache"
