@@ -11,6 +11,7 @@ Attention must be within the tolerances, appended cache bytes exact.
 import numpy as np
 import pytest
 
+import varlen_paged_kv_amd as vpk
 from synth import make_custom
 
 from gpu_util import run_and_check
@@ -79,3 +80,29 @@ def test_fuzz(i):
     wl = make_custom(**spec)
     run_and_check(wl, f"fuzz {i} q={spec['q_lens']} new={spec['new_lens']} cache={spec['cache_lens']}",
                   with_new=spec["new_lens"] is not None)
+
+
+N_SPLIT_CASES = 100
+
+
+@pytest.fixture
+def _planner_knobs():
+    yield
+    vpk.set_option("force_splits", 0)
+    vpk.set_option("split_min_keys", 256)
+    vpk.set_option("persistent", -1)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_SPLIT_CASES))
+def test_fuzz_split_and_persistent(i, _planner_knobs):
+    """The same draws with every tile cut into 2, 3 or 7 key parts (64-key minimum, so short ranges split
+    too; the LSE merge then combines them) and persistent queues forced on or off."""
+    spec = fuzz_case(i)
+    splits = (2, 3, 7)[i % 3]
+    persistent = (i // 3) % 2
+    vpk.set_option("force_splits", splits)
+    vpk.set_option("split_min_keys", 64)
+    vpk.set_option("persistent", persistent)
+    wl = make_custom(**spec)
+    run_and_check(wl, f"fuzz {i} splits {splits} persistent {persistent}", with_new=spec["new_lens"] is not None)
