@@ -841,6 +841,32 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "append launch");
     }
   }
+  // a8: LSE merge of split parts, after the grid that wrote them (the kernel
+  // boundary makes the partials visible across the device without per-part
+  // fences)
+  auto merge = [&](hipStream_t s) -> int32_t {
+    MergeParams mp{};
+    mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
+    mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
+    mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
+    mp.out = static_cast<uint16_t*>(out);
+    mp.lse = lse;
+    mp.num_groups = static_cast<int32_t>(plan.groups.size());
+    mp.hq = dims->num_q_heads;
+    mp.g = dims->num_q_heads / dims->num_kv_heads;
+    mp.total_q = dims->total_q;
+    mp.head_dim = dims->head_dim;
+    int rc;
+    if (timed) {
+      KernelTimer tm(3, s);
+      rc = vpk::launch_merge(mp, s);
+    } else {
+      rc = vpk::launch_merge(mp, s);
+    }
+    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
+    return VPK_SUCCESS;
+  };
+  bool merged = plan.groups.empty();
   if (run_pre || run_dec) {
     AttnParams p{};
     p.q = static_cast<const uint16_t*>(q);
@@ -952,6 +978,12 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       if ((e = hipEventRecord(side->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord (fork)");
       if ((e = hipStreamWaitEvent(side->aux, side->ev_fork, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (fork)");
       if ((st = launch(plan.decode, vpk::kGridDecode, side->aux, fuse_append))) return st;
+      // split parts of decode-mode tiles only: merged on the side stream
+      // too, while the prefill-mode grid still runs
+      if (!merged && std::all_of(plan.groups.begin(), plan.groups.end(), [](const MergeGroup& g) { return g.dec; })) {
+        if ((st = merge(side->aux))) return st;
+        merged = true;
+      }
       if ((e = hipEventRecord(side->ev_join, side->aux)) != hipSuccess) return hip_fail(e, "hipEventRecord (join)");
       if ((st = launch(plan.prefill, vpk::kGridPrefill, stream, false))) return st;
       if ((e = hipStreamWaitEvent(stream, side->ev_join, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent (join)");
@@ -961,29 +993,7 @@ int32_t enqueue_all(const Call& c, const Plan& plan, const Layout& L, const Base
       if (run_pre && (st = launch(plan.prefill, vpk::kGridPrefill, stream, fuse_append && !run_dec))) return st;
     }
   }
-  if (!plan.groups.empty()) {
-    // a8: LSE merge of split parts, after the grids (the kernel boundary makes
-    // the partials visible across the device without per-part fences)
-    MergeParams mp{};
-    mp.groups = reinterpret_cast<const MergeGroup*>(R + L.groups);
-    mp.part_o = reinterpret_cast<const float*>(PA + L.part_o);
-    mp.part_lse = reinterpret_cast<const float*>(PA + L.part_lse);
-    mp.out = static_cast<uint16_t*>(out);
-    mp.lse = lse;
-    mp.num_groups = static_cast<int32_t>(plan.groups.size());
-    mp.hq = dims->num_q_heads;
-    mp.g = dims->num_q_heads / dims->num_kv_heads;
-    mp.total_q = dims->total_q;
-    mp.head_dim = dims->head_dim;
-    int rc;
-    if (timed) {
-      KernelTimer tm(3, stream);
-      rc = vpk::launch_merge(mp, stream);
-    } else {
-      rc = vpk::launch_merge(mp, stream);
-    }
-    if (rc != 0) return hip_fail(static_cast<hipError_t>(rc), "merge launch");
-  }
+  if (!merged && (st = merge(stream))) return st;
   return VPK_SUCCESS;
 }
 

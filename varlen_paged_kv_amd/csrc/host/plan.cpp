@@ -245,7 +245,7 @@ void build_plan(const PlanInput& in, Plan& out) {
       for (int32_t h = 0; h < in.hkv; ++h) {
         out.groups.push_back(MergeGroup{t.seq, t.row0, t.nrows, h,
                                         static_cast<int32_t>(out.part_rows + static_cast<int64_t>(h) * u.nsplit * t.nrows),
-                                        u.nsplit, 0, 0, out.seqs[t.seq]});
+                                        u.nsplit, t.dec ? 1 : 0, 0, out.seqs[t.seq]});
       }
       group_base[gi++] = out.part_rows;
       out.part_rows += static_cast<int64_t>(in.hkv) * u.nsplit * t.nrows;

@@ -60,7 +60,8 @@ struct MergeGroup {
   int32_t kv_head;
   int32_t part;
   int32_t nsplit;
-  int32_t pad0, pad1;
+  int32_t dec;         // 1: a decode-mode tile (its parts run in the decode-mode grid)
+  int32_t pad1;
   SeqInfo s;           // copy of the sequence's SeqInfo
 };
 
